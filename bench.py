@@ -1,0 +1,209 @@
+"""Throughput of the HIP verify step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one spec_verify_run (rows kernel + draw kernel) over the workload
+B=64, gamma=5, V=151936, bf16 target logits, fp32 draft probabilities,
+T=0.8 on every request.  Inputs are synthetic (seeded, see synth/), already
+resident in HBM; R rotating copies of the inputs (more than the 256 MB
+Infinity Cache can hold) are cycled so every step streams from HBM.  Prints
+one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "spec-verify steps/s + HBM GB/s (% of peak) at B=64, γ=5, V=151936"
+PEAK_HBM_GBPS = 8000.0
+CONFIG_ID = 3
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rows_kernel_B64_g5_V151936_traffic.json")
+DEVICE_SRC = os.path.join(ROOT, "lossless_rejection_sampling_sampler_amd", "csrc", "sv_device.h")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(inp, num_accepted):
+    """Bytes the method must move for one step (see the measurement section of the design doc).
+
+    rows kernel: every target row once, the drafted-token gathers (id, logit, q),
+    temperature, uniforms and the outputs; draw kernel: the draw row's logits
+    again for every sampled request and its q row when it is a residual.
+    """
+    import numpy as np
+    B, G, V, D, R = inp.batch, inp.gamma, inp.vocab, inp.total_draft, inp.total_rows
+    sl = 2 if inp.dtype == "bf16" else 4
+    sampled = inp.temperature > 0
+    gam = inp.gammas
+    rows = R * V * sl + D * (4 + sl + 4) + 4 * B + 4 * B * (G + 2) + 4 * B * (G + 1) + 4 * B
+    if inp.offsets is not None:
+        rows += 4 * (B + 1)
+    residual = sampled & (num_accepted < gam)
+    draw = int(sampled.sum()) * V * sl + int(residual.sum()) * 4 * V
+    return int(rows), int(draw)
+
+
+def traffic_entry():
+    """HBM traffic of the rows kernel measured with rocprofv3 counters, if current."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    sha = hashlib.sha256(open(DEVICE_SRC, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s=12.0):
+    import oracle
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        oracle.verify(inp)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 50:
+            break
+    return {"value": n / el, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} full B={inp.batch} steps of the same workload (fp64 NumPy, one process)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--rotate", type=int, default=6)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed-replicate", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the verify step shards by "
+              "request with no exchange, so N GPUs run N independent copies of this step.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from lossless_rejection_sampling_sampler_amd import SpecVerify, upload
+    from synth import CONFIGS, make_config
+
+    spec = CONFIGS[CONFIG_ID]
+    log(f"[bench] generating {spec.name}")
+    inp = make_config(CONFIG_ID, replicate=args.seed_replicate)
+    dev = torch.device("cuda:0")
+    log("[bench] uploading, rotate=%d" % args.rotate)
+    base = upload(logits=inp.logits, logits_dtype=inp.dtype, draft_probs=inp.draft_probs,
+                  draft_ids=inp.draft_ids, temperature=inp.temperature, uniforms=inp.uniforms,
+                  gamma=inp.gamma, draft_offsets=inp.offsets, device=dev)
+    copies = [base]
+    for _ in range(args.rotate - 1):
+        c = upload(logits=inp.logits[:1], logits_dtype=inp.dtype, draft_probs=inp.draft_probs[:1],
+                   draft_ids=inp.draft_ids, temperature=inp.temperature, uniforms=inp.uniforms,
+                   gamma=inp.gamma, draft_offsets=inp.offsets, device=dev)
+        c.target_logits = base.target_logits.clone()
+        c.draft_probs = base.draft_probs.clone()
+        copies.append(c)
+    torch.cuda.synchronize()
+
+    sv = SpecVerify(inp.batch, inp.gamma, inp.vocab, inp.dtype, device=0)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    # argument blocks are built once so the timed loop is one C call per step
+    packed = [c.args() for c in copies]
+
+    def step(ctx, i):
+        st = ctx.run_args(packed[i % len(packed)], sh)
+        if st:
+            raise RuntimeError(f"spec_verify_run failed with status {st}")
+
+    for i in range(args.warmup):
+        step(sv, i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps, synchronised on both sides
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(sv, i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+
+    tok, num = base.results()
+    for c in copies[1:]:
+        t2, n2 = c.results()
+        assert np.array_equal(n2, num) and np.array_equal(t2, tok), "rotated copies disagree"
+    rows_b, draw_b = algorithmic_bytes(inp, num)
+    step_bytes = rows_b + draw_b
+
+    # ---- per-kernel durations: HIP events recorded by the library on this stream
+    svp = SpecVerify(inp.batch, inp.gamma, inp.vocab, inp.dtype, device=0, profile=True)
+    for i in range(args.warmup):
+        step(svp, i)
+    torch.cuda.synchronize()
+    svp.profile_read()
+    kp = max(200, min(args.steps, 2000))
+    for i in range(kp):
+        step(svp, i)
+    rows_ms, draw_ms, n_prof = svp.profile_read()
+    rows_avg_ms, draw_avg_ms = rows_ms / n_prof, draw_ms / n_prof
+    svp.close()
+
+    rows_gbps = rows_b / (rows_avg_ms * 1e-3) / 1e9
+    step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+    sampled = inp.temperature > 0
+    gam = inp.gammas
+    result = {
+        "metric": METRIC,
+        "value": round(1000.0 / ms_per_step, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in; f32 exp + f64 sums; f64 draw",
+        "data": "synthetic (seeded; shapes of the pages' gamma=5, T=0.8 deployment)",
+        "config": {"workload": f"verify step {spec.name}: B=64, gamma=5, V=151936, bf16 logits, "
+                               "fp32 q, T=0.8", "batch": inp.batch, "gamma": inp.gamma,
+                   "vocab": inp.vocab, "rotating_input_sets": len(copies)},
+        "hbm_gbps": round(step_gbps, 1),
+        "frac_of_peak": round(step_gbps / PEAK_HBM_GBPS, 4),
+        "algorithmic_bytes_per_step": step_bytes,
+        "kernels": {"rows_ms": round(rows_avg_ms, 6), "draw_ms": round(draw_avg_ms, 6),
+                    "rows_bytes": rows_b, "draw_bytes": draw_b, "events_over_steps": n_prof},
+        "acceptance": {"mean_accepted": float(num.mean()),
+                       "residual_draws": int((sampled & (num < gam)).sum()),
+                       "bonus_draws": int((sampled & (num == gam)).sum())},
+        "roofline": {"bound": "hbm", "achieved": round(rows_gbps, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(rows_gbps / PEAK_HBM_GBPS, 4),
+                     "kernel": "rows_kernel<BF16>", "traffic": traffic_entry()},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(result), flush=True)
+    sv.close()
+
+
+if __name__ == "__main__":
+    main()

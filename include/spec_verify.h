@@ -1,0 +1,177 @@
+/*
+ * spec_verify.h -- C ABI of the batched speculative-decoding verifier
+ * (lossless rejection sampler) for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the verify step defined on the spec-decoding page at
+ * dpshk.com/news/5598276 (scraped title "企业官网建设流程全解析"):
+ *
+ *   section 3.1  for every request b and draft position i the target model
+ *                supplies logits for gamma_b + 1 positions; p = softmax(l / T);
+ *                draft token x_i (drawn by the draft model from q_i) is
+ *                accepted with probability min(1, p_i(x_i) / q_i(x_i));
+ *                verification stops at the first rejection;
+ *   section 3.2  the rejected position is redrawn from the residual
+ *                (p - q)_+ / sum (p - q)_+, which makes the emitted tokens
+ *                distributed exactly as p;
+ *   section 5.2  q is floored at 1e-10 before dividing, the test is the strict
+ *                comparison "uniform < accept probability", and acceptance is a
+ *                prefix property (a cumulative product of the accept bits);
+ *   section 5.3  when all gamma_b drafts are accepted a bonus token is drawn
+ *                from the (gamma_b + 1)-th target distribution;
+ *   section 5.4  the number of accepted drafts is what the caller uses to
+ *                truncate its KV cache;
+ *   section 8    draft and target share one vocabulary (pitfall 1); T = 0 is
+ *                greedy decoding (pitfall 2).
+ *
+ * Readings where the page is silent (fixed here, identical in the CPU oracle):
+ *   - T_b <= 0 or NaN selects the greedy variant: g_i = argmax of the raw
+ *     logits (lowest id on ties); x_i is accepted iff x_i == g_i; the token
+ *     at the first mismatch (or the bonus position) is g.  q and the uniforms
+ *     are not read for such requests.
+ *   - The uniforms are an input, [B, gamma + 2] fp32 in [0, 1): columns
+ *     0 .. gamma_b - 1 drive the accept tests, column gamma the residual draw,
+ *     column gamma + 1 the bonus draw (gamma = the padded width below).
+ *   - A draw with weights w and uniform v returns min{x : C_x > v * S} where
+ *     C_x is the running sum of w in ascending token id and S = C_{V-1}
+ *     (zero-weight tokens are never returned).  If rounding leaves the
+ *     residual with S <= 0, the draw uses p instead.
+ *
+ * All entry points are plain C: device buffers are raw device pointers owned by
+ * the caller, sizes are integers, and the stream is an opaque hipStream_t
+ * (NULL = the legacy default stream).
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum sv_status {
+    SV_OK = 0,
+    SV_ERR_INVALID_ARG = 1,    /* a host-visible argument violates the contract */
+    SV_ERR_OUT_OF_MEMORY = 2,  /* device allocation failed in spec_verify_create */
+    SV_ERR_DEVICE = 3,         /* a HIP call failed (launch, event, copy) */
+    SV_ERR_UNSUPPORTED = 4,    /* dtype / size outside what this build handles */
+    SV_ERR_CAPACITY = 5        /* batch, gamma or vocab exceed the context's limits */
+};
+
+/* Logits element type. */
+enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 };
+
+/* Context flags. */
+enum sv_flags {
+    SV_FLAG_PROFILE = 1u,      /* record per-kernel HIP events (see spec_verify_profile_read) */
+    SV_FLAG_TWO_KERNEL = 2u,   /* schedule: rows kernel, then draw kernel */
+    SV_FLAG_ONE_LAUNCH = 4u    /* schedule: one cooperative launch (rows must be 16-byte aligned,
+                                  else the two-kernel schedule is used); with neither flag the
+                                  library picks the faster schedule for the shape */
+};
+
+/* Device-side contract violations, OR-ed into a sticky per-context word. */
+enum sv_device_error {
+    SV_DEVERR_DRAFT_ID = 1u,   /* a draft id outside [0, vocab); that draft counts as rejected */
+    SV_DEVERR_OFFSETS = 2u,    /* draft_offsets not prefix sums with 0 <= gamma_b <= gamma and
+                                  offsets[batch] <= total_draft; the affected requests' outputs
+                                  are unspecified (no access leaves the buffers' bounds) */
+    SV_DEVERR_NONFINITE = 4u   /* a draw row without positive finite mass (a target row with no
+                                  finite logit, or NaN logits); that token is unspecified */
+};
+
+/* Limits fixed at creation.  max_gamma <= SV_MAX_GAMMA. */
+#define SV_MAX_GAMMA 128
+typedef struct sv_config {
+    int32_t max_batch;     /* largest batch passed to run, >= 1 */
+    int32_t max_gamma;     /* largest padded draft width, 0 .. SV_MAX_GAMMA */
+    int32_t vocab;         /* V, shared by draft and target (page section 8, pitfall 1), 1 .. 524288 */
+    int32_t logits_dtype;  /* SV_F32 or SV_BF16 */
+    uint32_t flags;        /* SV_FLAG_* */
+} sv_config;
+
+/*
+ * One verify step.  Layout (row-major, contiguous, device memory):
+ *   request b owns gamma_b = off[b+1] - off[b] drafts, where off = draft_offsets
+ *   (prefix sums, off[0] = 0, off[batch] = total_draft) or, when draft_offsets is
+ *   NULL, gamma_b = gamma for every b and off[b] = b * gamma.
+ *   target_logits  [total_draft + batch, vocab]  logits_dtype; request b's rows
+ *                  are off[b] + b .. off[b] + b + gamma_b (the last one is the
+ *                  bonus position).  Rows must be aligned to the element size.
+ *   draft_probs    [total_draft, vocab] fp32 q; request b's rows are
+ *                  off[b] .. off[b] + gamma_b - 1.  Used as given (not
+ *                  renormalised).  Only the gathered q(x_i) and the one residual
+ *                  row per rejected request are read.
+ *   draft_ids      [total_draft] int32 x_i, in [0, vocab).
+ *   temperature    [batch] fp32; > 0 sampled, otherwise greedy.
+ *   uniforms       [batch, gamma + 2] fp32 in [0, 1) (see the column map above).
+ * Outputs (written for every request):
+ *   out_tokens       [batch, gamma + 1] int32: drafts 0..k-1, then the drawn (or
+ *                    greedy) token at k, then -1.
+ *   out_num_accepted [batch] int32: k, the number of accepted drafts.
+ * Optional diagnostics (NULL to skip):
+ *   diag_row_max   [total_draft + batch] fp32: max raw logit of every target row.
+ *   diag_row_norm  [total_draft + batch] fp64: Z = sum exp((l - max) / T) of every
+ *                  sampled row (0 for greedy rows).
+ *   diag_ratio     [total_draft] fp32: p(x_i) / max(q(x_i), 1e-10) of every draft
+ *                  of a sampled request (NaN for greedy requests).
+ */
+typedef struct sv_args {
+    int32_t batch;               /* 0 .. max_batch (0 is a no-op) */
+    int32_t gamma;               /* padded draft width, 0 .. max_gamma */
+    int32_t total_draft;         /* sum of gamma_b (= batch * gamma when draft_offsets is NULL) */
+    int32_t vocab;               /* must equal the context's vocab */
+    const int32_t *draft_offsets;   /* [batch + 1] or NULL */
+    const void    *target_logits;
+    const float   *draft_probs;
+    const int32_t *draft_ids;
+    const float   *temperature;
+    const float   *uniforms;
+    int32_t *out_tokens;
+    int32_t *out_num_accepted;
+    float   *diag_row_max;
+    double  *diag_row_norm;
+    float   *diag_ratio;
+} sv_args;
+
+typedef struct sv_ctx sv_ctx;    /* opaque; owns the device scratch of one stream */
+
+/* Creates a context on HIP device `device` and allocates its scratch (row
+ * statistics, counters, draw records) for cfg's limits.  On success *out
+ * holds the context (free it with spec_verify_destroy).  Returns
+ * SV_ERR_INVALID_ARG for bad limits, SV_ERR_OUT_OF_MEMORY / SV_ERR_DEVICE on
+ * HIP failure (then *out is NULL). */
+int spec_verify_create(const sv_config *cfg, int device, sv_ctx **out);
+
+/* Enqueues one verify step on `stream` (a hipStream_t; NULL = default stream)
+ * and returns without waiting.  Host-visible arguments are checked first; on a
+ * non-SV_OK status nothing is enqueued.  Outputs are valid once the stream has
+ * reached this point.  The call allocates nothing.  One context must not be
+ * used by two streams at the same time (its scratch is per call). */
+int spec_verify_run(sv_ctx *ctx, const sv_args *args, void *stream);
+
+/* Frees the context and its scratch after synchronising its device.  NULL is a
+ * no-op. */
+int spec_verify_destroy(sv_ctx *ctx);
+
+/* Reads (and, if clear != 0, resets) the sticky SV_DEVERR_* word.  Synchronises
+ * the context's device first.  Clearing also resets the context's arrival
+ * counters, which a call with inconsistent draft_offsets can leave behind: after
+ * a non-zero word, clear it before the next run. */
+int spec_verify_device_errors(sv_ctx *ctx, uint32_t *bits, int clear);
+
+/* With SV_FLAG_PROFILE: waits for the recorded events and returns the summed
+ * durations (milliseconds) over `*count` calls since the last read, then resets
+ * the sums.  rows_ms is the row-statistics kernel and draw_ms the draw kernel; for
+ * a one-launch step rows_ms is the whole step and draw_ms is ~0. */
+int spec_verify_profile_read(sv_ctx *ctx, double *rows_ms, double *draw_ms, int32_t *count);
+
+/* Static, human-readable name of a status code. */
+const char *spec_verify_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,414 @@
+// Host side of the speculative-decoding verifier: the C ABI declared in
+// include/spec_verify.h (context, argument checks, scratch, launches).
+//
+// Method: the spec-decoding page at dpshk.com/news/5598276, sections 3.1-3.2,
+// 5.2-5.4 and 8 (see the header for the operation and the readings).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "spec_verify.h"
+#include "sv_device.h"
+#include "sv_fused.h"
+
+namespace {
+
+constexpr int kRowVecsPerThread = 8;    // target 16-byte vectors per thread per row split
+constexpr int kDrawTargetWgs = 2048;    // draw-kernel workgroups to aim for per call
+constexpr int kProfileRing = 2048;      // calls between forced event folds
+
+struct Geometry {
+    int splits;          // split rows kernel: workgroups per row
+    int nblocks;         // draw blocks per row
+};
+
+Geometry geometry_for(int vocab, int dtype) {
+    const int esize = (dtype == SV_BF16) ? 2 : 4;
+    const long nvec = ((long)vocab * esize + 15) / 16;
+    long s = (nvec + (long)sv::kThreads * kRowVecsPerThread - 1) / ((long)sv::kThreads * kRowVecsPerThread);
+    s = std::max(1L, std::min(s, (long)sv::kMaxPieces));
+    Geometry g;
+    g.splits = static_cast<int>(s);
+    g.nblocks = (vocab + sv::kBlockElems - 1) / sv::kBlockElems;
+    return g;
+}
+
+// Fused step geometry: grid (all resident), rounds and draw chunks, or false
+// when the problem is too small to cut this way.
+struct FusedGeometry {
+    int grid, rounds, chunks;
+};
+
+bool fused_geometry(long nv, long vpr, int batch, int nblocks, int resident, FusedGeometry& fg) {
+    constexpr long kMinSlice = (long)sv::kThreads * sv::kRowUnroll;   // one batch of loads per thread
+    for (int rounds = 4; rounds >= 1; --rounds) {
+        long g = std::min<long>(resident, nv / rounds / kMinSlice);
+        if (g < 1) continue;
+        // no row may be cut into more than kMaxPieces pieces
+        // slices are at least lmin vectors long; a row meets at most
+        // ceil(vpr / lmin) + 1 slices of a round and may straddle two rounds
+        auto max_pieces = [&](long gg) {
+            const long lmin = std::max<long>(1, nv / rounds / gg - 1);
+            return (vpr + lmin - 1) / lmin + 2;
+        };
+        while (g > 1 && max_pieces(g) > sv::kMaxPieces) --g;
+        if (max_pieces(g) > sv::kMaxPieces || nv / rounds < g) continue;
+        fg.grid = static_cast<int>(g);
+        fg.rounds = rounds;
+        long c = (2 * g + batch - 1) / batch;
+        c = std::max(1L, std::min<long>(c, std::max(1, nblocks / 2)));
+        fg.chunks = static_cast<int>(c);
+        return true;
+    }
+    return false;
+}
+
+// Workgroups for the flat rows kernel: all resident at once, at least one batch
+// of loads per thread, and no row cut into more than kMaxPieces pieces.
+int flat_workgroups(long nv, long vpr, int resident) {
+    long g = std::min<long>(resident, std::max<long>(1, nv / ((long)sv::kThreads * sv::kRowUnroll)));
+    while (g > 1) {
+        const long lmin = nv / g;
+        const long pmax = (vpr + lmin - 1) / lmin + 1;
+        if (pmax <= sv::kMaxPieces) break;
+        --g;
+    }
+    return static_cast<int>(std::max<long>(1, g));
+}
+
+}  // namespace
+
+struct sv_ctx {
+    int device = 0;
+    sv_config cfg{};
+    Geometry geo{};
+    int max_rows = 0;
+    int resident_flat = 0;     // rows-flat workgroups resident at once on the device
+    int resident_fused = 0;    // fused-step workgroups resident at once (0: no cooperative launch)
+    uint32_t epoch = 0;        // tag of the fused step's publication words
+    sv::FPiece* fpieces = nullptr;
+    sv::DrawParams* dparams = nullptr;
+    unsigned long long* words = nullptr;
+    // device scratch (one allocation)
+    void* scratch = nullptr;
+    sv::Piece* parts = nullptr;
+    sv::RowStat* rows = nullptr;
+    sv::DrawTask* tasks = nullptr;
+    sv::BlockRec* recs = nullptr;
+    uint32_t* row_cnt = nullptr;
+    uint32_t* req_cnt = nullptr;
+    uint32_t* draw_cnt = nullptr;
+    uint32_t* err = nullptr;
+    // profiling
+    std::vector<hipEvent_t> events;    // 3 per call
+    int prof_n = 0;
+    double prof_rows_ms = 0.0, prof_draw_ms = 0.0;
+    int prof_calls = 0;
+};
+
+namespace {
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int fold_profile(sv_ctx* ctx) {
+    if (ctx->prof_n == 0) return SV_OK;
+    if (hipEventSynchronize(ctx->events[3 * (ctx->prof_n - 1) + 2]) != hipSuccess) return SV_ERR_DEVICE;
+    for (int i = 0; i < ctx->prof_n; ++i) {
+        float a = 0.f, b = 0.f;
+        if (hipEventElapsedTime(&a, ctx->events[3 * i], ctx->events[3 * i + 1]) != hipSuccess ||
+            hipEventElapsedTime(&b, ctx->events[3 * i + 1], ctx->events[3 * i + 2]) != hipSuccess)
+            return SV_ERR_DEVICE;
+        ctx->prof_rows_ms += a;
+        ctx->prof_draw_ms += b;
+    }
+    ctx->prof_calls += ctx->prof_n;
+    ctx->prof_n = 0;
+    return SV_OK;
+}
+
+void free_ctx(sv_ctx* ctx) {
+    if (!ctx) return;
+    int prev = 0;
+    (void)hipGetDevice(&prev);
+    (void)hipSetDevice(ctx->device);
+    for (hipEvent_t e : ctx->events) (void)hipEventDestroy(e);
+    if (ctx->scratch) (void)hipFree(ctx->scratch);
+    (void)hipSetDevice(prev);
+    delete ctx;
+}
+
+struct DeviceGuard {
+    int prev = -1;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        if (prev != dev) (void)hipSetDevice(dev);
+    }
+    ~DeviceGuard() {
+        int cur = -1;
+        (void)hipGetDevice(&cur);
+        if (prev >= 0 && cur != prev) (void)hipSetDevice(prev);
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char* spec_verify_status_string(int status) {
+    switch (status) {
+        case SV_OK: return "ok";
+        case SV_ERR_INVALID_ARG: return "invalid argument";
+        case SV_ERR_OUT_OF_MEMORY: return "out of device memory";
+        case SV_ERR_DEVICE: return "HIP device error";
+        case SV_ERR_UNSUPPORTED: return "unsupported configuration";
+        case SV_ERR_CAPACITY: return "exceeds the context's limits";
+        default: return "unknown status";
+    }
+}
+
+int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
+    if (!out) return SV_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (!cfg) return SV_ERR_INVALID_ARG;
+    if (cfg->max_batch < 1 || cfg->max_gamma < 0 || cfg->max_gamma > SV_MAX_GAMMA || cfg->vocab < 1)
+        return SV_ERR_INVALID_ARG;
+    if (cfg->logits_dtype != SV_F32 && cfg->logits_dtype != SV_BF16) return SV_ERR_UNSUPPORTED;
+    if ((long)cfg->vocab > (long)sv::kMaxDrawBlocks * sv::kBlockElems) return SV_ERR_UNSUPPORTED;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev) return SV_ERR_DEVICE;
+
+    sv_ctx* ctx = new (std::nothrow) sv_ctx();
+    if (!ctx) return SV_ERR_OUT_OF_MEMORY;
+    ctx->device = device;
+    ctx->cfg = *cfg;
+    ctx->geo = geometry_for(cfg->vocab, cfg->logits_dtype);
+    ctx->max_rows = cfg->max_batch * (cfg->max_gamma + 1);
+
+    DeviceGuard guard(device);
+    {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sv::rows_flat_kernel<sv::BF16>, sv::kThreads, 0) != hipSuccess) {
+            delete ctx;
+            return SV_ERR_DEVICE;
+        }
+        ctx->resident_flat = std::max(1, cus * std::max(1, per_cu));
+        int coop = 0, per_cu_fused = 0;
+        if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, device) != hipSuccess) coop = 0;
+        if (coop && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_fused, sv::fused_step_kernel<sv::BF16>,
+                                                                 sv::kThreads, 0) == hipSuccess) {
+            int per_f32 = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_f32, sv::fused_step_kernel<sv::F32>,
+                                                             sv::kThreads, 0) != hipSuccess) per_f32 = 0;
+            ctx->resident_fused = cus * std::min(per_cu_fused, per_f32);
+        }
+        (void)hipGetLastError();
+    }
+    const size_t n_rows = (size_t)ctx->max_rows;
+    const size_t n_b = (size_t)cfg->max_batch;
+    size_t off = 0;
+    const size_t o_parts = off; off = align_up(off + n_rows * sv::kMaxPieces * sizeof(sv::Piece), 256);
+    const size_t o_rows = off;  off = align_up(off + n_rows * sizeof(sv::RowStat), 256);
+    const size_t o_tasks = off; off = align_up(off + n_b * sizeof(sv::DrawTask), 256);
+    const size_t o_recs = off;  off = align_up(off + n_b * ctx->geo.nblocks * sizeof(sv::BlockRec), 256);
+    const size_t o_cnt = off;   off = align_up(off + (n_rows + 2 * n_b + 1) * sizeof(uint32_t), 256);
+    const size_t o_fp = off;    off = align_up(off + n_rows * sv::kMaxPieces * sizeof(sv::FPiece), 256);
+    const size_t o_dp = off;    off = align_up(off + n_b * sizeof(sv::DrawParams), 256);
+    const size_t o_wd = off;    off = align_up(off + n_b * sizeof(unsigned long long), 256);
+    const size_t total = off;
+    if (hipMalloc(&ctx->scratch, total) != hipSuccess) {
+        (void)hipGetLastError();
+        delete ctx;
+        return SV_ERR_OUT_OF_MEMORY;
+    }
+    char* base = static_cast<char*>(ctx->scratch);
+    ctx->parts = reinterpret_cast<sv::Piece*>(base + o_parts);
+    ctx->rows = reinterpret_cast<sv::RowStat*>(base + o_rows);
+    ctx->tasks = reinterpret_cast<sv::DrawTask*>(base + o_tasks);
+    ctx->recs = reinterpret_cast<sv::BlockRec*>(base + o_recs);
+    ctx->row_cnt = reinterpret_cast<uint32_t*>(base + o_cnt);
+    ctx->req_cnt = ctx->row_cnt + n_rows;
+    ctx->draw_cnt = ctx->req_cnt + n_b;
+    ctx->err = ctx->draw_cnt + n_b;
+    ctx->fpieces = reinterpret_cast<sv::FPiece*>(base + o_fp);
+    ctx->dparams = reinterpret_cast<sv::DrawParams*>(base + o_dp);
+    ctx->words = reinterpret_cast<unsigned long long*>(base + o_wd);
+    if (hipMemset(ctx->scratch, 0, total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        free_ctx(ctx);
+        return SV_ERR_DEVICE;
+    }
+    if (cfg->flags & SV_FLAG_PROFILE) {
+        ctx->events.resize(3 * kProfileRing, nullptr);
+        for (auto& e : ctx->events) {
+            if (hipEventCreate(&e) != hipSuccess) {
+                e = nullptr;
+                free_ctx(ctx);
+                return SV_ERR_DEVICE;
+            }
+        }
+    }
+    *out = ctx;
+    return SV_OK;
+}
+
+int spec_verify_destroy(sv_ctx* ctx) {
+    if (!ctx) return SV_OK;
+    {
+        DeviceGuard guard(ctx->device);
+        (void)hipDeviceSynchronize();
+    }
+    free_ctx(ctx);
+    return SV_OK;
+}
+
+int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
+    if (!ctx || !a) return SV_ERR_INVALID_ARG;
+    const sv_config& cfg = ctx->cfg;
+    if (a->batch < 0 || a->gamma < 0 || a->total_draft < 0) return SV_ERR_INVALID_ARG;
+    if (a->batch == 0) return SV_OK;
+    if (a->batch > cfg.max_batch || a->gamma > cfg.max_gamma) return SV_ERR_CAPACITY;
+    if (a->vocab != cfg.vocab) return SV_ERR_INVALID_ARG;   // one vocabulary for draft and target
+    if ((long)a->total_draft > (long)a->batch * a->gamma) return SV_ERR_INVALID_ARG;
+    if (!a->draft_offsets && a->total_draft != a->batch * a->gamma) return SV_ERR_INVALID_ARG;
+    if (!a->target_logits || !a->temperature || !a->uniforms || !a->out_tokens || !a->out_num_accepted)
+        return SV_ERR_INVALID_ARG;
+    if (a->total_draft > 0 && (!a->draft_probs || !a->draft_ids)) return SV_ERR_INVALID_ARG;
+    const size_t esize = (cfg.logits_dtype == SV_BF16) ? 2 : 4;
+    if (reinterpret_cast<uintptr_t>(a->target_logits) % esize) return SV_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(a->draft_probs) % 4 || reinterpret_cast<uintptr_t>(a->draft_ids) % 4)
+        return SV_ERR_INVALID_ARG;
+
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    DeviceGuard guard(ctx->device);
+
+    sv::Params P;
+    P.logits = a->target_logits;
+    P.q = a->draft_probs;
+    P.ids = a->draft_ids;
+    P.temperature = a->temperature;
+    P.uniforms = a->uniforms;
+    P.offsets = a->draft_offsets;
+    P.out_tokens = a->out_tokens;
+    P.out_num = a->out_num_accepted;
+    P.diag_m = a->diag_row_max;
+    P.diag_z = a->diag_row_norm;
+    P.diag_r = a->diag_ratio;
+    P.batch = a->batch;
+    P.gamma = a->gamma;
+    P.total_draft = a->total_draft;
+    P.vocab = a->vocab;
+    P.splits = ctx->geo.splits;
+    P.nblocks = ctx->geo.nblocks;
+    int C = (kDrawTargetWgs + a->batch - 1) / a->batch;
+    C = std::max(1, std::min(C, (ctx->geo.nblocks + sv::kWaves - 1) / sv::kWaves));
+    P.draw_wgs = C;
+    P.parts = ctx->parts;
+    P.rows = ctx->rows;
+    P.tasks = ctx->tasks;
+    P.recs = ctx->recs;
+    P.row_cnt = ctx->row_cnt;
+    P.req_cnt = ctx->req_cnt;
+    P.draw_cnt = ctx->draw_cnt;
+    P.err = ctx->err;
+
+    const long rows = (long)a->total_draft + a->batch;
+    // rows start on 16-byte boundaries: stream the flattened rows in equal ranges
+    const bool aligned = (reinterpret_cast<uintptr_t>(a->target_logits) % 16 == 0) &&
+                         (((long)a->vocab * (long)esize) % 16 == 0);
+    P.flat_vpr = (long)a->vocab * (long)esize / 16;
+    P.flat_nv = rows * P.flat_vpr;
+
+    sv::FusedParams F;
+    FusedGeometry fg{};
+    // the one-launch step is opt-in until it beats the two-kernel schedule
+    const bool want_fused = (cfg.flags & SV_FLAG_ONE_LAUNCH) && !(cfg.flags & SV_FLAG_TWO_KERNEL);
+    const bool fused = aligned && want_fused && ctx->resident_fused > 0 &&
+                       fused_geometry(P.flat_nv, P.flat_vpr, a->batch, ctx->geo.nblocks, ctx->resident_fused, fg);
+
+    const bool prof = (cfg.flags & SV_FLAG_PROFILE) != 0;
+    if (prof && ctx->prof_n == kProfileRing) {
+        const int st = fold_profile(ctx);
+        if (st != SV_OK) return st;
+    }
+    hipEvent_t* ev = prof ? &ctx->events[3 * ctx->prof_n] : nullptr;
+    if (prof && hipEventRecord(ev[0], stream) != hipSuccess) return SV_ERR_DEVICE;
+    if (fused) {
+        if (++ctx->epoch == 0) ctx->epoch = 1;
+        F.p = P;
+        F.p.parts = nullptr;
+        F.nv = P.flat_nv;
+        F.vpr = P.flat_vpr;
+        F.nrounds = fg.rounds;
+        F.chunks = fg.chunks;
+        F.epoch = ctx->epoch;
+        F.pieces = ctx->fpieces;
+        F.dparams = ctx->dparams;
+        F.words = ctx->words;
+        void* kargs[] = {&F};
+        const void* fn = (cfg.logits_dtype == SV_BF16)
+                             ? reinterpret_cast<const void*>(&sv::fused_step_kernel<sv::BF16>)
+                             : reinterpret_cast<const void*>(&sv::fused_step_kernel<sv::F32>);
+        if (hipLaunchCooperativeKernel(fn, dim3(fg.grid), dim3(sv::kThreads), kargs, 0, stream) != hipSuccess)
+            return SV_ERR_DEVICE;
+        if (prof && hipEventRecord(ev[1], stream) != hipSuccess) return SV_ERR_DEVICE;
+    } else {
+        const long grid1 = aligned ? flat_workgroups(P.flat_nv, P.flat_vpr, ctx->resident_flat) : rows * P.splits;
+        const long grid2 = (long)a->batch * C;
+        if (aligned) {
+            if (cfg.logits_dtype == SV_BF16)
+                hipLaunchKernelGGL(sv::rows_flat_kernel<sv::BF16>, dim3((unsigned)grid1), dim3(sv::kThreads), 0, stream, P);
+            else
+                hipLaunchKernelGGL(sv::rows_flat_kernel<sv::F32>, dim3((unsigned)grid1), dim3(sv::kThreads), 0, stream, P);
+        } else {
+            if (cfg.logits_dtype == SV_BF16)
+                hipLaunchKernelGGL(sv::rows_split_kernel<sv::BF16>, dim3((unsigned)grid1), dim3(sv::kThreads), 0, stream, P);
+            else
+                hipLaunchKernelGGL(sv::rows_split_kernel<sv::F32>, dim3((unsigned)grid1), dim3(sv::kThreads), 0, stream, P);
+        }
+        if (prof && hipEventRecord(ev[1], stream) != hipSuccess) return SV_ERR_DEVICE;
+        if (cfg.logits_dtype == SV_BF16)
+            hipLaunchKernelGGL(sv::draw_kernel<sv::BF16>, dim3((unsigned)grid2), dim3(sv::kThreads), 0, stream, P);
+        else
+            hipLaunchKernelGGL(sv::draw_kernel<sv::F32>, dim3((unsigned)grid2), dim3(sv::kThreads), 0, stream, P);
+    }
+    if (prof) {
+        if (hipEventRecord(ev[2], stream) != hipSuccess) return SV_ERR_DEVICE;
+        ctx->prof_n++;
+    }
+    if (hipGetLastError() != hipSuccess) return SV_ERR_DEVICE;
+    return SV_OK;
+}
+
+int spec_verify_device_errors(sv_ctx* ctx, uint32_t* bits, int clear) {
+    if (!ctx || !bits) return SV_ERR_INVALID_ARG;
+    DeviceGuard guard(ctx->device);
+    if (hipDeviceSynchronize() != hipSuccess) return SV_ERR_DEVICE;
+    if (hipMemcpy(bits, ctx->err, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess) return SV_ERR_DEVICE;
+    if (clear) {
+        // also drop arrival counts a call with inconsistent offsets may have left behind
+        const size_t n = (size_t)ctx->max_rows + 2 * (size_t)ctx->cfg.max_batch + 1;
+        if (hipMemset(ctx->row_cnt, 0, n * sizeof(uint32_t)) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+            return SV_ERR_DEVICE;
+    }
+    return SV_OK;
+}
+
+int spec_verify_profile_read(sv_ctx* ctx, double* rows_ms, double* draw_ms, int32_t* count) {
+    if (!ctx || !rows_ms || !draw_ms || !count) return SV_ERR_INVALID_ARG;
+    if (!(ctx->cfg.flags & SV_FLAG_PROFILE)) return SV_ERR_INVALID_ARG;
+    DeviceGuard guard(ctx->device);
+    const int st = fold_profile(ctx);
+    if (st != SV_OK) return st;
+    *rows_ms = ctx->prof_rows_ms;
+    *draw_ms = ctx->prof_draw_ms;
+    *count = ctx->prof_calls;
+    ctx->prof_rows_ms = ctx->prof_draw_ms = 0.0;
+    ctx->prof_calls = 0;
+    return SV_OK;
+}
+
+}  // extern "C"

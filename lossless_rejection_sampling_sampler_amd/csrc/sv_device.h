@@ -1,0 +1,1021 @@
+// Device code of the speculative-decoding verifier for gfx950 (CDNA4).
+//
+// Method: the spec-decoding page at dpshk.com/news/5598276 ("企业官网建设流程全解析"),
+// sections 3.1-3.2 (accept with probability min(1, p/q), stop at the first
+// rejection, redraw from (p - q)_+), 5.2 (q floored at 1e-10, strict
+// "uniform < accept probability", prefix acceptance), 5.3 (bonus token from the
+// last target row) and 8 (T = 0 is greedy).
+//
+// Two kernels per verify step, both bandwidth-bound streams over the vocabulary:
+//
+//   rows kernel  streams every target row once with 16-byte loads (two batches
+//                of loads in flight per thread), keeping a per-thread online max
+//                and sum of exp2((l - m) * log2(e) / T) (fp32 exponentials summed
+//                into fp64), or a running argmax for greedy rows; reduces across
+//                the 64-wide waves with cross-lane shuffles and across the four
+//                waves through LDS, and writes one partial per (row, piece).
+//                When rows are 16-byte aligned the flattened [rows x vocab]
+//                stream is cut into equal contiguous ranges, one per workgroup
+//                (a range covers pieces of one or two rows); otherwise each row
+//                is cut into equal splits with scalar head/tail handling.
+//                The last piece of a row to finish merges the pieces; the last
+//                row of a request to finish runs that request's accept tests,
+//                finds the first rejection, writes the outputs and leaves a draw
+//                task.
+//   draw kernel  streams the one draw row of every sampled request (residual
+//                (p - q)_+ or bonus p) in fp64, one 512-token block per wave, and
+//                records per-block sums; the last workgroup of the request
+//                rebuilds the exact fp64 normaliser, picks the block holding
+//                v * S with an LDS block scan, rescans that block token by token
+//                and writes the token.
+//
+// Cross-workgroup hand-off uses per-row / per-request arrival counters; see
+// the note at wait_stores().  Counters are reset by their last arrival (rows,
+// draws) or by the draw kernel (requests), so every call leaves the scratch
+// ready for the next.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+namespace sv {
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));   // one 16-byte load
+
+constexpr int kThreads = 256;            // 4 waves of 64
+constexpr int kWaves = kThreads / 64;
+constexpr int kRowUnroll = 4;            // 16-byte vectors per thread per batch (two batches in flight)
+constexpr int kMaxPieces = 16;           // partials per row
+constexpr int kDrawPerLane = 8;          // draw block: one wave, 8 tokens per lane
+constexpr int kBlockElems = 64 * kDrawPerLane;   // 512 tokens
+constexpr int kMaxDrawBlocks = 1024;     // vocab up to 2^19 tokens
+constexpr int kMarginSlots = 2;          // marginal tokens kept inline per block record (code assumes 2)
+constexpr double kLog2e = 1.4426950408889634;
+constexpr double kQFloor = 1e-10;        // page section 5.2: q.clamp(min=1e-10)
+// Relative margin within which a residual weight's sign could depend on the
+// last bits of the normaliser; such tokens are kept aside and re-evaluated with
+// the exact fp64 normaliser.
+constexpr double kSignMargin = 1e-5;
+
+enum : int { kDrawNone = 0, kDrawResidual = 1, kDrawBonus = 2, kDrawDegenerate = 3 };
+enum : uint32_t { kErrDraftId = 1u, kErrOffsets = 2u, kErrNonFinite = 4u };
+
+struct Piece {           // one (row, piece) partial
+    float m;             // piece max of the raw logits (or the argmax value)
+    int g;               // piece argmax (greedy rows)
+    double z;            // sum of exp2((l - m) * c) over the piece
+};
+
+struct RowStat {         // merged statistics of one target row
+    float m;             // max raw logit
+    int g;               // argmax (greedy rows), -1 otherwise
+    double z;            // normaliser Z (fp32 exponentials, fp64 sum)
+    float lx;            // logit of the drafted token of this position
+    float qx;            // q of the drafted token
+    int x;               // drafted token, -1 if invalid / none
+    int pad;
+};
+
+struct DrawTask {        // written by the resolving workgroup, read by the draw kernel
+    int kind;            // kDraw*
+    int row;             // target row holding the draw distribution
+    int drow;            // draft row of q (residual only)
+    int pos;             // output column k
+    float v;             // uniform of the draw
+    int pad[3];
+};
+
+struct BlockRec {        // per (request, 512-token draw block) sums
+    double se;           // sum of e = exp((l - m) / T) in fp64
+    double ea;           // sum of e over tokens whose residual is clearly positive
+    double qa;           // sum of q over the same tokens
+    int nm;              // tokens whose residual sign is marginal
+    int mx[kMarginSlots];        // their ids (first kMarginSlots, in token order)
+    float mq[kMarginSlots];      // their q
+    int pad;
+    double me[kMarginSlots];     // their e
+};
+
+struct Params {
+    // problem
+    const void* logits;
+    const float* q;
+    const int32_t* ids;
+    const float* temperature;
+    const float* uniforms;
+    const int32_t* offsets;
+    int32_t* out_tokens;
+    int32_t* out_num;
+    float* diag_m;
+    double* diag_z;
+    float* diag_r;
+    int batch, gamma, total_draft, vocab;
+    // launch geometry
+    int splits;          // split rows kernel: workgroups per row
+    long flat_nv;        // flat rows kernel: total 16-byte vectors
+    long flat_vpr;       // flat rows kernel: vectors per row
+    int draw_wgs;        // draw kernel: workgroups per request
+    int nblocks;         // draw blocks per row
+    // scratch
+    Piece* parts;        // [rows][kMaxPieces]
+    RowStat* rows;
+    DrawTask* tasks;
+    BlockRec* recs;
+    uint32_t* row_cnt;
+    uint32_t* req_cnt;
+    uint32_t* draw_cnt;
+    uint32_t* err;
+};
+
+// ----------------------------------------------------------------- element types
+struct F32 {
+    using T = float;
+    static constexpr int kPerVec = 4;
+    static __device__ __forceinline__ void decode(const v4u& v, float* f) {
+        f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+        f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+    }
+    static __device__ __forceinline__ float load1(const void* row, long x) {
+        return static_cast<const float*>(row)[x];
+    }
+    static constexpr uint32_t kNegInfWord = 0xff800000u;
+};
+
+struct BF16 {
+    using T = uint16_t;
+    static constexpr int kPerVec = 8;
+    static __device__ __forceinline__ void decode(const v4u& v, float* f) {
+        f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
+        f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
+        f[4] = __uint_as_float(v.z << 16); f[5] = __uint_as_float(v.z & 0xffff0000u);
+        f[6] = __uint_as_float(v.w << 16); f[7] = __uint_as_float(v.w & 0xffff0000u);
+    }
+    static __device__ __forceinline__ float load1(const void* row, long x) {
+        return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(row)[x]) << 16);
+    }
+    static constexpr uint32_t kNegInfWord = 0xff80ff80u;
+};
+
+// ----------------------------------------------------------------- cross-workgroup hand-off
+// gfx950 has one L2 per XCD and the L2s are not coherent with each other.  A
+// C++ release/acquire at agent scope therefore writes back and invalidates the
+// whole L2 of the issuing XCD, which costs microseconds and would be paid by
+// thousands of workgroups per call.  The hand-off here avoids it: data another
+// workgroup will read is written with device-scope stores (written through to
+// the device-coherent level) and read with device-scope loads; every writing
+// wave waits for its own stores to complete before the workgroup bumps an
+// arrival counter, and the counter RMW is performed at the device-coherent
+// level.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+template <typename T>
+__device__ __forceinline__ void st_coherent(T* p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_coherent(const T* p) {
+    return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t arrive(uint32_t* cnt) {
+    wait_stores();
+    return __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void reset_counter(uint32_t* cnt) {
+    __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void flag_error(uint32_t* err, uint32_t bits) {
+    __hip_atomic_fetch_or(err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ----------------------------------------------------------------- fp64 exp2
+// 2^(j/64) for j = 0..63, each the double nearest the exact value (computed with
+// 50-digit decimal arithmetic).
+__constant__ double kExp2Table[64] = {
+    1.0, 1.0108892860517005, 1.0218971486541166, 1.0330248790212284,
+    1.0442737824274138, 1.0556451783605572, 1.0671404006768237, 1.0787607977571199,
+    1.0905077326652577, 1.102382583307841, 1.1143867425958924, 1.1265216186082418,
+    1.1387886347566916, 1.1511892299529827, 1.1637248587775775, 1.1763969916502812,
+    1.189207115002721, 1.202156731452703, 1.215247359980469, 1.22848053610687,
+    1.241857812073484, 1.255380757024691, 1.2690509571917332, 1.2828700160787783,
+    1.2968395546510096, 1.3109612115247644, 1.3252366431597413, 1.339667524053303,
+    1.3542555469368927, 1.3690024229745905, 1.383909881963832, 1.3989796725383112,
+    1.4142135623730951, 1.42961333839197, 1.4451808069770467, 1.460917794180647,
+    1.4768261459394993, 1.4929077282912648, 1.5091644275934228, 1.5255981507445384,
+    1.5422108254079407, 1.559004400237837, 1.5759808451078865, 1.593142151342267,
+    1.6104903319492543, 1.6280274218573478, 1.645755478153965, 1.6636765803267364,
+    1.681792830507429, 1.7001063537185235, 1.718619298122478, 1.7373338352737062,
+    1.7562521603732995, 1.7753764925265212, 1.7947090750031072, 1.8142521755003989,
+    1.8340080864093424, 1.8539791250833855, 1.8741676341103, 1.8945759815869656,
+    1.9152065613971474, 1.9360617934922943, 1.9571441241754002, 1.978456026387951,
+};
+
+// 2^y for y <= 0 (y = -inf allowed), relative error about 3e-16: y = k/64 + r
+// with |r| <= 1/128 exactly, 2^r by its Taylor series in r*ln2 to degree 5
+// (truncation below 4e-17), 2^(j/64) from the table (kept in LDS by the
+// caller), and the power of two by ldexp.  Results below 2^-1070 are 0.
+__device__ __forceinline__ double exp2_nonpos(double y, const double* tab) {
+    const double kf = rint(y * 64.0);
+    const double r = fma(kf, -0.015625, y);
+    double p = fma(r, 0.0013333558146428443, 0.009618129107628477);
+    p = fma(r, p, 0.05550410866482158);
+    p = fma(r, p, 0.24022650695910072);
+    p = fma(r, p, 0.6931471805599453);
+    p = fma(r, p, 1.0);
+    const int k = static_cast<int>(kf);
+    const double res = ldexp(tab[k & 63] * p, k >> 6);
+    return (y > -1070.0) ? res : 0.0;
+}
+
+// ----------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ int wave_min_int(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+    return v;
+}
+// (value, index) argmax: larger value wins, lower index on ties.
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
+    if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+}
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        float v2 = __shfl_xor(v, o, 64);
+        int i2 = __shfl_xor(i, o, 64);
+        argmax_merge(v, i, v2, i2);
+    }
+}
+
+// Workgroup reductions: every thread receives the result (fixed combination order).
+struct RedScratch {
+    float f[kWaves];
+    double d[kWaves];
+    int i[kWaves];
+};
+
+__device__ __forceinline__ float wg_max(float v, RedScratch& s) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    v = wave_max(v);
+    if (lane == 0) s.f[w] = v;
+    __syncthreads();
+    float r = s.f[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) r = fmaxf(r, s.f[k]);
+    __syncthreads();
+    return r;
+}
+__device__ __forceinline__ double wg_sum(double v, RedScratch& s) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    v = wave_sum(v);
+    if (lane == 0) s.d[w] = v;
+    __syncthreads();
+    double r = s.d[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) r += s.d[k];
+    __syncthreads();
+    return r;
+}
+__device__ __forceinline__ int wg_sum_int(int v, RedScratch& s) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    v = wave_sum_int(v);
+    if (lane == 0) s.i[w] = v;
+    __syncthreads();
+    int r = 0;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) r += s.i[k];
+    __syncthreads();
+    return r;
+}
+__device__ __forceinline__ int wg_min_int(int v, RedScratch& s) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    v = wave_min_int(v);
+    if (lane == 0) s.i[w] = v;
+    __syncthreads();
+    int r = s.i[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) r = min(r, s.i[k]);
+    __syncthreads();
+    return r;
+}
+__device__ __forceinline__ int wg_max_int(int v, RedScratch& s) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    v = wave_max_int(v);
+    if (lane == 0) s.i[w] = v;
+    __syncthreads();
+    int r = s.i[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) r = max(r, s.i[k]);
+    __syncthreads();
+    return r;
+}
+__device__ __forceinline__ void wg_argmax(float& v, int& i, RedScratch& s) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    wave_argmax(v, i);
+    if (lane == 0) { s.f[w] = v; s.i[w] = i; }
+    __syncthreads();
+    float rv = s.f[0];
+    int ri = s.i[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) argmax_merge(rv, ri, s.f[k], s.i[k]);
+    __syncthreads();
+    v = rv; i = ri;
+}
+// Inclusive prefix sum over the workgroup (thread order); also returns the total.
+__device__ __forceinline__ double wg_inclusive_scan(double v, double& total, RedScratch& s) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        double y = __shfl_up(v, o, 64);
+        if (lane >= o) v += y;
+    }
+    if (lane == 63) s.d[w] = v;
+    __syncthreads();
+    double before = 0.0, tot = 0.0;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+        if (k < w) before += s.d[k];
+        tot += s.d[k];
+    }
+    __syncthreads();
+    total = tot;
+    return before + v;
+}
+
+// ----------------------------------------------------------------- request lookup
+// Maps target row t to (request b, position i, gamma_b, first draft row).
+struct RowMap {
+    int b, i, gb, d0;
+    bool ok;
+};
+
+__device__ __forceinline__ RowMap map_row(const Params& P, int t, RedScratch& red) {
+    RowMap r;
+    if (P.offsets == nullptr) {
+        r.b = t / (P.gamma + 1);
+        r.i = t - r.b * (P.gamma + 1);
+        r.gb = P.gamma;
+        r.d0 = r.b * P.gamma;
+        r.ok = true;
+        return r;
+    }
+    // request b starts at target row offsets[b] + b: count the starts <= t
+    int cnt = 0;
+    for (int j = threadIdx.x; j < P.batch; j += kThreads) cnt += (P.offsets[j] + j <= t);
+    const int b = wg_sum_int(cnt, red) - 1;
+    r.b = b;
+    r.ok = false;
+    r.i = r.gb = r.d0 = 0;
+    if (b < 0 || b >= P.batch) return r;
+    const int o0 = P.offsets[b], o1 = P.offsets[b + 1];
+    r.gb = o1 - o0;
+    r.d0 = o0;
+    r.i = t - (o0 + b);
+    r.ok = (o0 >= 0) && (o1 <= P.total_draft) && (r.gb >= 0) && (r.gb <= P.gamma) &&
+           (r.i >= 0) && (r.i <= r.gb);
+    return r;
+}
+
+// ----------------------------------------------------------------- row streaming
+struct RowShared {
+    RedScratch red;
+    int flag;
+    int k;
+};
+
+// Per-thread online max / sum over one batch of decoded logits.
+template <int N>
+__device__ __forceinline__ void accumulate_batch(const float* f, float c, float& mt, double& st) {
+    float bm = f[0];
+#pragma unroll
+    for (int k = 1; k < N; ++k) bm = fmaxf(bm, f[k]);
+    if (bm > mt) {
+        if (mt > -INFINITY)
+            st *= exp2((static_cast<double>(mt) - static_cast<double>(bm)) * static_cast<double>(c));
+        mt = bm;
+    }
+    if (mt > -INFINITY) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < N; ++k) acc += __builtin_amdgcn_exp2f((f[k] - mt) * c);
+        st += static_cast<double>(acc);
+    }
+}
+
+template <typename E>
+__device__ __forceinline__ void load_batch(v4u* buf, const v4u* vp, long first, int count) {
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u)
+        buf[u] = (u < count) ? __builtin_nontemporal_load(vp + first + (long)u * kThreads) : v4u(E::kNegInfWord);
+}
+
+// Streams vectors [v0, v1) of target row t (vectors counted from the row's first
+// 16-byte aligned element), adds the scalar head (piece 0) and tail (last piece),
+// publishes the piece and, for the last piece / last row, merges and resolves.
+template <typename E>
+__device__ void row_piece(const Params& P, int t, long v0, long v1, int piece, int npieces, RowShared& sh) {
+    const int tid = threadIdx.x;
+    const int V = P.vocab;
+
+    const RowMap rm = map_row(P, t, sh.red);
+    if (!rm.ok) {
+        if (tid == 0 && piece == 0) flag_error(P.err, kErrOffsets);
+        return;
+    }
+    const int b = rm.b, i = rm.i, gb = rm.gb;
+    const float T = P.temperature[b];
+    const bool greedy = !(T > 0.0f);
+    const float c = greedy ? 0.0f : static_cast<float>(kLog2e / static_cast<double>(T));
+
+    // the drafted token id of this position, fetched early for the row merge
+    int xdraft = -1;
+    if (tid == 0 && !greedy && i < gb) xdraft = P.ids[rm.d0 + i];
+
+    const typename E::T* row = static_cast<const typename E::T*>(P.logits) + (size_t)t * V;
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
+    int head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(typename E::T));
+    if (head > V) head = V;
+    const long nvec = (V - head) / E::kPerVec;
+    const int tail = V - head - static_cast<int>(nvec * E::kPerVec);
+    const v4u* vp = reinterpret_cast<const v4u*>(row + head);
+
+    // this thread's vectors: v0 + tid + 256 j, j < n
+    const long span = v1 - v0 - tid;
+    const int n = span > 0 ? static_cast<int>((span + kThreads - 1) / kThreads) : 0;
+    const long first = v0 + tid;
+    constexpr int EB = kRowUnroll * E::kPerVec;
+
+    float mloc;          // piece max (sampled) / argmax value (greedy)
+    int gloc = -1;       // argmax (greedy)
+    double zloc = 0.0;   // piece sum (sampled)
+    if (!greedy) {
+        float mt = -INFINITY;
+        double st = 0.0;
+        v4u A[kRowUnroll], Bf[kRowUnroll];
+        if (n > 0) load_batch<E>(A, vp, first, n);
+        for (int jb = 0; jb < n; jb += 2 * kRowUnroll) {
+            if (jb + kRowUnroll < n)
+                load_batch<E>(Bf, vp, first + (long)(jb + kRowUnroll) * kThreads, n - jb - kRowUnroll);
+            {
+                float f[EB];
+#pragma unroll
+                for (int u = 0; u < kRowUnroll; ++u) E::decode(A[u], f + u * E::kPerVec);
+                accumulate_batch<EB>(f, c, mt, st);
+            }
+            if (jb + kRowUnroll >= n) break;
+            if (jb + 2 * kRowUnroll < n)
+                load_batch<E>(A, vp, first + (long)(jb + 2 * kRowUnroll) * kThreads, n - jb - 2 * kRowUnroll);
+            {
+                float f[EB];
+#pragma unroll
+                for (int u = 0; u < kRowUnroll; ++u) E::decode(Bf[u], f + u * E::kPerVec);
+                accumulate_batch<EB>(f, c, mt, st);
+            }
+        }
+        // unaligned head (piece 0) and tail (last piece): at most 7 scalars each
+        float fx = -INFINITY;
+        if (piece == 0 && tid < head) fx = E::load1(row, tid);
+        if (piece == npieces - 1 && tid >= 64 && tid - 64 < tail) fx = E::load1(row, head + nvec * E::kPerVec + (tid - 64));
+        accumulate_batch<1>(&fx, c, mt, st);
+
+        mloc = wg_max(mt, sh.red);
+        double zs = 0.0;
+        if (mt > -INFINITY)
+            zs = st * exp2((static_cast<double>(mt) - static_cast<double>(mloc)) * static_cast<double>(c));
+        zloc = wg_sum(zs, sh.red);
+    } else {
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+        for (int jb = 0; jb < n; jb += kRowUnroll) {
+            v4u A[kRowUnroll];
+            load_batch<E>(A, vp, first + (long)jb * kThreads, n - jb);
+#pragma unroll
+            for (int u = 0; u < kRowUnroll; ++u) {
+                float f[E::kPerVec];
+                E::decode(A[u], f);
+                const int x0 = head + static_cast<int>((first + (long)(jb + u) * kThreads) * E::kPerVec);
+                if (jb + u < n) {
+#pragma unroll
+                    for (int k = 0; k < E::kPerVec; ++k) argmax_merge(bv, bi, f[k], x0 + k);
+                }
+            }
+        }
+        if (piece == 0 && tid < head) argmax_merge(bv, bi, E::load1(row, tid), tid);
+        if (piece == npieces - 1 && tid >= 64 && tid - 64 < tail) {
+            const int x = head + static_cast<int>(nvec * E::kPerVec) + (tid - 64);
+            argmax_merge(bv, bi, E::load1(row, x), x);
+        }
+        wg_argmax(bv, bi, sh.red);
+        mloc = bv;
+        gloc = bi;
+    }
+
+    // ---- publish the piece; the last piece of the row merges
+    if (tid == 0) {
+        Piece* pp = &P.parts[(size_t)t * kMaxPieces + piece];
+        st_coherent(&pp->m, mloc);
+        st_coherent(&pp->g, gloc);
+        st_coherent(&pp->z, zloc);
+        sh.flag = (arrive(&P.row_cnt[t]) == static_cast<uint32_t>(npieces - 1));
+    }
+    __syncthreads();
+    if (!sh.flag) return;
+    if (tid == 0) reset_counter(&P.row_cnt[t]);
+
+    RowStat st;
+    st.pad = 0;
+    {
+        float mj = -INFINITY;
+        int gj = 0x7fffffff;
+        double zj = 0.0;
+        if (tid < npieces) {
+            const Piece* pp = &P.parts[(size_t)t * kMaxPieces + tid];
+            mj = ld_coherent(&pp->m);
+            gj = ld_coherent(&pp->g);
+            zj = ld_coherent(&pp->z);
+        }
+        if (!greedy) {
+            const float M = wg_max(mj, sh.red);
+            double zz = 0.0;
+            if (tid < npieces && mj > -INFINITY)
+                zz = zj * exp2((static_cast<double>(mj) - static_cast<double>(M)) * static_cast<double>(c));
+            st.m = M; st.g = -1; st.z = wg_sum(zz, sh.red);
+        } else {
+            wg_argmax(mj, gj, sh.red);
+            st.m = mj; st.g = gj; st.z = 0.0;
+        }
+    }
+    st.lx = 0.0f; st.qx = 0.0f; st.x = -1;
+    if (tid == 0) {
+        if (!greedy && i < gb) {
+            const int x = xdraft;
+            if (x >= 0 && x < V) {
+                st.x = x;
+                st.lx = E::load1(row, x);
+                st.qx = P.q[(size_t)(rm.d0 + i) * V + x];
+            } else {
+                flag_error(P.err, kErrDraftId);
+            }
+        }
+        RowStat* rp = &P.rows[t];
+        st_coherent(&rp->m, st.m);
+        st_coherent(&rp->g, st.g);
+        st_coherent(&rp->z, st.z);
+        st_coherent(&rp->lx, st.lx);
+        st_coherent(&rp->qx, st.qx);
+        st_coherent(&rp->x, st.x);
+        if (P.diag_m) P.diag_m[t] = st.m;
+        if (P.diag_z) P.diag_z[t] = greedy ? 0.0 : st.z;
+        sh.flag = (arrive(&P.req_cnt[b]) == static_cast<uint32_t>(gb));
+    }
+    __syncthreads();
+    if (!sh.flag) return;
+
+    // ---- resolve request b: accept tests, first rejection, outputs, draw task
+    const int G = P.gamma;
+    const int t0 = rm.d0 + b;
+    if (tid == 0) sh.k = gb;
+    __syncthreads();
+    int xj = -1;
+    if (tid < gb) xj = P.ids[rm.d0 + tid];
+    if (tid < gb) {
+        bool acc;
+        const RowStat* rs = &P.rows[t0 + tid];
+        if (greedy) {
+            const int g = ld_coherent(&rs->g);
+            acc = (xj == g);
+            if (P.diag_r) P.diag_r[rm.d0 + tid] = __uint_as_float(0x7fc00000u);
+        } else {
+            const float m = ld_coherent(&rs->m);
+            const double Z = ld_coherent(&rs->z);
+            const float lx = ld_coherent(&rs->lx);
+            const float qx = ld_coherent(&rs->qx);
+            const int xv = ld_coherent(&rs->x);
+            const double invT = 1.0 / static_cast<double>(T);
+            const double px = exp((static_cast<double>(lx) - static_cast<double>(m)) * invT) / Z;
+            const double r = px / fmax(static_cast<double>(qx), kQFloor);
+            const double u = static_cast<double>(P.uniforms[(size_t)b * (G + 2) + tid]);
+            acc = (xv >= 0) && (u < fmin(1.0, r));
+            if (P.diag_r) P.diag_r[rm.d0 + tid] = static_cast<float>(r);
+        }
+        if (!acc) atomicMin(&sh.k, tid);
+    }
+    __syncthreads();
+    const int k = sh.k;
+    if (tid <= G) {
+        int tok = -1;
+        if (tid < k) tok = xj;
+        else if (tid == k && greedy) tok = ld_coherent(&P.rows[t0 + k].g);
+        P.out_tokens[(size_t)b * (G + 1) + tid] = tok;
+    }
+    if (tid == 0) {
+        P.out_num[b] = k;
+        DrawTask tk;
+        tk.kind = greedy ? kDrawNone : (k < gb ? kDrawResidual : kDrawBonus);
+        tk.row = t0 + k;
+        tk.drow = rm.d0 + k;
+        tk.pos = k;
+        tk.v = greedy ? 0.0f : P.uniforms[(size_t)b * (G + 2) + (k < gb ? G : G + 1)];
+        tk.pad[0] = tk.pad[1] = tk.pad[2] = 0;
+        P.tasks[b] = tk;
+    }
+}
+
+// General rows kernel: one workgroup per (target row, split); rows need not be
+// 16-byte aligned.
+template <typename E>
+__global__ __launch_bounds__(kThreads) void rows_split_kernel(Params P) {
+    __shared__ RowShared sh;
+    const int S = P.splits;
+    const int t = blockIdx.x / S;
+    const int s = blockIdx.x - t * S;
+    const int V = P.vocab;
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(static_cast<const typename E::T*>(P.logits) + (size_t)t * V);
+    int head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(typename E::T));
+    if (head > V) head = V;
+    const long nvec = (V - head) / E::kPerVec;
+    row_piece<E>(P, t, (long)s * nvec / S, (long)(s + 1) * nvec / S, s, S, sh);
+}
+
+// Workgroup owning vector v when nv vectors are cut into g equal ranges
+// [floor(w nv / g), floor((w+1) nv / g)).
+__device__ __forceinline__ int range_owner(long v, long nv, int g) {
+    return static_cast<int>(((v + 1) * (long)g - 1) / nv);
+}
+
+// Aligned rows kernel: the flattened [rows x vectors-per-row] stream is cut into
+// gridDim.x equal contiguous ranges; a range covers pieces of one or more rows.
+template <typename E>
+__global__ __launch_bounds__(kThreads) void rows_flat_kernel(Params P) {
+    __shared__ RowShared sh;
+    const int w = blockIdx.x;
+    const int G = gridDim.x;
+    const long NV = P.flat_nv, VPR = P.flat_vpr;
+    const long a = (long)w * NV / G, e = (long)(w + 1) * NV / G;
+    long r = a / VPR;
+    for (long s0 = a; s0 < e; ++r) {
+        const long rs = r * VPR, re = rs + VPR;
+        const long s1 = e < re ? e : re;
+        const int wf = range_owner(rs, NV, G), wl = range_owner(re - 1, NV, G);
+        row_piece<E>(P, static_cast<int>(r), s0 - rs, s1 - rs, w - wf, wl - wf + 1, sh);
+        __syncthreads();
+        s0 = s1;
+    }
+}
+
+// ----------------------------------------------------------------- draw kernel
+// The 8 tokens x0 .. x0+7 of one lane in a draw block.
+template <typename E>
+__device__ __forceinline__ void load_draw8(const typename E::T* lrow, const float* qrow, long x0,
+                                           int V, bool lalign, bool qalign, float* l, float* q) {
+    if (x0 + kDrawPerLane <= V && lalign) {
+        const v4u* lp = reinterpret_cast<const v4u*>(lrow + x0);
+#pragma unroll
+        for (int u = 0; u < kDrawPerLane / E::kPerVec; ++u)
+            E::decode(__builtin_nontemporal_load(lp + u), l + u * E::kPerVec);
+    } else {
+#pragma unroll
+        for (int k = 0; k < kDrawPerLane; ++k)
+            l[k] = (x0 + k < V) ? E::load1(lrow, x0 + k) : -INFINITY;
+    }
+    if (qrow) {
+        if (x0 + kDrawPerLane <= V && qalign) {
+            const v4u* qp = reinterpret_cast<const v4u*>(qrow + x0);
+#pragma unroll
+            for (int u = 0; u < kDrawPerLane / 4; ++u) {
+                const v4u w = __builtin_nontemporal_load(qp + u);
+                q[4 * u + 0] = __uint_as_float(w.x); q[4 * u + 1] = __uint_as_float(w.y);
+                q[4 * u + 2] = __uint_as_float(w.z); q[4 * u + 3] = __uint_as_float(w.w);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < kDrawPerLane; ++k) q[k] = (x0 + k < V) ? qrow[x0 + k] : 0.0f;
+        }
+    }
+}
+
+struct DrawShared {
+    RedScratch red;
+    double tab[64];
+    double w[kMaxDrawBlocks];
+    int list[kMaxDrawBlocks];
+    int n;
+    int flag;
+    double base;
+};
+
+// Everything a workgroup needs to work on one request's draw row.
+template <typename E>
+struct DrawRow {
+    int kind;            // kDrawResidual / kDrawBonus
+    int pos;             // output column
+    float v;             // uniform of the draw
+    double m;            // row max (raw logits)
+    double c2;           // log2(e) / T
+    double z32;          // normaliser from the fp32-exponential pass
+    const typename E::T* lrow;
+    const float* qrow;   // residual: q row, else nullptr
+    bool lalign, qalign;
+};
+
+// Per-block sums of draw blocks jfirst + wave, + jstride, ... < jend (one
+// 512-token block per wave at a time), written to recs with device-scope stores.
+template <typename E>
+__device__ void draw_blocks(const DrawRow<E>& d, int V, BlockRec* recs, int jfirst, int jstride, int jend,
+                            const double* tab) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const bool residual = (d.kind == kDrawResidual);
+    const double invZ32 = 1.0 / d.z32;
+    for (int j = jfirst + wv; j < jend; j += jstride) {
+        const long x0 = (long)j * kBlockElems + (long)lane * kDrawPerLane;
+        float l[kDrawPerLane], q[kDrawPerLane];
+        load_draw8<E>(d.lrow, d.qrow, x0, V, d.lalign, d.qalign, l, q);
+        double se = 0.0, ea = 0.0, qa = 0.0;
+        int nm = 0;
+        // this lane's first two marginal tokens (kMarginSlots == 2), in token order
+        double e_m0 = 0.0, e_m1 = 0.0;
+        float q_m0 = 0.0f, q_m1 = 0.0f;
+        int x_m0 = -1, x_m1 = -1;
+#pragma unroll
+        for (int k = 0; k < kDrawPerLane; ++k) {
+            const double e = exp2_nonpos((static_cast<double>(l[k]) - d.m) * d.c2, tab);
+            se += e;
+            if (residual && e > 0.0) {
+                const double pz = e * invZ32;
+                const double qd = static_cast<double>(q[k]);
+                const double dd = pz - qd;
+                if (dd > kSignMargin * pz) {
+                    ea += e; qa += qd;
+                } else if (dd >= -kSignMargin * pz) {
+                    if (nm == 0) { e_m0 = e; q_m0 = q[k]; x_m0 = static_cast<int>(x0) + k; }
+                    else if (nm == 1) { e_m1 = e; q_m1 = q[k]; x_m1 = static_cast<int>(x0) + k; }
+                    nm += 1;
+                }
+            }
+        }
+        se = wave_sum(se);
+        int nmw = 0;
+        if (residual) {
+            ea = wave_sum(ea);
+            qa = wave_sum(qa);
+            nmw = wave_sum_int(nm);
+        }
+        BlockRec* rec = &recs[j];
+        if (lane == 0) {
+            st_coherent(&rec->se, se);
+            st_coherent(&rec->ea, ea);
+            st_coherent(&rec->qa, qa);
+            st_coherent(&rec->nm, nmw);
+        }
+        if (nmw > 0 && nmw <= kMarginSlots) {
+            // slots in token order: exclusive prefix of the per-lane counts
+            int incl = nm;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += y;
+            }
+            const int before = incl - nm;
+            if (nm > 0 && before < kMarginSlots) {
+                st_coherent(&rec->mx[before], x_m0);
+                st_coherent(&rec->mq[before], q_m0);
+                st_coherent(&rec->me[before], e_m0);
+            }
+            if (nm > 1 && before + 1 < kMarginSlots) {
+                st_coherent(&rec->mx[before + 1], x_m1);
+                st_coherent(&rec->mq[before + 1], q_m1);
+                st_coherent(&rec->me[before + 1], e_m1);
+            }
+        }
+    }
+}
+
+// Select for one request once all its draw blocks are recorded: rebuilds the
+// exact fp64 normaliser, fixes every block's weight (re-evaluating blocks with
+// several marginal-sign tokens, or all blocks if the fp32-pass normaliser is off
+// by more than half the margin), finds the block holding v * S with a block scan
+// and the token with a token scan of that block.  Returns the token (uniform).
+template <typename E>
+__device__ int draw_select(const DrawRow<E>& d, int V, int NB, const BlockRec* recs, DrawShared& sh,
+                           uint32_t* err) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
+    constexpr int kPer = kMaxDrawBlocks / kThreads;    // blocks per thread (contiguous)
+    double se_t[kPer];
+    double zpart = 0.0;
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+        const int j = tid * kPer + r;
+        se_t[r] = (j < NB) ? ld_coherent(&recs[j].se) : 0.0;
+        zpart += se_t[r];
+    }
+    const double Z64 = wg_sum(zpart, sh.red);
+    const double invZ64 = 1.0 / Z64;
+    const bool residual = (d.kind == kDrawResidual);
+    int kind = d.kind;
+    if (tid == 0) sh.n = 0;
+    __syncthreads();
+    if (residual) {
+        const bool full = !(fabs(Z64 - d.z32) <= 0.5 * kSignMargin * Z64);
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) {
+            const int j = tid * kPer + r;
+            if (j < NB) {
+                const int nm = ld_coherent(&recs[j].nm);
+                if (!full && nm <= kMarginSlots) {
+                    double w = ld_coherent(&recs[j].ea) * invZ64 - ld_coherent(&recs[j].qa);
+                    for (int s = 0; s < nm; ++s)
+                        w += fmax(ld_coherent(&recs[j].me[s]) * invZ64 -
+                                  static_cast<double>(ld_coherent(&recs[j].mq[s])), 0.0);
+                    sh.w[j] = w;
+                } else {
+                    sh.list[atomicAdd(&sh.n, 1)] = j;
+                }
+            }
+        }
+        __syncthreads();
+        // blocks with several marginal tokens (or an inexact fp32-pass normaliser)
+        const int n_list = sh.n;
+        for (int li = wv; li < n_list; li += kWaves) {
+            const int j = sh.list[li];
+            const long x0 = (long)j * kBlockElems + (long)lane * kDrawPerLane;
+            float l[kDrawPerLane], q[kDrawPerLane];
+            load_draw8<E>(d.lrow, d.qrow, x0, V, d.lalign, d.qalign, l, q);
+            double w = 0.0;
+#pragma unroll
+            for (int k = 0; k < kDrawPerLane; ++k) {
+                const double e = exp2_nonpos((static_cast<double>(l[k]) - d.m) * d.c2, sh.tab);
+                w += fmax(e * invZ64 - static_cast<double>(q[k]), 0.0);
+            }
+            w = wave_sum(w);
+            if (lane == 0) sh.w[j] = w;
+        }
+        __syncthreads();
+        double wp = 0.0;
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) {
+            const int j = tid * kPer + r;
+            if (j < NB) wp += sh.w[j];
+        }
+        const double Sres = wg_sum(wp, sh.red);
+        if (!(Sres > 0.0)) kind = kDrawDegenerate;      // residual lost to rounding: use p
+    }
+    if (kind != kDrawResidual) {
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) {
+            const int j = tid * kPer + r;
+            if (j < NB) sh.w[j] = se_t[r];
+        }
+    }
+    __syncthreads();
+    // block-level inclusive scan (thread-contiguous blocks)
+    double wt[kPer];
+    double own = 0.0;
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+        const int j = tid * kPer + r;
+        wt[r] = (j < NB) ? sh.w[j] : 0.0;
+        own += wt[r];
+    }
+    double Stot;
+    const double incl = wg_inclusive_scan(own, Stot, sh.red);
+    const double tsel = static_cast<double>(d.v) * Stot;
+    int cand = 0x7fffffff;
+    int lastpos = -1;
+    double cand_before = 0.0;
+    {
+        double run = incl - own;
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) {
+            const int j = tid * kPer + r;
+            const double before = run;
+            run += wt[r];
+            if (j < NB && wt[r] > 0.0) lastpos = j;
+            if (j < NB && cand == 0x7fffffff && run > tsel) { cand = j; cand_before = before; }
+        }
+    }
+    int jsel = wg_min_int(cand, sh.red);
+    if (cand == jsel && jsel != 0x7fffffff) sh.base = cand_before;   // the owner of the first block
+    __syncthreads();
+    bool block_fallback = false;
+    if (jsel == 0x7fffffff) {           // rounding left no block above v * S
+        jsel = wg_max_int(lastpos, sh.red);
+        block_fallback = true;
+        if (tid == 0 && jsel >= 0) {
+            double bsum = 0.0;
+            for (int j = 0; j < jsel; ++j) bsum += sh.w[j];
+            sh.base = bsum;
+        }
+        __syncthreads();
+    }
+    if (jsel < 0) {                     // no positive finite weight (non-finite logits)
+        jsel = 0;
+        block_fallback = true;
+        if (tid == 0) { sh.base = 0.0; flag_error(err, kErrNonFinite); }
+        __syncthreads();
+    }
+    const double base = sh.base;
+
+    // token-level scan of the selected block: 2 tokens per thread
+    constexpr int kTok = kBlockElems / kThreads;
+    const long x0 = (long)jsel * kBlockElems + (long)tid * kTok;
+    double w[kTok];
+    double tsum = 0.0;
+#pragma unroll
+    for (int k = 0; k < kTok; ++k) {
+        const long x = x0 + k;
+        double e = 0.0, qd = 0.0;
+        if (x < V) {
+            e = exp2_nonpos((static_cast<double>(E::load1(d.lrow, x)) - d.m) * d.c2, sh.tab);
+            if (kind == kDrawResidual) qd = static_cast<double>(d.qrow[x]);
+        }
+        w[k] = (kind == kDrawResidual) ? fmax(e * invZ64 - qd, 0.0) : e;
+        tsum += w[k];
+    }
+    double dummy;
+    double run = base + (wg_inclusive_scan(tsum, dummy, sh.red) - tsum);
+    int ycand = 0x7fffffff, ylast = -1;
+#pragma unroll
+    for (int k = 0; k < kTok; ++k) {
+        run += w[k];
+        const int x = static_cast<int>(x0) + k;
+        if (w[k] > 0.0) ylast = x;
+        if (!block_fallback && ycand == 0x7fffffff && run > tsel) ycand = x;
+    }
+    int y = wg_min_int(ycand, sh.red);
+    if (y == 0x7fffffff) y = wg_max_int(ylast, sh.red);
+    if (y < 0) y = min(V - 1, static_cast<int>(jsel) * kBlockElems + kBlockElems - 1);
+    return y;
+}
+
+template <typename E>
+__device__ __forceinline__ void init_draw_row(DrawRow<E>& d, const Params& P, int kind, int row, int drow,
+                                              int pos, float v, float m, double z32, float T) {
+    d.kind = kind;
+    d.pos = pos;
+    d.v = v;
+    d.m = static_cast<double>(m);
+    d.c2 = kLog2e / static_cast<double>(T);
+    d.z32 = z32;
+    d.lrow = static_cast<const typename E::T*>(P.logits) + (size_t)row * P.vocab;
+    d.qrow = (kind == kDrawResidual) ? P.q + (size_t)drow * P.vocab : nullptr;
+    d.lalign = (reinterpret_cast<uintptr_t>(d.lrow) & 15u) == 0;
+    d.qalign = (reinterpret_cast<uintptr_t>(d.qrow) & 15u) == 0;
+}
+
+template <typename E>
+__global__ __launch_bounds__(kThreads) void draw_kernel(Params P) {
+    __shared__ DrawShared sh;
+
+    const int tid = threadIdx.x;
+    const int C = P.draw_wgs;
+    const int b = blockIdx.x / C;
+    const int c = blockIdx.x - b * C;
+    const int NB = P.nblocks;
+
+    if (c == 0 && tid == 0) reset_counter(&P.req_cnt[b]);     // ready for the next call
+    const DrawTask tk = P.tasks[b];
+    if (tk.kind == kDrawNone) return;
+    const bool residual = (tk.kind == kDrawResidual);
+    if (tk.row < 0 || tk.row >= P.total_draft + P.batch || tk.pos < 0 || tk.pos > P.gamma ||
+        (residual && (tk.drow < 0 || tk.drow >= P.total_draft)))
+        return;                                    // only reachable with inconsistent offsets
+    if (tid < 64) sh.tab[tid] = kExp2Table[tid];
+    const RowStat rs = P.rows[tk.row];
+    DrawRow<E> d;
+    init_draw_row<E>(d, P, tk.kind, tk.row, tk.drow, tk.pos, tk.v, rs.m, rs.z, P.temperature[b]);
+    __syncthreads();
+    BlockRec* recs = P.recs + (size_t)b * NB;
+    draw_blocks<E>(d, P.vocab, recs, c * kWaves, C * kWaves, NB, sh.tab);
+    wait_stores();                 // every wave's record stores complete before the arrival
+    __syncthreads();
+    if (tid == 0) sh.flag = (arrive(&P.draw_cnt[b]) == static_cast<uint32_t>(C - 1));
+    __syncthreads();
+    if (!sh.flag) return;
+    if (tid == 0) reset_counter(&P.draw_cnt[b]);
+    const int y = draw_select<E>(d, P.vocab, NB, recs, sh, P.err);
+    if (tid == 0) {
+        P.out_tokens[(size_t)b * (P.gamma + 1) + tk.pos] = y;
+        P.tasks[b].kind = kDrawNone;               // consumed: a stale task is never replayed
+    }
+}
+
+}  // namespace sv

@@ -1,0 +1,106 @@
+"""Parity of the HIP verifier with the CPU oracle (runs on an MI355X).
+
+Every case prints its name, shape and seed before touching the GPU.
+"""
+
+import numpy as np
+import pytest
+
+from synth import CONFIGS, make_config, make_inputs
+from synth.workloads import uniforms_from_seed
+from tests.gpu_helpers import log, parity_check
+
+pytestmark = pytest.mark.gpu
+
+EXCUSED_BUDGET = 1e-4
+
+
+def _assert_ok(rep, errs, min_requests=0):
+    assert not rep.unexcused, "\n".join(rep.unexcused[:10])
+    assert not errs, errs
+    assert rep.requests >= min_requests
+    assert rep.excused <= EXCUSED_BUDGET * rep.requests + 1e-9 or rep.excused == 0, \
+        f"excused {rep.excused} of {rep.requests}"
+
+
+# ---------------------------------------------------------------- small cases
+SMALL = [
+    ("c1", dict(n=1)),
+    ("c2", dict(n=2)),
+    ("c3_small", dict(n=3, vocab=9001, batch=12)),                  # bf16, ragged tail block
+    ("c4_small", dict(n=4, vocab=5000, batch=40)),                  # T mix incl. greedy
+    ("c5_small", dict(n=5, vocab=4099, batch=64)),                  # ragged, gamma_b = 0, q = p
+    ("c3_oddV_bf16", dict(n=3, vocab=1001, batch=16)),              # rows not 16-byte aligned
+    ("c2_oddV_f32", dict(n=2, vocab=777, batch=8)),
+    ("c2_offsets", dict(n=2, vocab=3000, batch=8, explicit_offsets=True)),
+    ("c1_tinyV", dict(n=1, vocab=3, batch=33)),
+]
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "twokernel"])
+@pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
+def test_small_parity(name, kw, fused):
+    kw = dict(kw)
+    n = kw.pop("n")
+    inp = make_config(n, replicate=7, **kw)
+    sets = [inp.uniforms] + [uniforms_from_seed(inp.uniforms.shape, s) for s in range(15)]
+    rep, errs, _ = parity_check(inp, sets, label=name, fused=fused)
+    _assert_ok(rep, errs)
+
+
+def test_temperature_edge_values():
+    """NaN / negative / zero temperatures take the greedy path; tiny T still samples."""
+    inp = make_config(2, replicate=3, vocab=2000, batch=8)
+    inp.temperature[:] = np.array([0.0, -1.0, np.nan, 1e-3, 0.05, 1.0, 4.0, 0.0], dtype=np.float32)
+    rep, errs, _ = parity_check(inp, label="T-edge")
+    _assert_ok(rep, errs)
+
+
+def test_greedy_requests_never_read_q():
+    """q rows of greedy requests are NaN-poisoned: results must not change."""
+    inp = make_config(4, replicate=5, vocab=3000, batch=32)
+    greedy = ~(inp.temperature > 0)
+    assert greedy.any() and (~greedy).any()
+    off = inp.draft_offsets
+    for b in np.nonzero(greedy)[0]:
+        inp.draft_probs[off[b]:off[b + 1]] = np.nan
+    rep, errs, _ = parity_check(inp, label="greedy-nan-q")
+    _assert_ok(rep, errs)
+
+
+def test_repeated_calls_are_identical():
+    """The arrival counters reset themselves: back-to-back calls agree."""
+    from tests.gpu_helpers import run_gpu
+    inp = make_config(3, replicate=2, vocab=20000, batch=24)
+    res, _, sv = run_gpu(inp, [inp.uniforms] * 4)
+    for tok, num in res[1:]:
+        assert np.array_equal(tok, res[0][0]) and np.array_equal(num, res[0][1])
+    # a smaller batch through the same context, then the full one again
+    small = make_config(3, replicate=3, vocab=20000, batch=5)
+    rs, _, _ = run_gpu(small, sv=sv)
+    res2, _, _ = run_gpu(inp, sv=sv)
+    assert np.array_equal(res2[0][0], res[0][0])
+
+
+# ---------------------------------------------------------------- full workloads
+# >= 2e4 requests per configuration: fresh uniforms over the same logits.
+FULL = [(1, 20000), (2, 2500), (3, 313), (4, 157), (5, 79)]
+
+
+@pytest.mark.parametrize("n,nsets", FULL, ids=[f"config{n}" for n, _ in FULL])
+def test_full_workload_parity(n, nsets):
+    log(f"[full] config {n} ({CONFIGS[n].name}) seed={1000 * n} sets={nsets}")
+    inp = make_config(n)
+    sets = [inp.uniforms] + [uniforms_from_seed(inp.uniforms.shape, 100 + s) for s in range(nsets - 1)]
+    rep, errs, _ = parity_check(inp, sets, label=f"config{n}")
+    _assert_ok(rep, errs, min_requests=20000)
+
+
+@pytest.mark.parametrize("n", [3, 5], ids=["config3", "config5"])
+def test_full_workload_two_kernel_schedule(n):
+    """The two-kernel schedule on the full workloads (fewer uniform sets)."""
+    log(f"[full-2k] config {n} seed={1000 * n}")
+    inp = make_config(n)
+    sets = [inp.uniforms] + [uniforms_from_seed(inp.uniforms.shape, 500 + s) for s in range(19)]
+    rep, errs, _ = parity_check(inp, sets, label=f"config{n}-2k", fused=False)
+    _assert_ok(rep, errs)
