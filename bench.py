@@ -2,7 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-A step is one spec_verify_run (rows kernel + draw kernel) over the workload
+A step is one spec_verify_run (one cooperative launch, or rows kernel + draw
+kernel, as the library or --schedule picks) over the workload
 B=64, gamma=5, V=151936, bf16 target logits, fp32 draft probabilities,
 T=0.8 on every request.  Inputs are synthetic (seeded, see synth/), already
 resident in HBM; R rotating copies of the inputs (more than the 256 MB
@@ -26,8 +27,22 @@ if ROOT not in sys.path:
 METRIC = "spec-verify steps/s + HBM GB/s (% of peak) at B=64, γ=5, V=151936"
 PEAK_HBM_GBPS = 8000.0
 CONFIG_ID = 3
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rows_kernel_B64_g5_V151936_traffic.json")
-DEVICE_SRC = os.path.join(ROOT, "lossless_rejection_sampling_sampler_amd", "csrc", "sv_device.h")
+KDT = "BF16"
+CSRC = os.path.join(ROOT, "lossless_rejection_sampling_sampler_amd", "csrc")
+KERNEL_SOURCES = ("sv_device.h", "sv_fused.h", "spec_verify.hip")
+
+
+def traffic_path(kernel: str) -> str:
+    """Counter-derived HBM traffic of one kernel on this workload (written from rocprofv3 runs)."""
+    stem = kernel.replace("<", "_").replace(">", "")
+    return os.path.join(ROOT, "profiles", f"{stem}_B64_g5_V151936_traffic.json")
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()
 
 
 def log(msg):
@@ -54,14 +69,14 @@ def algorithmic_bytes(inp, num_accepted):
     return int(rows), int(draw)
 
 
-def traffic_entry():
-    """HBM traffic of the rows kernel measured with rocprofv3 counters, if current."""
+def traffic_entry(kernel: str):
+    """HBM bytes per launch of ``kernel`` from rocprofv3 counters, or None when the
+    record is missing or was taken from other kernel sources."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(traffic_path(kernel)))
     except (OSError, ValueError):
         return None
-    sha = hashlib.sha256(open(DEVICE_SRC, "rb").read()).hexdigest()
-    if rec.get("kernel_source_sha256") != sha:
+    if rec.get("kernel_source_sha256") != kernel_source_sha():
         return None
     return rec.get("bytes_per_launch")
 
@@ -88,6 +103,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed-replicate", type=int, default=0)
+    ap.add_argument("--schedule", choices=["auto", "fused", "twokernel"], default="auto",
+                    help="one-launch step, rows + draw kernels, or the library's choice")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the verify step shards by "
@@ -99,6 +116,7 @@ def main():
     import torch
 
     from lossless_rejection_sampling_sampler_amd import SpecVerify, upload
+    from lossless_rejection_sampling_sampler_amd._lib import SV_SCHEDULE_FLAT, SV_SCHEDULE_ONE_LAUNCH, SV_SCHEDULE_SPLIT
     from synth import CONFIGS, make_config
 
     spec = CONFIGS[CONFIG_ID]
@@ -119,7 +137,8 @@ def main():
         copies.append(c)
     torch.cuda.synchronize()
 
-    sv = SpecVerify(inp.batch, inp.gamma, inp.vocab, inp.dtype, device=0)
+    fused = {"auto": None, "fused": True, "twokernel": False}[args.schedule]
+    sv = SpecVerify(inp.batch, inp.gamma, inp.vocab, inp.dtype, device=0, fused=fused)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     # argument blocks are built once so the timed loop is one C call per step
@@ -146,6 +165,7 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
 
+    sv_schedule = sv.last_schedule()
     tok, num = base.results()
     for c in copies[1:]:
         t2, n2 = c.results()
@@ -154,7 +174,7 @@ def main():
     step_bytes = rows_b + draw_b
 
     # ---- per-kernel durations: HIP events recorded by the library on this stream
-    svp = SpecVerify(inp.batch, inp.gamma, inp.vocab, inp.dtype, device=0, profile=True)
+    svp = SpecVerify(inp.batch, inp.gamma, inp.vocab, inp.dtype, device=0, profile=True, fused=fused)
     for i in range(args.warmup):
         step(svp, i)
     torch.cuda.synchronize()
@@ -163,10 +183,17 @@ def main():
     for i in range(kp):
         step(svp, i)
     rows_ms, draw_ms, n_prof = svp.profile_read()
+    svp_schedule = svp.last_schedule()
     rows_avg_ms, draw_avg_ms = rows_ms / n_prof, draw_ms / n_prof
     svp.close()
 
-    rows_gbps = rows_b / (rows_avg_ms * 1e-3) / 1e9
+    one_launch = svp_schedule == SV_SCHEDULE_ONE_LAUNCH
+    if one_launch:
+        # one kernel does the whole step: its bytes are the step's
+        kname, kbytes = f"fused_step_kernel<{KDT}>", step_bytes
+    else:
+        kname, kbytes = f"rows_flat_kernel<{KDT}>", rows_b
+    kernel_gbps = kbytes / (rows_avg_ms * 1e-3) / 1e9
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     sampled = inp.temperature > 0
     gam = inp.gammas
@@ -189,14 +216,16 @@ def main():
         "hbm_gbps": round(step_gbps, 1),
         "frac_of_peak": round(step_gbps / PEAK_HBM_GBPS, 4),
         "algorithmic_bytes_per_step": step_bytes,
+        "schedule": {SV_SCHEDULE_ONE_LAUNCH: "one-launch", SV_SCHEDULE_FLAT: "rows+draw",
+                     SV_SCHEDULE_SPLIT: "rows-split+draw"}.get(sv_schedule, "none"),
         "kernels": {"rows_ms": round(rows_avg_ms, 6), "draw_ms": round(draw_avg_ms, 6),
                     "rows_bytes": rows_b, "draw_bytes": draw_b, "events_over_steps": n_prof},
         "acceptance": {"mean_accepted": float(num.mean()),
                        "residual_draws": int((sampled & (num < gam)).sum()),
                        "bonus_draws": int((sampled & (num == gam)).sum())},
-        "roofline": {"bound": "hbm", "achieved": round(rows_gbps, 1), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(rows_gbps / PEAK_HBM_GBPS, 4),
-                     "kernel": "rows_kernel<BF16>", "traffic": traffic_entry()},
+        "roofline": {"bound": "hbm", "achieved": round(kernel_gbps, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(kernel_gbps / PEAK_HBM_GBPS, 4),
+                     "kernel": kname, "bytes_per_launch": kbytes, "traffic": traffic_entry(kname)},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")

@@ -167,6 +167,18 @@ int spec_verify_device_errors(sv_ctx *ctx, uint32_t *bits, int clear);
  * a one-launch step rows_ms is the whole step and draw_ms is ~0. */
 int spec_verify_profile_read(sv_ctx *ctx, double *rows_ms, double *draw_ms, int32_t *count);
 
+/* Schedule the last successful spec_verify_run on this context launched. */
+enum sv_schedule {
+    SV_SCHEDULE_NONE = 0,       /* no call yet, or the last call had batch == 0 */
+    SV_SCHEDULE_SPLIT = 1,      /* rows kernel with per-row pieces (unaligned rows), draw kernel */
+    SV_SCHEDULE_FLAT = 2,       /* rows kernel over the flattened rows, draw kernel */
+    SV_SCHEDULE_ONE_LAUNCH = 3  /* one cooperative launch */
+};
+
+/* Writes the sv_schedule of the last successful run to *schedule.  Host-only
+ * (no device work); SV_ERR_INVALID_ARG on null pointers. */
+int spec_verify_last_schedule(const sv_ctx *ctx, int32_t *schedule);
+
 /* Static, human-readable name of a status code. */
 const char *spec_verify_status_string(int status);
 

@@ -30,6 +30,10 @@ SV_DEVERR_DRAFT_ID = 1
 SV_DEVERR_OFFSETS = 2
 SV_DEVERR_NONFINITE = 4
 SV_MAX_GAMMA = 128
+SV_SCHEDULE_NONE = 0
+SV_SCHEDULE_SPLIT = 1
+SV_SCHEDULE_FLAT = 2
+SV_SCHEDULE_ONE_LAUNCH = 3
 
 EXPORTS = (
     "spec_verify_create",
@@ -37,6 +41,7 @@ EXPORTS = (
     "spec_verify_destroy",
     "spec_verify_device_errors",
     "spec_verify_profile_read",
+    "spec_verify_last_schedule",
     "spec_verify_status_string",
 )
 
@@ -102,6 +107,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_verify_profile_read.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_double),
                                              ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]
     lib.spec_verify_profile_read.restype = ctypes.c_int
+    lib.spec_verify_last_schedule.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)]
+    lib.spec_verify_last_schedule.restype = ctypes.c_int
     lib.spec_verify_status_string.argtypes = [ctypes.c_int]
     lib.spec_verify_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -175,6 +182,14 @@ class SpecVerify:
         if st != SV_OK:
             raise SpecVerifyError(st, "spec_verify_profile_read")
         return a.value, b.value, n.value
+
+    def last_schedule(self) -> int:
+        """SV_SCHEDULE_* of the last successful run on this context."""
+        v = ctypes.c_int32()
+        st = self._lib.spec_verify_last_schedule(self._ctx, ctypes.byref(v))
+        if st != SV_OK:
+            raise SpecVerifyError(st, "spec_verify_last_schedule")
+        return v.value
 
     def close(self) -> None:
         if getattr(self, "_ctx", None):

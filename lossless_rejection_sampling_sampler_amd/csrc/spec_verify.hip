@@ -37,34 +37,24 @@ Geometry geometry_for(int vocab, int dtype) {
     return g;
 }
 
-// Fused step geometry: grid (all resident), rounds and draw chunks, or false
-// when the problem is too small to cut this way.
+// One-launch geometry: pieces per row (about 8 vectors per thread each), grid
+// (all resident, no more workgroups than pieces) and draw chunks per request
+// (about two per workgroup, at most kMaxOwnChunks).
 struct FusedGeometry {
-    int grid, rounds, chunks;
+    int grid, pieces, items, chunks;
 };
 
-bool fused_geometry(long nv, long vpr, int batch, int nblocks, int resident, FusedGeometry& fg) {
-    constexpr long kMinSlice = (long)sv::kThreads * sv::kRowUnroll;   // one batch of loads per thread
-    for (int rounds = 4; rounds >= 1; --rounds) {
-        long g = std::min<long>(resident, nv / rounds / kMinSlice);
-        if (g < 1) continue;
-        // no row may be cut into more than kMaxPieces pieces
-        // slices are at least lmin vectors long; a row meets at most
-        // ceil(vpr / lmin) + 1 slices of a round and may straddle two rounds
-        auto max_pieces = [&](long gg) {
-            const long lmin = std::max<long>(1, nv / rounds / gg - 1);
-            return (vpr + lmin - 1) / lmin + 2;
-        };
-        while (g > 1 && max_pieces(g) > sv::kMaxPieces) --g;
-        if (max_pieces(g) > sv::kMaxPieces || nv / rounds < g) continue;
-        fg.grid = static_cast<int>(g);
-        fg.rounds = rounds;
-        long c = (2 * g + batch - 1) / batch;
-        c = std::max(1L, std::min<long>(c, std::max(1, nblocks / 2)));
-        fg.chunks = static_cast<int>(c);
-        return true;
-    }
-    return false;
+FusedGeometry fused_geometry(long vpr, int gamma, int batch, int nblocks, int resident) {
+    FusedGeometry fg;
+    long p = (vpr + (long)sv::kThreads * 8 / 2) / ((long)sv::kThreads * 8);
+    fg.pieces = static_cast<int>(std::max(1L, std::min<long>(p, sv::kMaxPieces)));
+    fg.items = (gamma + 1) * batch * fg.pieces;
+    fg.grid = std::max(1, std::min(resident, fg.items));
+    long c = (2L * fg.grid + batch - 1) / batch;
+    c = std::max(1L, std::min<long>(c, nblocks));
+    while (c > 1 && (long)batch * c > (long)fg.grid * sv::kMaxOwnChunks) --c;
+    fg.chunks = static_cast<int>(c);
+    return fg;
 }
 
 // Workgroups for the flat rows kernel: all resident at once, at least one batch
@@ -90,9 +80,11 @@ struct sv_ctx {
     int resident_flat = 0;     // rows-flat workgroups resident at once on the device
     int resident_fused = 0;    // fused-step workgroups resident at once (0: no cooperative launch)
     uint32_t epoch = 0;        // tag of the fused step's publication words
+    int last_schedule = SV_SCHEDULE_NONE;
     sv::FPiece* fpieces = nullptr;
     sv::DrawParams* dparams = nullptr;
     unsigned long long* words = nullptr;
+    unsigned long long* state = nullptr;
     // device scratch (one allocation)
     void* scratch = nullptr;
     sv::Piece* parts = nullptr;
@@ -219,6 +211,7 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
     const size_t o_fp = off;    off = align_up(off + n_rows * sv::kMaxPieces * sizeof(sv::FPiece), 256);
     const size_t o_dp = off;    off = align_up(off + n_b * sizeof(sv::DrawParams), 256);
     const size_t o_wd = off;    off = align_up(off + n_b * sizeof(unsigned long long), 256);
+    const size_t o_st = off;    off = align_up(off + n_b * sizeof(unsigned long long), 256);
     const size_t total = off;
     if (hipMalloc(&ctx->scratch, total) != hipSuccess) {
         (void)hipGetLastError();
@@ -237,6 +230,7 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
     ctx->fpieces = reinterpret_cast<sv::FPiece*>(base + o_fp);
     ctx->dparams = reinterpret_cast<sv::DrawParams*>(base + o_dp);
     ctx->words = reinterpret_cast<unsigned long long*>(base + o_wd);
+    ctx->state = reinterpret_cast<unsigned long long*>(base + o_st);
     if (hipMemset(ctx->scratch, 0, total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         free_ctx(ctx);
         return SV_ERR_DEVICE;
@@ -269,7 +263,10 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
     if (!ctx || !a) return SV_ERR_INVALID_ARG;
     const sv_config& cfg = ctx->cfg;
     if (a->batch < 0 || a->gamma < 0 || a->total_draft < 0) return SV_ERR_INVALID_ARG;
-    if (a->batch == 0) return SV_OK;
+    if (a->batch == 0) {
+        ctx->last_schedule = SV_SCHEDULE_NONE;
+        return SV_OK;
+    }
     if (a->batch > cfg.max_batch || a->gamma > cfg.max_gamma) return SV_ERR_CAPACITY;
     if (a->vocab != cfg.vocab) return SV_ERR_INVALID_ARG;   // one vocabulary for draft and target
     if ((long)a->total_draft > (long)a->batch * a->gamma) return SV_ERR_INVALID_ARG;
@@ -323,11 +320,12 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
     P.flat_nv = rows * P.flat_vpr;
 
     sv::FusedParams F;
-    FusedGeometry fg{};
+    const FusedGeometry fg = fused_geometry(P.flat_vpr, a->gamma, a->batch, ctx->geo.nblocks, ctx->resident_fused);
     // the one-launch step is opt-in until it beats the two-kernel schedule
     const bool want_fused = (cfg.flags & SV_FLAG_ONE_LAUNCH) && !(cfg.flags & SV_FLAG_TWO_KERNEL);
-    const bool fused = aligned && want_fused && ctx->resident_fused > 0 &&
-                       fused_geometry(P.flat_nv, P.flat_vpr, a->batch, ctx->geo.nblocks, ctx->resident_fused, fg);
+    // every draw chunk must have an owner (at most kMaxOwnChunks per workgroup)
+    const bool owned = (long)a->batch * fg.chunks <= (long)fg.grid * sv::kMaxOwnChunks;
+    const bool fused = aligned && want_fused && owned && ctx->resident_fused > 0 && a->gamma <= sv::kMaxGammaFused;
 
     const bool prof = (cfg.flags & SV_FLAG_PROFILE) != 0;
     if (prof && ctx->prof_n == kProfileRing) {
@@ -340,14 +338,15 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
         if (++ctx->epoch == 0) ctx->epoch = 1;
         F.p = P;
         F.p.parts = nullptr;
-        F.nv = P.flat_nv;
         F.vpr = P.flat_vpr;
-        F.nrounds = fg.rounds;
+        F.pieces = fg.pieces;
+        F.items = fg.items;
         F.chunks = fg.chunks;
         F.epoch = ctx->epoch;
-        F.pieces = ctx->fpieces;
+        F.fpieces = ctx->fpieces;
         F.dparams = ctx->dparams;
         F.words = ctx->words;
+        F.state = ctx->state;
         void* kargs[] = {&F};
         const void* fn = (cfg.logits_dtype == SV_BF16)
                              ? reinterpret_cast<const void*>(&sv::fused_step_kernel<sv::BF16>)
@@ -380,6 +379,13 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
         ctx->prof_n++;
     }
     if (hipGetLastError() != hipSuccess) return SV_ERR_DEVICE;
+    ctx->last_schedule = fused ? SV_SCHEDULE_ONE_LAUNCH : (aligned ? SV_SCHEDULE_FLAT : SV_SCHEDULE_SPLIT);
+    return SV_OK;
+}
+
+int spec_verify_last_schedule(const sv_ctx* ctx, int32_t* schedule) {
+    if (!ctx || !schedule) return SV_ERR_INVALID_ARG;
+    *schedule = ctx->last_schedule;
     return SV_OK;
 }
 
@@ -391,7 +397,9 @@ int spec_verify_device_errors(sv_ctx* ctx, uint32_t* bits, int clear) {
     if (clear) {
         // also drop arrival counts a call with inconsistent offsets may have left behind
         const size_t n = (size_t)ctx->max_rows + 2 * (size_t)ctx->cfg.max_batch + 1;
-        if (hipMemset(ctx->row_cnt, 0, n * sizeof(uint32_t)) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+        if (hipMemset(ctx->row_cnt, 0, n * sizeof(uint32_t)) != hipSuccess ||
+            hipMemset(ctx->state, 0, (size_t)ctx->cfg.max_batch * sizeof(unsigned long long)) != hipSuccess ||
+            hipDeviceSynchronize() != hipSuccess)
             return SV_ERR_DEVICE;
     }
     return SV_OK;

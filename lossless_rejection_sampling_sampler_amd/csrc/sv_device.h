@@ -139,6 +139,11 @@ struct F32 {
     static __device__ __forceinline__ float load1(const void* row, long x) {
         return static_cast<const float*>(row)[x];
     }
+    static __device__ __forceinline__ uint32_t bits1(const void* row, long x) {
+        return static_cast<const uint32_t*>(row)[x];
+    }
+    static constexpr int kBits = 32;
+    static constexpr uint32_t kNegInfBits = 0xff800000u;
     static constexpr uint32_t kNegInfWord = 0xff800000u;
 };
 
@@ -154,6 +159,11 @@ struct BF16 {
     static __device__ __forceinline__ float load1(const void* row, long x) {
         return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(row)[x]) << 16);
     }
+    static __device__ __forceinline__ uint32_t bits1(const void* row, long x) {
+        return static_cast<uint32_t>(static_cast<const uint16_t*>(row)[x]);
+    }
+    static constexpr int kBits = 16;
+    static constexpr uint32_t kNegInfBits = 0xff80u;
     static constexpr uint32_t kNegInfWord = 0xff80ff80u;
 };
 
@@ -212,8 +222,11 @@ __constant__ double kExp2Table[64] = {
 // 2^y for y <= 0 (y = -inf allowed), relative error about 3e-16: y = k/64 + r
 // with |r| <= 1/128 exactly, 2^r by its Taylor series in r*ln2 to degree 5
 // (truncation below 4e-17), 2^(j/64) from the table (kept in LDS by the
-// caller), and the power of two by ldexp.  Results below 2^-1070 are 0.
+// caller), and the power of two by ldexp.  y is clamped at -1080 first, whose
+// power of two is below the smallest double, so such results (and NaN inputs)
+// are 0.
 __device__ __forceinline__ double exp2_nonpos(double y, const double* tab) {
+    y = fmax(y, -1080.0);
     const double kf = rint(y * 64.0);
     const double r = fma(kf, -0.015625, y);
     double p = fma(r, 0.0013333558146428443, 0.009618129107628477);
@@ -222,47 +235,117 @@ __device__ __forceinline__ double exp2_nonpos(double y, const double* tab) {
     p = fma(r, p, 0.6931471805599453);
     p = fma(r, p, 1.0);
     const int k = static_cast<int>(kf);
-    const double res = ldexp(tab[k & 63] * p, k >> 6);
-    return (y > -1070.0) ? res : 0.0;
+    return ldexp(tab[k & 63] * p, k >> 6);
 }
 
 // ----------------------------------------------------------------- reductions
+// Wave reductions use DPP lane moves inside each 16-lane row (quad swaps, then
+// the half-row and row mirrors, after which every lane of a row holds the row's
+// result) and combine the four rows in a fixed order with readlane, so every
+// lane receives the same value.
+constexpr int kDppQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+template <int Ctrl, int RowMask = 0xf>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+    return __builtin_amdgcn_update_dpp(old, v, Ctrl, RowMask, 0xf, false);
+}
+template <int Ctrl, int RowMask = 0xf>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+    return __int_as_float(dpp_i<Ctrl, RowMask>(__float_as_int(old), __float_as_int(v)));
+}
+template <int Ctrl, int RowMask = 0xf>
+__device__ __forceinline__ double dpp_d(double old, double v) {
+    const long long o = __double_as_longlong(old), x = __double_as_longlong(v);
+    const int lo = dpp_i<Ctrl, RowMask>(static_cast<int>(o), static_cast<int>(x));
+    const int hi = dpp_i<Ctrl, RowMask>(static_cast<int>(o >> 32), static_cast<int>(x >> 32));
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+__device__ __forceinline__ int rdlane(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ float rdlane(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
+__device__ __forceinline__ double rdlane(double v, int l) {
+    const long long x = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane(static_cast<int>(x), l);
+    const int hi = __builtin_amdgcn_readlane(static_cast<int>(x >> 32), l);
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+
+// Row-wide combine with op (all 16 lanes of a row end with the row result),
+// then the four rows in order 0, 1, 2, 3.
+#define SV_WAVE_REDUCE(T, DPP, OP, v)                                   \
+    do {                                                                \
+        v = OP(v, DPP<kDppQuadSwap1>(v, v));                            \
+        v = OP(v, DPP<kDppQuadSwap2>(v, v));                            \
+        v = OP(v, DPP<kDppRowHalfMirror>(v, v));                        \
+        v = OP(v, DPP<kDppRowMirror>(v, v));                            \
+        const T r0 = rdlane(v, 15), r1 = rdlane(v, 31), r2 = rdlane(v, 47), r3 = rdlane(v, 63); \
+        v = OP(OP(OP(r0, r1), r2), r3);                                 \
+    } while (0)
+
+__device__ __forceinline__ float op_maxf(float a, float b) { return fmaxf(a, b); }
+__device__ __forceinline__ double op_addd(double a, double b) { return a + b; }
+__device__ __forceinline__ int op_addi(int a, int b) { return a + b; }
+__device__ __forceinline__ int op_mini(int a, int b) { return min(a, b); }
+__device__ __forceinline__ int op_maxi(int a, int b) { return max(a, b); }
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    SV_WAVE_REDUCE(float, dpp_f, op_maxf, v);
     return v;
 }
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    SV_WAVE_REDUCE(double, dpp_d, op_addd, v);
     return v;
 }
 __device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    SV_WAVE_REDUCE(int, dpp_i, op_addi, v);
     return v;
 }
 __device__ __forceinline__ int wave_min_int(int v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+    SV_WAVE_REDUCE(int, dpp_i, op_mini, v);
     return v;
 }
 __device__ __forceinline__ int wave_max_int(int v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+    SV_WAVE_REDUCE(int, dpp_i, op_maxi, v);
     return v;
 }
 // (value, index) argmax: larger value wins, lower index on ties.
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
     if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
 }
+template <int Ctrl>
+__device__ __forceinline__ void argmax_dpp_step(float& v, int& i) {
+    const float v2 = dpp_f<Ctrl>(v, v);
+    const int i2 = dpp_i<Ctrl>(i, i);
+    argmax_merge(v, i, v2, i2);
+}
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        float v2 = __shfl_xor(v, o, 64);
-        int i2 = __shfl_xor(i, o, 64);
-        argmax_merge(v, i, v2, i2);
-    }
+    argmax_dpp_step<kDppQuadSwap1>(v, i);
+    argmax_dpp_step<kDppQuadSwap2>(v, i);
+    argmax_dpp_step<kDppRowHalfMirror>(v, i);
+    argmax_dpp_step<kDppRowMirror>(v, i);
+    float rv = rdlane(v, 15);
+    int ri = rdlane(i, 15);
+    argmax_merge(rv, ri, rdlane(v, 31), rdlane(i, 31));
+    argmax_merge(rv, ri, rdlane(v, 47), rdlane(i, 47));
+    argmax_merge(rv, ri, rdlane(v, 63), rdlane(i, 63));
+    v = rv;
+    i = ri;
+}
+// Inclusive prefix sum over the wave's lanes (row shifts 1, 2, 4, 8, then the
+// row broadcasts 15 and 31).
+__device__ __forceinline__ double wave_inclusive_scan(double v) {
+    v += dpp_d<kDppRowShr1>(0.0, v);
+    v += dpp_d<kDppRowShr1 + 1>(0.0, v);
+    v += dpp_d<kDppRowShr1 + 3>(0.0, v);
+    v += dpp_d<kDppRowShr1 + 7>(0.0, v);
+    v += dpp_d<kDppRowBcast15, 0xa>(0.0, v);
+    v += dpp_d<kDppRowBcast31, 0xc>(0.0, v);
+    return v;
 }
 
 // Workgroup reductions: every thread receives the result (fixed combination order).
@@ -342,11 +425,7 @@ __device__ __forceinline__ void wg_argmax(float& v, int& i, RedScratch& s) {
 // Inclusive prefix sum over the workgroup (thread order); also returns the total.
 __device__ __forceinline__ double wg_inclusive_scan(double v, double& total, RedScratch& s) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        double y = __shfl_up(v, o, 64);
-        if (lane >= o) v += y;
-    }
+    v = wave_inclusive_scan(v);
     if (lane == 63) s.d[w] = v;
     __syncthreads();
     double before = 0.0, tot = 0.0;
@@ -431,7 +510,7 @@ __device__ __forceinline__ void load_batch(v4u* buf, const v4u* vp, long first, 
 // 16-byte aligned element), adds the scalar head (piece 0) and tail (last piece),
 // publishes the piece and, for the last piece / last row, merges and resolves.
 template <typename E>
-__device__ void row_piece(const Params& P, int t, long v0, long v1, int piece, int npieces, RowShared& sh) {
+__device__ __forceinline__ void row_piece(const Params& P, int t, long v0, long v1, int piece, int npieces, RowShared& sh) {
     const int tid = threadIdx.x;
     const int V = P.vocab;
 
@@ -683,43 +762,17 @@ __global__ __launch_bounds__(kThreads) void rows_flat_kernel(Params P) {
 
 // ----------------------------------------------------------------- draw kernel
 // The 8 tokens x0 .. x0+7 of one lane in a draw block.
-template <typename E>
-__device__ __forceinline__ void load_draw8(const typename E::T* lrow, const float* qrow, long x0,
-                                           int V, bool lalign, bool qalign, float* l, float* q) {
-    if (x0 + kDrawPerLane <= V && lalign) {
-        const v4u* lp = reinterpret_cast<const v4u*>(lrow + x0);
-#pragma unroll
-        for (int u = 0; u < kDrawPerLane / E::kPerVec; ++u)
-            E::decode(__builtin_nontemporal_load(lp + u), l + u * E::kPerVec);
-    } else {
-#pragma unroll
-        for (int k = 0; k < kDrawPerLane; ++k)
-            l[k] = (x0 + k < V) ? E::load1(lrow, x0 + k) : -INFINITY;
-    }
-    if (qrow) {
-        if (x0 + kDrawPerLane <= V && qalign) {
-            const v4u* qp = reinterpret_cast<const v4u*>(qrow + x0);
-#pragma unroll
-            for (int u = 0; u < kDrawPerLane / 4; ++u) {
-                const v4u w = __builtin_nontemporal_load(qp + u);
-                q[4 * u + 0] = __uint_as_float(w.x); q[4 * u + 1] = __uint_as_float(w.y);
-                q[4 * u + 2] = __uint_as_float(w.z); q[4 * u + 3] = __uint_as_float(w.w);
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < kDrawPerLane; ++k) q[k] = (x0 + k < V) ? qrow[x0 + k] : 0.0f;
-        }
-    }
-}
-
 struct DrawShared {
     RedScratch red;
     double tab[64];
     double w[kMaxDrawBlocks];
     int list[kMaxDrawBlocks];
+    double sums[kWaves][3];      // per wave: se, ea, qa
+    int counts[kWaves][2];       // per wave: blocks with many marginal tokens, with any
+    double pick_before[kWaves][2];
+    int pick_block[kWaves][2];   // per wave: first crossing block, last positive block
     int n;
     int flag;
-    double base;
 };
 
 // Everything a workgroup needs to work on one request's draw row.
@@ -730,177 +783,345 @@ struct DrawRow {
     float v;             // uniform of the draw
     double m;            // row max (raw logits)
     double c2;           // log2(e) / T
+    double mc2;          // m * c2
     double z32;          // normaliser from the fp32-exponential pass
     const typename E::T* lrow;
     const float* qrow;   // residual: q row, else nullptr
     bool lalign, qalign;
 };
 
-// Per-block sums of draw blocks jfirst + wave, + jstride, ... < jend (one
-// 512-token block per wave at a time), written to recs with device-scope stores.
+// e = exp((l - m) / T) of one token, in fp64 (the same expression everywhere).
 template <typename E>
-__device__ void draw_blocks(const DrawRow<E>& d, int V, BlockRec* recs, int jfirst, int jstride, int jend,
-                            const double* tab) {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const bool residual = (d.kind == kDrawResidual);
-    const double invZ32 = 1.0 / d.z32;
-    for (int j = jfirst + wv; j < jend; j += jstride) {
-        const long x0 = (long)j * kBlockElems + (long)lane * kDrawPerLane;
-        float l[kDrawPerLane], q[kDrawPerLane];
-        load_draw8<E>(d.lrow, d.qrow, x0, V, d.lalign, d.qalign, l, q);
-        double se = 0.0, ea = 0.0, qa = 0.0;
-        int nm = 0;
-        // this lane's first two marginal tokens (kMarginSlots == 2), in token order
-        double e_m0 = 0.0, e_m1 = 0.0;
-        float q_m0 = 0.0f, q_m1 = 0.0f;
-        int x_m0 = -1, x_m1 = -1;
+__device__ __forceinline__ double draw_e(const DrawRow<E>& d, float l, const double* tab) {
+    return exp2_nonpos(fma(static_cast<double>(l), d.c2, -d.mc2), tab);
+}
+
+// One lane's 8 tokens of a draw block as loaded (raw element bits), so that
+// several blocks can be in flight before any is decoded.
+template <typename E>
+struct Raw8 {
+    v4u l[kDrawPerLane / E::kPerVec];
+    v4u q[kDrawPerLane / 4];
+};
+
+// Issues the loads of tokens [x0, x0 + 8) element by element (logits past V
+// read as -inf, q as 0): the tail block and rows that are not 16-byte aligned.
+template <typename E>
+__device__ __forceinline__ void issue_draw8_any(const DrawRow<E>& d, long x0, int V, Raw8<E>& r) {
+    constexpr int NL = kDrawPerLane / E::kPerVec;
+    const bool full = x0 + kDrawPerLane <= V;
+    if (full && d.lalign) {
+        const v4u* lp = reinterpret_cast<const v4u*>(d.lrow + x0);
+#pragma unroll
+        for (int u = 0; u < NL; ++u) r.l[u] = __builtin_nontemporal_load(lp + u);
+    } else {
+        uint32_t w[4 * NL];
+#pragma unroll
+        for (int k = 0; k < 4 * NL; ++k) w[k] = 0u;
 #pragma unroll
         for (int k = 0; k < kDrawPerLane; ++k) {
-            const double e = exp2_nonpos((static_cast<double>(l[k]) - d.m) * d.c2, tab);
-            se += e;
-            if (residual && e > 0.0) {
-                const double pz = e * invZ32;
-                const double qd = static_cast<double>(q[k]);
-                const double dd = pz - qd;
-                if (dd > kSignMargin * pz) {
-                    ea += e; qa += qd;
-                } else if (dd >= -kSignMargin * pz) {
-                    if (nm == 0) { e_m0 = e; q_m0 = q[k]; x_m0 = static_cast<int>(x0) + k; }
-                    else if (nm == 1) { e_m1 = e; q_m1 = q[k]; x_m1 = static_cast<int>(x0) + k; }
-                    nm += 1;
-                }
-            }
+            const uint32_t bits = (x0 + k < V) ? E::bits1(d.lrow, x0 + k) : E::kNegInfBits;
+            if (E::kBits == 16) w[k >> 1] |= bits << (16 * (k & 1));
+            else w[k] = bits;
         }
-        se = wave_sum(se);
-        int nmw = 0;
-        if (residual) {
-            ea = wave_sum(ea);
-            qa = wave_sum(qa);
-            nmw = wave_sum_int(nm);
-        }
-        BlockRec* rec = &recs[j];
-        if (lane == 0) {
-            st_coherent(&rec->se, se);
-            st_coherent(&rec->ea, ea);
-            st_coherent(&rec->qa, qa);
-            st_coherent(&rec->nm, nmw);
-        }
-        if (nmw > 0 && nmw <= kMarginSlots) {
-            // slots in token order: exclusive prefix of the per-lane counts
-            int incl = nm;
 #pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int y = __shfl_up(incl, o, 64);
-                if (lane >= o) incl += y;
-            }
-            const int before = incl - nm;
-            if (nm > 0 && before < kMarginSlots) {
-                st_coherent(&rec->mx[before], x_m0);
-                st_coherent(&rec->mq[before], q_m0);
-                st_coherent(&rec->me[before], e_m0);
-            }
-            if (nm > 1 && before + 1 < kMarginSlots) {
-                st_coherent(&rec->mx[before + 1], x_m1);
-                st_coherent(&rec->mq[before + 1], q_m1);
-                st_coherent(&rec->me[before + 1], e_m1);
+        for (int u = 0; u < NL; ++u) r.l[u] = v4u{w[4 * u], w[4 * u + 1], w[4 * u + 2], w[4 * u + 3]};
+    }
+    if (d.qrow) {
+        if (full && d.qalign) {
+            const v4u* qp = reinterpret_cast<const v4u*>(d.qrow + x0);
+#pragma unroll
+            for (int u = 0; u < kDrawPerLane / 4; ++u) r.q[u] = __builtin_nontemporal_load(qp + u);
+        } else {
+            uint32_t w[kDrawPerLane];
+#pragma unroll
+            for (int k = 0; k < kDrawPerLane; ++k)
+                w[k] = (x0 + k < V) ? __float_as_uint(d.qrow[x0 + k]) : 0u;
+#pragma unroll
+            for (int u = 0; u < kDrawPerLane / 4; ++u) r.q[u] = v4u{w[4 * u], w[4 * u + 1], w[4 * u + 2], w[4 * u + 3]};
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kDrawPerLane / 4; ++u) r.q[u] = v4u(0u);
+    }
+}
+
+// Vector loads of tokens [x0, x0 + 8) of a full block of 16-byte aligned rows.
+template <typename E, bool with_q>
+__device__ __forceinline__ void issue_draw8_fast(const DrawRow<E>& d, long x0, Raw8<E>& r) {
+    const v4u* lp = reinterpret_cast<const v4u*>(d.lrow + x0);
+#pragma unroll
+    for (int u = 0; u < kDrawPerLane / E::kPerVec; ++u) r.l[u] = __builtin_nontemporal_load(lp + u);
+    if (with_q) {
+        const v4u* qp = reinterpret_cast<const v4u*>(d.qrow + x0);
+#pragma unroll
+        for (int u = 0; u < kDrawPerLane / 4; ++u) r.q[u] = __builtin_nontemporal_load(qp + u);
+    }
+}
+
+template <typename E>
+__device__ __forceinline__ void decode_draw8(const Raw8<E>& r, bool with_q, float* l, float* q) {
+#pragma unroll
+    for (int u = 0; u < kDrawPerLane / E::kPerVec; ++u) E::decode(r.l[u], l + u * E::kPerVec);
+#pragma unroll
+    for (int u = 0; u < kDrawPerLane / 4; ++u) {
+        if (with_q) F32::decode(r.q[u], q + 4 * u);
+        else q[4 * u] = q[4 * u + 1] = q[4 * u + 2] = q[4 * u + 3] = 0.0f;
+    }
+}
+
+// Sums of one loaded block, written to its record with device-scope stores.
+// Residual rows split the tokens three ways with the fp32-pass normaliser:
+// clearly positive residual (e / Z32 * (1 - margin) > q: summed into ea and qa),
+// clearly non-positive (e / Z32 * (1 + margin) < q: dropped) and marginal (the
+// rest: counted, the first kMarginSlots kept inline).  Branch-free except for
+// the marginal capture, which only runs when some lane has a marginal token.
+// Wave-uniform call.
+template <typename E, bool kResidual>
+__device__ __forceinline__ void block_record(const DrawRow<E>& d, const Raw8<E>& r, long x0, double apos,
+                                             double aneg, const double* tab, BlockRec* rec) {
+    const int lane = threadIdx.x & 63;
+    constexpr bool residual = kResidual;
+    float l[kDrawPerLane], q[kDrawPerLane];
+    decode_draw8<E>(r, residual, l, q);
+    double se = 0.0, ea = 0.0, qa = 0.0;
+    uint32_t mmask = 0u;
+    if (residual) {
+#pragma unroll
+        for (int k = 0; k < kDrawPerLane; ++k) {
+            const double e = draw_e<E>(d, l[k], tab);
+            const double qd = static_cast<double>(q[k]);
+            se += e;
+            const bool pos = e * apos > qd;
+            const bool neg = e * aneg < qd;
+            ea += pos ? e : 0.0;
+            qa += pos ? qd : 0.0;
+            mmask |= static_cast<uint32_t>(!pos && !neg && e > 0.0) << k;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < kDrawPerLane; ++k) se += draw_e<E>(d, l[k], tab);
+    }
+    se = wave_sum(se);
+    int nmw = 0;
+    if (residual) {
+        ea = wave_sum(ea);
+        qa = wave_sum(qa);
+        if (__ballot(mmask != 0u) != 0ull) nmw = wave_sum_int(__popc(mmask));
+    }
+    if (lane == 0) {
+        st_coherent(&rec->se, se);
+        st_coherent(&rec->ea, ea);
+        st_coherent(&rec->qa, qa);
+        st_coherent(&rec->nm, nmw);
+    }
+    if (nmw > 0 && nmw <= kMarginSlots) {
+        // slots in token order: exclusive prefix of the per-lane counts
+        const int nm = __popc(mmask);
+        int incl = nm;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += y;
+        }
+        int slot = incl - nm;
+#pragma unroll
+        for (int k = 0; k < kDrawPerLane; ++k) {
+            if ((mmask >> k) & 1u) {
+                if (slot < kMarginSlots) {
+                    st_coherent(&rec->mx[slot], static_cast<int>(x0) + k);
+                    st_coherent(&rec->mq[slot], q[k]);
+                    st_coherent(&rec->me[slot], draw_e<E>(d, l[k], tab));
+                }
+                ++slot;
             }
         }
     }
 }
 
-// Select for one request once all its draw blocks are recorded: rebuilds the
-// exact fp64 normaliser, fixes every block's weight (re-evaluating blocks with
-// several marginal-sign tokens, or all blocks if the fp32-pass normaliser is off
-// by more than half the margin), finds the block holding v * S with a block scan
-// and the token with a token scan of that block.  Returns the token (uniform).
+constexpr int kDrawInFlight = 4;         // draw blocks per wave with loads in flight together
+
+// Per-block sums of draw blocks jfirst + wave, + jstride, ... < jend, written to
+// recs.  Full blocks of aligned rows: each wave issues the vector loads of up to
+// kDrawInFlight of its blocks before it works on the first.  Other blocks: one
+// at a time, element by element.
+template <typename E, bool kResidual>
+__device__ __forceinline__ void draw_blocks_kind(const DrawRow<E>& d, int V, BlockRec* recs, int jfirst, int jstride,
+                                                 int jend, const double* tab) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const double invZ32 = 1.0 / d.z32;
+    const double apos = invZ32 * (1.0 - kSignMargin), aneg = invZ32 * (1.0 + kSignMargin);
+    const bool fastrow = d.lalign && (!kResidual || d.qalign);
+    const int jfull = V / kBlockElems;                  // blocks entirely inside the row
+    for (int j = jfirst + wv; j < jend; j += kDrawInFlight * jstride) {
+        const int jlast = min(j + (kDrawInFlight - 1) * jstride, jend - 1);
+        if (fastrow && jlast < jfull) {
+            Raw8<E> r[kDrawInFlight];
+#pragma unroll
+            for (int s = 0; s < kDrawInFlight; ++s) {
+                // past the end: reload the wave's first block (in bounds, never recorded)
+                const int js = (j + s * jstride < jend) ? j + s * jstride : j;
+                issue_draw8_fast<E, kResidual>(d, (long)js * kBlockElems + (long)lane * kDrawPerLane, r[s]);
+            }
+#pragma unroll
+            for (int s = 0; s < kDrawInFlight; ++s) {
+                const int js = j + s * jstride;
+                if (js < jend)
+                    block_record<E, kResidual>(d, r[s], (long)js * kBlockElems + (long)lane * kDrawPerLane, apos, aneg,
+                                               tab, &recs[js]);
+            }
+        } else {
+            for (int s = 0; s < kDrawInFlight; ++s) {
+                const int js = j + s * jstride;
+                if (js >= jend) break;
+                Raw8<E> r;
+                const long x0 = (long)js * kBlockElems + (long)lane * kDrawPerLane;
+                issue_draw8_any<E>(d, x0, V, r);
+                block_record<E, kResidual>(d, r, x0, apos, aneg, tab, &recs[js]);
+            }
+        }
+    }
+}
+
 template <typename E>
-__device__ int draw_select(const DrawRow<E>& d, int V, int NB, const BlockRec* recs, DrawShared& sh,
+__device__ __forceinline__ void draw_blocks(const DrawRow<E>& d, int V, BlockRec* recs, int jfirst, int jstride, int jend,
+                            const double* tab) {
+    if (d.kind == kDrawResidual) draw_blocks_kind<E, true>(d, V, recs, jfirst, jstride, jend, tab);
+    else draw_blocks_kind<E, false>(d, V, recs, jfirst, jstride, jend, tab);
+}
+
+// Select for one request once all its draw blocks are recorded.  The
+// workgroup rebuilds the exact fp64 normaliser Z64 and every block's weight
+// (e / Z64 - q summed over the clearly positive tokens plus the inline marginal
+// ones; blocks with more marginal tokens than slots, or every block when the
+// fp32-pass normaliser is off by more than half the margin, are re-evaluated
+// from their tokens), finds the block holding v * S by a block scan, and wave 0
+// finds the token with a token scan of that block.  Returns the token in wave 0
+// (other waves: unspecified).
+template <typename E>
+__device__ __forceinline__ int draw_select(const DrawRow<E>& d, int V, int NB, const BlockRec* recs, DrawShared& sh,
                            uint32_t* err) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     constexpr int kPer = kMaxDrawBlocks / kThreads;    // blocks per thread (contiguous)
-    double se_t[kPer];
-    double zpart = 0.0;
+    const bool residual = (d.kind == kDrawResidual);
+    // every field of this thread's records in one round of loads
+    double se_t[kPer], ea_t[kPer], qa_t[kPer], me0_t[kPer], me1_t[kPer];
+    float mq0_t[kPer], mq1_t[kPer];
+    int nm_t[kPer];
 #pragma unroll
     for (int r = 0; r < kPer; ++r) {
         const int j = tid * kPer + r;
-        se_t[r] = (j < NB) ? ld_coherent(&recs[j].se) : 0.0;
-        zpart += se_t[r];
+        const bool in = j < NB;
+        const BlockRec* rc = &recs[in ? j : 0];
+        se_t[r] = in ? ld_coherent(&rc->se) : 0.0;
+        ea_t[r] = qa_t[r] = me0_t[r] = me1_t[r] = 0.0;
+        mq0_t[r] = mq1_t[r] = 0.0f;
+        nm_t[r] = 0;
+        if (residual && in) {
+            ea_t[r] = ld_coherent(&rc->ea);
+            qa_t[r] = ld_coherent(&rc->qa);
+            nm_t[r] = ld_coherent(&rc->nm);
+            me0_t[r] = ld_coherent(&rc->me[0]);
+            me1_t[r] = ld_coherent(&rc->me[1]);
+            mq0_t[r] = ld_coherent(&rc->mq[0]);
+            mq1_t[r] = ld_coherent(&rc->mq[1]);
+        }
     }
-    const double Z64 = wg_sum(zpart, sh.red);
-    const double invZ64 = 1.0 / Z64;
-    const bool residual = (d.kind == kDrawResidual);
-    int kind = d.kind;
-    if (tid == 0) sh.n = 0;
+    // ---- one workgroup reduction: Z64, and the counts that pick the path
+    double zpart = 0.0;
+    int nbig = 0;
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+        zpart += se_t[r];
+        nbig += (nm_t[r] > kMarginSlots);
+    }
+    zpart = wave_sum(zpart);
+    nbig = wave_sum_int(nbig);
+    if (lane == 0) { sh.sums[wv][0] = zpart; sh.counts[wv][0] = nbig; }
     __syncthreads();
+    double Z64 = 0.0;
+    int NBIG = 0;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) { Z64 += sh.sums[k][0]; NBIG += sh.counts[k][0]; }
+    const double invZ64 = 1.0 / Z64;
+    int kind = d.kind;
+    double wt[kPer];
     if (residual) {
         const bool full = !(fabs(Z64 - d.z32) <= 0.5 * kSignMargin * Z64);
+        if (!full && NBIG == 0) {
 #pragma unroll
-        for (int r = 0; r < kPer; ++r) {
-            const int j = tid * kPer + r;
-            if (j < NB) {
-                const int nm = ld_coherent(&recs[j].nm);
-                if (!full && nm <= kMarginSlots) {
-                    double w = ld_coherent(&recs[j].ea) * invZ64 - ld_coherent(&recs[j].qa);
-                    for (int s = 0; s < nm; ++s)
-                        w += fmax(ld_coherent(&recs[j].me[s]) * invZ64 -
-                                  static_cast<double>(ld_coherent(&recs[j].mq[s])), 0.0);
-                    sh.w[j] = w;
-                } else {
-                    sh.list[atomicAdd(&sh.n, 1)] = j;
+            for (int r = 0; r < kPer; ++r) {
+                // a marginal slot is only meaningful when the block recorded it
+                double w = ea_t[r] * invZ64 - qa_t[r];
+                if (nm_t[r] > 0) w += fmax(me0_t[r] * invZ64 - static_cast<double>(mq0_t[r]), 0.0);
+                if (nm_t[r] > 1) w += fmax(me1_t[r] * invZ64 - static_cast<double>(mq1_t[r]), 0.0);
+                wt[r] = w;
+            }
+        } else {
+            // rare: re-evaluate the listed blocks from their tokens
+            if (tid == 0) sh.n = 0;
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < kPer; ++r) {
+                const int j = tid * kPer + r;
+                if (j < NB) {
+                    if (!full && nm_t[r] <= kMarginSlots) {
+                        double w = ea_t[r] * invZ64 - qa_t[r];
+                        if (nm_t[r] > 0) w += fmax(me0_t[r] * invZ64 - static_cast<double>(mq0_t[r]), 0.0);
+                        if (nm_t[r] > 1) w += fmax(me1_t[r] * invZ64 - static_cast<double>(mq1_t[r]), 0.0);
+                        sh.w[j] = w;
+                    } else {
+                        sh.list[atomicAdd(&sh.n, 1)] = j;
+                    }
                 }
             }
-        }
-        __syncthreads();
-        // blocks with several marginal tokens (or an inexact fp32-pass normaliser)
-        const int n_list = sh.n;
-        for (int li = wv; li < n_list; li += kWaves) {
-            const int j = sh.list[li];
-            const long x0 = (long)j * kBlockElems + (long)lane * kDrawPerLane;
-            float l[kDrawPerLane], q[kDrawPerLane];
-            load_draw8<E>(d.lrow, d.qrow, x0, V, d.lalign, d.qalign, l, q);
-            double w = 0.0;
+            __syncthreads();
+            const int n_list = sh.n;
+            for (int li = wv; li < n_list; li += kWaves) {
+                const int j = sh.list[li];
+                const long x0 = (long)j * kBlockElems + (long)lane * kDrawPerLane;
+                Raw8<E> raw;
+                issue_draw8_any<E>(d, x0, V, raw);
+                float l[kDrawPerLane], q[kDrawPerLane];
+                decode_draw8<E>(raw, true, l, q);
+                double w = 0.0;
 #pragma unroll
-            for (int k = 0; k < kDrawPerLane; ++k) {
-                const double e = exp2_nonpos((static_cast<double>(l[k]) - d.m) * d.c2, sh.tab);
-                w += fmax(e * invZ64 - static_cast<double>(q[k]), 0.0);
+                for (int k = 0; k < kDrawPerLane; ++k)
+                    w += fmax(draw_e<E>(d, l[k], sh.tab) * invZ64 - static_cast<double>(q[k]), 0.0);
+                w = wave_sum(w);
+                if (lane == 0) sh.w[j] = w;
             }
-            w = wave_sum(w);
-            if (lane == 0) sh.w[j] = w;
-        }
-        __syncthreads();
-        double wp = 0.0;
+            __syncthreads();
 #pragma unroll
-        for (int r = 0; r < kPer; ++r) {
-            const int j = tid * kPer + r;
-            if (j < NB) wp += sh.w[j];
+            for (int r = 0; r < kPer; ++r) {
+                const int j = tid * kPer + r;
+                wt[r] = (j < NB) ? sh.w[j] : 0.0;
+            }
         }
-        const double Sres = wg_sum(wp, sh.red);
-        if (!(Sres > 0.0)) kind = kDrawDegenerate;      // residual lost to rounding: use p
-    }
-    if (kind != kDrawResidual) {
+    } else {
 #pragma unroll
-        for (int r = 0; r < kPer; ++r) {
-            const int j = tid * kPer + r;
-            if (j < NB) sh.w[j] = se_t[r];
-        }
+        for (int r = 0; r < kPer; ++r) wt[r] = se_t[r];
     }
-    __syncthreads();
-    // block-level inclusive scan (thread-contiguous blocks)
-    double wt[kPer];
+    // ---- block scan (thread-contiguous blocks)
     double own = 0.0;
 #pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-        const int j = tid * kPer + r;
-        wt[r] = (j < NB) ? sh.w[j] : 0.0;
-        own += wt[r];
-    }
+    for (int r = 0; r < kPer; ++r) own += wt[r];
     double Stot;
-    const double incl = wg_inclusive_scan(own, Stot, sh.red);
+    double incl = wg_inclusive_scan(own, Stot, sh.red);
+    if (residual && !(Stot > 0.0)) {
+        // residual lost to rounding: draw from p itself
+        kind = kDrawDegenerate;
+        own = 0.0;
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) { wt[r] = se_t[r]; own += wt[r]; }
+        incl = wg_inclusive_scan(own, Stot, sh.red);
+    }
     const double tsel = static_cast<double>(d.v) * Stot;
-    int cand = 0x7fffffff;
-    int lastpos = -1;
-    double cand_before = 0.0;
+    // this thread's first block whose inclusive sum passes tsel, and its last
+    // block of positive weight, each with the sum before it
+    int cand = -1, lastpos = -1;
+    double cand_before = 0.0, last_before = 0.0;
     {
         double run = incl - own;
 #pragma unroll
@@ -908,61 +1129,76 @@ __device__ int draw_select(const DrawRow<E>& d, int V, int NB, const BlockRec* r
             const int j = tid * kPer + r;
             const double before = run;
             run += wt[r];
-            if (j < NB && wt[r] > 0.0) lastpos = j;
-            if (j < NB && cand == 0x7fffffff && run > tsel) { cand = j; cand_before = before; }
+            if (j < NB && wt[r] > 0.0) { lastpos = j; last_before = before; }
+            if (j < NB && cand < 0 && run > tsel) { cand = j; cand_before = before; }
         }
     }
-    int jsel = wg_min_int(cand, sh.red);
-    if (cand == jsel && jsel != 0x7fffffff) sh.base = cand_before;   // the owner of the first block
-    __syncthreads();
-    bool block_fallback = false;
-    if (jsel == 0x7fffffff) {           // rounding left no block above v * S
-        jsel = wg_max_int(lastpos, sh.red);
-        block_fallback = true;
-        if (tid == 0 && jsel >= 0) {
-            double bsum = 0.0;
-            for (int j = 0; j < jsel; ++j) bsum += sh.w[j];
-            sh.base = bsum;
+    // per wave: the lowest lane with a crossing, the highest with a positive block
+    {
+        const unsigned long long cm = __ballot(cand >= 0), lm = __ballot(lastpos >= 0);
+        const int cl = cm ? __ffsll(static_cast<long long>(cm)) - 1 : 0;
+        const int ll = lm ? 63 - __clzll(static_cast<long long>(lm)) : 0;
+        const int cw = rdlane(cand, cl);
+        const double cbw = rdlane(cand_before, cl);
+        const int lw = rdlane(lastpos, ll);
+        const double lbw = rdlane(last_before, ll);
+        if (lane == 0) {
+            sh.pick_block[wv][0] = cm ? cw : -1;
+            sh.pick_before[wv][0] = cbw;
+            sh.pick_block[wv][1] = lm ? lw : -1;
+            sh.pick_before[wv][1] = lbw;
         }
-        __syncthreads();
+    }
+    __syncthreads();
+    int jsel = -1;
+    double base = 0.0;
+    bool block_fallback = false;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+        if (jsel < 0 && sh.pick_block[k][0] >= 0) { jsel = sh.pick_block[k][0]; base = sh.pick_before[k][0]; }
+    }
+    if (jsel < 0) {                     // rounding left no block above v * S: the last positive one
+        block_fallback = true;
+#pragma unroll
+        for (int k = 0; k < kWaves; ++k) {
+            if (sh.pick_block[k][1] >= 0) { jsel = sh.pick_block[k][1]; base = sh.pick_before[k][1]; }
+        }
     }
     if (jsel < 0) {                     // no positive finite weight (non-finite logits)
         jsel = 0;
-        block_fallback = true;
-        if (tid == 0) { sh.base = 0.0; flag_error(err, kErrNonFinite); }
-        __syncthreads();
+        base = 0.0;
+        if (tid == 0) flag_error(err, kErrNonFinite);
     }
-    const double base = sh.base;
+    if (wv != 0) return -1;
 
-    // token-level scan of the selected block: 2 tokens per thread
-    constexpr int kTok = kBlockElems / kThreads;
-    const long x0 = (long)jsel * kBlockElems + (long)tid * kTok;
-    double w[kTok];
+    // ---- token scan of the selected block by wave 0: 8 tokens per lane
+    const long x0 = (long)jsel * kBlockElems + (long)lane * kDrawPerLane;
+    Raw8<E> raw;
+    issue_draw8_any<E>(d, x0, V, raw);
+    float l[kDrawPerLane], q[kDrawPerLane];
+    const bool res_w = (kind == kDrawResidual);
+    decode_draw8<E>(raw, res_w, l, q);
+    double w[kDrawPerLane];
     double tsum = 0.0;
 #pragma unroll
-    for (int k = 0; k < kTok; ++k) {
-        const long x = x0 + k;
-        double e = 0.0, qd = 0.0;
-        if (x < V) {
-            e = exp2_nonpos((static_cast<double>(E::load1(d.lrow, x)) - d.m) * d.c2, sh.tab);
-            if (kind == kDrawResidual) qd = static_cast<double>(d.qrow[x]);
-        }
-        w[k] = (kind == kDrawResidual) ? fmax(e * invZ64 - qd, 0.0) : e;
+    for (int k = 0; k < kDrawPerLane; ++k) {
+        const double e = draw_e<E>(d, l[k], sh.tab);
+        w[k] = res_w ? fmax(e * invZ64 - static_cast<double>(q[k]), 0.0) : e;
+        if (x0 + k >= V) w[k] = 0.0;
         tsum += w[k];
     }
-    double dummy;
-    double run = base + (wg_inclusive_scan(tsum, dummy, sh.red) - tsum);
+    double run = base + (wave_inclusive_scan(tsum) - tsum);
     int ycand = 0x7fffffff, ylast = -1;
 #pragma unroll
-    for (int k = 0; k < kTok; ++k) {
+    for (int k = 0; k < kDrawPerLane; ++k) {
         run += w[k];
         const int x = static_cast<int>(x0) + k;
         if (w[k] > 0.0) ylast = x;
         if (!block_fallback && ycand == 0x7fffffff && run > tsel) ycand = x;
     }
-    int y = wg_min_int(ycand, sh.red);
-    if (y == 0x7fffffff) y = wg_max_int(ylast, sh.red);
-    if (y < 0) y = min(V - 1, static_cast<int>(jsel) * kBlockElems + kBlockElems - 1);
+    int y = wave_min_int(ycand);
+    if (y == 0x7fffffff) y = wave_max_int(ylast);
+    if (y < 0) y = min(V - 1, jsel * kBlockElems + kBlockElems - 1);
     return y;
 }
 
@@ -974,6 +1210,7 @@ __device__ __forceinline__ void init_draw_row(DrawRow<E>& d, const Params& P, in
     d.v = v;
     d.m = static_cast<double>(m);
     d.c2 = kLog2e / static_cast<double>(T);
+    d.mc2 = d.m * d.c2;
     d.z32 = z32;
     d.lrow = static_cast<const typename E::T*>(P.logits) + (size_t)row * P.vocab;
     d.qrow = (kind == kDrawResidual) ? P.q + (size_t)drow * P.vocab : nullptr;

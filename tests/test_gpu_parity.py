@@ -34,7 +34,15 @@ SMALL = [
     ("c2_oddV_f32", dict(n=2, vocab=777, batch=8)),
     ("c2_offsets", dict(n=2, vocab=3000, batch=8, explicit_offsets=True)),
     ("c1_tinyV", dict(n=1, vocab=3, batch=33)),
+    ("c1_tinyV_aligned", dict(n=1, vocab=8, batch=33)),             # one 32-byte row: one piece
+    ("c3_aligned", dict(n=3, vocab=16384, batch=32)),
+    ("c5_aligned", dict(n=5, vocab=4096, batch=64)),                # ragged, gamma_b = 0, q = p
 ]
+
+
+def _aligned(inp) -> bool:
+    esize = 2 if inp.dtype == "bf16" else 4
+    return inp.vocab * esize % 16 == 0
 
 
 @pytest.mark.parametrize("fused", [True, False], ids=["fused", "twokernel"])
@@ -44,8 +52,12 @@ def test_small_parity(name, kw, fused):
     n = kw.pop("n")
     inp = make_config(n, replicate=7, **kw)
     sets = [inp.uniforms] + [uniforms_from_seed(inp.uniforms.shape, s) for s in range(15)]
-    rep, errs, _ = parity_check(inp, sets, label=name, fused=fused)
+    rep, errs, sv = parity_check(inp, sets, label=name, fused=fused)
     _assert_ok(rep, errs)
+    from lossless_rejection_sampling_sampler_amd._lib import (SV_SCHEDULE_FLAT, SV_SCHEDULE_ONE_LAUNCH,
+                                                              SV_SCHEDULE_SPLIT)
+    want = SV_SCHEDULE_SPLIT if not _aligned(inp) else (SV_SCHEDULE_ONE_LAUNCH if fused else SV_SCHEDULE_FLAT)
+    assert sv.last_schedule() == want
 
 
 def test_temperature_edge_values():
