@@ -29,7 +29,7 @@ PEAK_HBM_GBPS = 8000.0
 CONFIG_ID = 3
 KDT = "BF16"
 CSRC = os.path.join(ROOT, "lossless_rejection_sampling_sampler_amd", "csrc")
-KERNEL_SOURCES = ("sv_device.h", "sv_fused.h", "spec_verify.hip")
+KERNEL_SOURCES = ("sv_device.h", "sv_step.h", "spec_verify.hip")
 
 
 def traffic_path(kernel: str) -> str:
@@ -190,7 +190,7 @@ def main():
     one_launch = svp_schedule == SV_SCHEDULE_ONE_LAUNCH
     if one_launch:
         # one kernel does the whole step: its bytes are the step's
-        kname, kbytes = f"fused_step_kernel<{KDT}>", step_bytes
+        kname, kbytes = f"step_kernel<{KDT}>", step_bytes
     else:
         kname, kbytes = f"rows_flat_kernel<{KDT}>", rows_b
     kernel_gbps = kbytes / (rows_avg_ms * 1e-3) / 1e9

@@ -77,8 +77,11 @@ enum sv_device_error {
     SV_DEVERR_OFFSETS = 2u,    /* draft_offsets not prefix sums with 0 <= gamma_b <= gamma and
                                   offsets[batch] <= total_draft; the affected requests' outputs
                                   are unspecified (no access leaves the buffers' bounds) */
-    SV_DEVERR_NONFINITE = 4u   /* a draw row without positive finite mass (a target row with no
+    SV_DEVERR_NONFINITE = 4u,  /* a draw row without positive finite mass (a target row with no
                                   finite logit, or NaN logits); that token is unspecified */
+    SV_DEVERR_STALLED = 8u     /* one-launch schedule: a bounded wait for data another workgroup
+                                  had already sent expired (never expected); that call's outputs
+                                  are unspecified */
 };
 
 /* Limits fixed at creation.  max_gamma <= SV_MAX_GAMMA. */

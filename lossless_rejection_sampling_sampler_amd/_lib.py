@@ -29,6 +29,7 @@ SV_FLAG_ONE_LAUNCH = 4
 SV_DEVERR_DRAFT_ID = 1
 SV_DEVERR_OFFSETS = 2
 SV_DEVERR_NONFINITE = 4
+SV_DEVERR_STALLED = 8
 SV_MAX_GAMMA = 128
 SV_SCHEDULE_NONE = 0
 SV_SCHEDULE_SPLIT = 1

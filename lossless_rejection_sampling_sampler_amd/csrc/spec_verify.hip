@@ -13,7 +13,7 @@
 
 #include "spec_verify.h"
 #include "sv_device.h"
-#include "sv_fused.h"
+#include "sv_step.h"
 
 namespace {
 
@@ -37,24 +37,29 @@ Geometry geometry_for(int vocab, int dtype) {
     return g;
 }
 
-// One-launch geometry: pieces per row (about 8 vectors per thread each), grid
-// (all resident, no more workgroups than pieces) and draw chunks per request
-// (about two per workgroup, at most kMaxOwnChunks).
-struct FusedGeometry {
-    int grid, pieces, items, chunks;
+// One-launch geometry: pieces per row (about kPieceVecs vectors per lane each,
+// at most one per merge lane); the resident single-wave workgroups split into
+// row waves and draw waves (enough draw waves that every draw block has an
+// owner lane, and about kDrawShare of the grid otherwise).
+constexpr double kDrawShare = 0.375;
+
+struct StepGeometry {
+    int grid, row_waves, pieces, items;
+    bool ok;
 };
 
-FusedGeometry fused_geometry(long vpr, int gamma, int batch, int nblocks, int resident) {
-    FusedGeometry fg;
-    long p = (vpr + (long)sv::kThreads * 8 / 2) / ((long)sv::kThreads * 8);
-    fg.pieces = static_cast<int>(std::max(1L, std::min<long>(p, sv::kMaxPieces)));
-    fg.items = (gamma + 1) * batch * fg.pieces;
-    fg.grid = std::max(1, std::min(resident, fg.items));
-    long c = (2L * fg.grid + batch - 1) / batch;
-    c = std::max(1L, std::min<long>(c, nblocks));
-    while (c > 1 && (long)batch * c > (long)fg.grid * sv::kMaxOwnChunks) --c;
-    fg.chunks = static_cast<int>(c);
-    return fg;
+StepGeometry step_geometry(long vpr, int gamma, int batch, int nblocks, int resident) {
+    StepGeometry sg;
+    long p = (vpr + 64L * sv::kPieceVecs - 1) / (64L * sv::kPieceVecs);
+    sg.pieces = static_cast<int>(std::max(1L, std::min<long>(p, sv::kMaxStepPieces)));
+    sg.items = (gamma + 1) * batch * sg.pieces;
+    const long need = ((long)batch * nblocks + sv::kMaxOwnBlocks - 1) / sv::kMaxOwnBlocks;
+    const long draw = std::max<long>(need, static_cast<long>(resident * kDrawShare));
+    const long rows = std::min<long>(resident - draw, sg.items);
+    sg.row_waves = static_cast<int>(std::max(0L, rows));
+    sg.grid = static_cast<int>(std::max(0L, rows + draw));
+    sg.ok = resident > 0 && rows >= 1 && gamma <= sv::kMaxGammaStep;
+    return sg;
 }
 
 // Workgroups for the flat rows kernel: all resident at once, at least one batch
@@ -78,10 +83,10 @@ struct sv_ctx {
     Geometry geo{};
     int max_rows = 0;
     int resident_flat = 0;     // rows-flat workgroups resident at once on the device
-    int resident_fused = 0;    // fused-step workgroups resident at once (0: no cooperative launch)
-    uint32_t epoch = 0;        // tag of the fused step's publication words
+    int resident_step = 0;     // one-launch (single-wave) workgroups resident at once (0: no cooperative launch)
+    uint32_t epoch = 0;        // tag of the one-launch step's publication words
     int last_schedule = SV_SCHEDULE_NONE;
-    sv::FPiece* fpieces = nullptr;
+    sv::PieceRec* precs = nullptr;
     sv::DrawParams* dparams = nullptr;
     unsigned long long* words = nullptr;
     unsigned long long* state = nullptr;
@@ -189,15 +194,14 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
             return SV_ERR_DEVICE;
         }
         ctx->resident_flat = std::max(1, cus * std::max(1, per_cu));
-        int coop = 0, per_cu_fused = 0;
+        int coop = 0, per_bf16 = 0, per_f32 = 0;
         if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, device) != hipSuccess) coop = 0;
-        if (coop && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_fused, sv::fused_step_kernel<sv::BF16>,
-                                                                 sv::kThreads, 0) == hipSuccess) {
-            int per_f32 = 0;
-            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_f32, sv::fused_step_kernel<sv::F32>,
-                                                             sv::kThreads, 0) != hipSuccess) per_f32 = 0;
-            ctx->resident_fused = cus * std::min(per_cu_fused, per_f32);
-        }
+        if (coop &&
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_bf16, sv::step_kernel<sv::BF16>, sv::kStepLanes, 0) ==
+                hipSuccess &&
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_f32, sv::step_kernel<sv::F32>, sv::kStepLanes, 0) ==
+                hipSuccess)
+            ctx->resident_step = cus * std::min(per_bf16, per_f32);
         (void)hipGetLastError();
     }
     const size_t n_rows = (size_t)ctx->max_rows;
@@ -208,7 +212,7 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
     const size_t o_tasks = off; off = align_up(off + n_b * sizeof(sv::DrawTask), 256);
     const size_t o_recs = off;  off = align_up(off + n_b * ctx->geo.nblocks * sizeof(sv::BlockRec), 256);
     const size_t o_cnt = off;   off = align_up(off + (n_rows + 2 * n_b + 1) * sizeof(uint32_t), 256);
-    const size_t o_fp = off;    off = align_up(off + n_rows * sv::kMaxPieces * sizeof(sv::FPiece), 256);
+    const size_t o_fp = off;    off = align_up(off + n_rows * sv::kMaxStepPieces * sizeof(sv::PieceRec), 256);
     const size_t o_dp = off;    off = align_up(off + n_b * sizeof(sv::DrawParams), 256);
     const size_t o_wd = off;    off = align_up(off + n_b * sizeof(unsigned long long), 256);
     const size_t o_st = off;    off = align_up(off + n_b * sizeof(unsigned long long), 256);
@@ -227,7 +231,7 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
     ctx->req_cnt = ctx->row_cnt + n_rows;
     ctx->draw_cnt = ctx->req_cnt + n_b;
     ctx->err = ctx->draw_cnt + n_b;
-    ctx->fpieces = reinterpret_cast<sv::FPiece*>(base + o_fp);
+    ctx->precs = reinterpret_cast<sv::PieceRec*>(base + o_fp);
     ctx->dparams = reinterpret_cast<sv::DrawParams*>(base + o_dp);
     ctx->words = reinterpret_cast<unsigned long long*>(base + o_wd);
     ctx->state = reinterpret_cast<unsigned long long*>(base + o_st);
@@ -319,13 +323,10 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
     P.flat_vpr = (long)a->vocab * (long)esize / 16;
     P.flat_nv = rows * P.flat_vpr;
 
-    sv::FusedParams F;
-    const FusedGeometry fg = fused_geometry(P.flat_vpr, a->gamma, a->batch, ctx->geo.nblocks, ctx->resident_fused);
+    const StepGeometry sg = step_geometry(P.flat_vpr, a->gamma, a->batch, ctx->geo.nblocks, ctx->resident_step);
     // the one-launch step is opt-in until it beats the two-kernel schedule
     const bool want_fused = (cfg.flags & SV_FLAG_ONE_LAUNCH) && !(cfg.flags & SV_FLAG_TWO_KERNEL);
-    // every draw chunk must have an owner (at most kMaxOwnChunks per workgroup)
-    const bool owned = (long)a->batch * fg.chunks <= (long)fg.grid * sv::kMaxOwnChunks;
-    const bool fused = aligned && want_fused && owned && ctx->resident_fused > 0 && a->gamma <= sv::kMaxGammaFused;
+    const bool fused = aligned && want_fused && sg.ok;
 
     const bool prof = (cfg.flags & SV_FLAG_PROFILE) != 0;
     if (prof && ctx->prof_n == kProfileRing) {
@@ -336,22 +337,22 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
     if (prof && hipEventRecord(ev[0], stream) != hipSuccess) return SV_ERR_DEVICE;
     if (fused) {
         if (++ctx->epoch == 0) ctx->epoch = 1;
-        F.p = P;
-        F.p.parts = nullptr;
-        F.vpr = P.flat_vpr;
-        F.pieces = fg.pieces;
-        F.items = fg.items;
-        F.chunks = fg.chunks;
-        F.epoch = ctx->epoch;
-        F.fpieces = ctx->fpieces;
-        F.dparams = ctx->dparams;
-        F.words = ctx->words;
-        F.state = ctx->state;
-        void* kargs[] = {&F};
-        const void* fn = (cfg.logits_dtype == SV_BF16)
-                             ? reinterpret_cast<const void*>(&sv::fused_step_kernel<sv::BF16>)
-                             : reinterpret_cast<const void*>(&sv::fused_step_kernel<sv::F32>);
-        if (hipLaunchCooperativeKernel(fn, dim3(fg.grid), dim3(sv::kThreads), kargs, 0, stream) != hipSuccess)
+        sv::StepParams S;
+        S.p = P;
+        S.p.parts = nullptr;
+        S.vpr = P.flat_vpr;
+        S.pieces = sg.pieces;
+        S.items = sg.items;
+        S.epoch = ctx->epoch;
+        S.row_waves = sg.row_waves;
+        S.precs = ctx->precs;
+        S.dparams = ctx->dparams;
+        S.words = ctx->words;
+        S.state = ctx->state;
+        void* kargs[] = {&S};
+        const void* fn = (cfg.logits_dtype == SV_BF16) ? reinterpret_cast<const void*>(&sv::step_kernel<sv::BF16>)
+                                                        : reinterpret_cast<const void*>(&sv::step_kernel<sv::F32>);
+        if (hipLaunchCooperativeKernel(fn, dim3(sg.grid), dim3(sv::kStepLanes), kargs, 0, stream) != hipSuccess)
             return SV_ERR_DEVICE;
         if (prof && hipEventRecord(ev[1], stream) != hipSuccess) return SV_ERR_DEVICE;
     } else {

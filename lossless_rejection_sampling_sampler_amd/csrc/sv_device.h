@@ -47,9 +47,15 @@ constexpr int kThreads = 256;            // 4 waves of 64
 constexpr int kWaves = kThreads / 64;
 constexpr int kRowUnroll = 4;            // 16-byte vectors per thread per batch (two batches in flight)
 constexpr int kMaxPieces = 16;           // partials per row
-constexpr int kDrawPerLane = 8;          // draw block: one wave, 8 tokens per lane
-constexpr int kBlockElems = 64 * kDrawPerLane;   // 512 tokens
-constexpr int kMaxDrawBlocks = 1024;     // vocab up to 2^19 tokens
+// A draw block is 2048 consecutive tokens of a draw row, worked on by one wave:
+// four sub-blocks of 512 tokens, lane L holding tokens 8L .. 8L+7 of each, so
+// every 16-byte load instruction of the wave reads one contiguous span.
+constexpr int kSubTokens = 8;                        // tokens per lane per sub-block
+constexpr int kSubBlocks = 4;
+constexpr int kSubElems = 64 * kSubTokens;           // 512
+constexpr int kBlockElems = kSubBlocks * kSubElems;  // 2048
+constexpr int kMaxDrawBlocks = 256;                  // vocab up to 2^19 tokens
+constexpr int kSelPer = kMaxDrawBlocks / 64;         // blocks per lane in the select
 constexpr int kMarginSlots = 2;          // marginal tokens kept inline per block record (code assumes 2)
 constexpr double kLog2e = 1.4426950408889634;
 constexpr double kQFloor = 1e-10;        // page section 5.2: q.clamp(min=1e-10)
@@ -59,7 +65,7 @@ constexpr double kQFloor = 1e-10;        // page section 5.2: q.clamp(min=1e-10)
 constexpr double kSignMargin = 1e-5;
 
 enum : int { kDrawNone = 0, kDrawResidual = 1, kDrawBonus = 2, kDrawDegenerate = 3 };
-enum : uint32_t { kErrDraftId = 1u, kErrOffsets = 2u, kErrNonFinite = 4u };
+enum : uint32_t { kErrDraftId = 1u, kErrOffsets = 2u, kErrNonFinite = 4u, kErrStalled = 8u };
 
 struct Piece {           // one (row, piece) partial
     float m;             // piece max of the raw logits (or the argmax value)
@@ -83,10 +89,11 @@ struct DrawTask {        // written by the resolving workgroup, read by the draw
     int drow;            // draft row of q (residual only)
     int pos;             // output column k
     float v;             // uniform of the draw
-    int pad[3];
+    float m;             // the draw row's max logit
+    double z32;          // the draw row's normaliser (fp32 exponentials)
 };
 
-struct BlockRec {        // per (request, 512-token draw block) sums
+struct BlockRec {        // per (request, draw block) sums
     double se;           // sum of e = exp((l - m) / T) in fp64
     double ea;           // sum of e over tokens whose residual is clearly positive
     double qa;           // sum of q over the same tokens
@@ -478,6 +485,8 @@ struct RowShared {
     RedScratch red;
     int flag;
     int k;
+    float mk;            // resolve: statistics of row k for the draw task
+    double zk;
 };
 
 // Per-thread online max / sum over one batch of decoded logits.
@@ -507,26 +516,25 @@ __device__ __forceinline__ void load_batch(v4u* buf, const v4u* vp, long first, 
 }
 
 // Streams vectors [v0, v1) of target row t (vectors counted from the row's first
-// 16-byte aligned element), adds the scalar head (piece 0) and tail (last piece),
-// publishes the piece and, for the last piece / last row, merges and resolves.
+// 16-byte aligned element), adds the scalar head (piece 0) and tail (last piece)
+// and publishes the piece.  Returns, in thread 0, the row's arrival count before
+// this piece (-1 for a row outside the request layout); the caller decides when
+// to look at it, so the counter's round trip can overlap further streaming.
 template <typename E>
-__device__ __forceinline__ void row_piece(const Params& P, int t, long v0, long v1, int piece, int npieces, RowShared& sh) {
+__device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0, long v1, int piece, int npieces,
+                                                 RowShared& sh) {
     const int tid = threadIdx.x;
     const int V = P.vocab;
 
     const RowMap rm = map_row(P, t, sh.red);
     if (!rm.ok) {
         if (tid == 0 && piece == 0) flag_error(P.err, kErrOffsets);
-        return;
+        return -1;
     }
     const int b = rm.b, i = rm.i, gb = rm.gb;
     const float T = P.temperature[b];
     const bool greedy = !(T > 0.0f);
     const float c = greedy ? 0.0f : static_cast<float>(kLog2e / static_cast<double>(T));
-
-    // the drafted token id of this position, fetched early for the row merge
-    int xdraft = -1;
-    if (tid == 0 && !greedy && i < gb) xdraft = P.ids[rm.d0 + i];
 
     const typename E::T* row = static_cast<const typename E::T*>(P.logits) + (size_t)t * V;
     const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
@@ -607,16 +615,34 @@ __device__ __forceinline__ void row_piece(const Params& P, int t, long v0, long 
         gloc = bi;
     }
 
-    // ---- publish the piece; the last piece of the row merges
+    // ---- publish the piece
+    int old = 0;
     if (tid == 0) {
         Piece* pp = &P.parts[(size_t)t * kMaxPieces + piece];
         st_coherent(&pp->m, mloc);
         st_coherent(&pp->g, gloc);
         st_coherent(&pp->z, zloc);
-        sh.flag = (arrive(&P.row_cnt[t]) == static_cast<uint32_t>(npieces - 1));
+        old = static_cast<int>(arrive(&P.row_cnt[t]));
     }
-    __syncthreads();
-    if (!sh.flag) return;
+    return old;
+}
+
+// Merge of row t by the workgroup that landed its last piece: row statistics,
+// the drafted token's logit and q, and, when it is the request's last row to
+// finish, the request's resolve (accept tests, first rejection, outputs, draw task).
+template <typename E>
+__device__ __forceinline__ void row_merge(const Params& P, int t, int npieces, RowShared& sh) {
+    const int tid = threadIdx.x;
+    const int V = P.vocab;
+    const RowMap rm = map_row(P, t, sh.red);
+    if (!rm.ok) return;
+    const int b = rm.b, i = rm.i, gb = rm.gb;
+    const float T = P.temperature[b];
+    const bool greedy = !(T > 0.0f);
+    const float c = greedy ? 0.0f : static_cast<float>(kLog2e / static_cast<double>(T));
+    int xdraft = -1;
+    if (tid == 0 && !greedy && i < gb) xdraft = P.ids[rm.d0 + i];
+    const typename E::T* row = static_cast<const typename E::T*>(P.logits) + (size_t)t * V;
     if (tid == 0) reset_counter(&P.row_cnt[t]);
 
     RowStat st;
@@ -675,6 +701,13 @@ __device__ __forceinline__ void row_piece(const Params& P, int t, long v0, long 
     __syncthreads();
     int xj = -1;
     if (tid < gb) xj = P.ids[rm.d0 + tid];
+    // every row's statistics (the bonus row's too, for the draw task)
+    float m_t = 0.0f;
+    double z_t = 0.0;
+    if (tid <= gb && !greedy) {
+        m_t = ld_coherent(&P.rows[t0 + tid].m);
+        z_t = ld_coherent(&P.rows[t0 + tid].z);
+    }
     if (tid < gb) {
         bool acc;
         const RowStat* rs = &P.rows[t0 + tid];
@@ -683,8 +716,8 @@ __device__ __forceinline__ void row_piece(const Params& P, int t, long v0, long 
             acc = (xj == g);
             if (P.diag_r) P.diag_r[rm.d0 + tid] = __uint_as_float(0x7fc00000u);
         } else {
-            const float m = ld_coherent(&rs->m);
-            const double Z = ld_coherent(&rs->z);
+            const float m = m_t;
+            const double Z = z_t;
             const float lx = ld_coherent(&rs->lx);
             const float qx = ld_coherent(&rs->qx);
             const int xv = ld_coherent(&rs->x);
@@ -699,12 +732,14 @@ __device__ __forceinline__ void row_piece(const Params& P, int t, long v0, long 
     }
     __syncthreads();
     const int k = sh.k;
+    if (tid == k) { sh.mk = m_t; sh.zk = z_t; }
     if (tid <= G) {
         int tok = -1;
         if (tid < k) tok = xj;
         else if (tid == k && greedy) tok = ld_coherent(&P.rows[t0 + k].g);
         P.out_tokens[(size_t)b * (G + 1) + tid] = tok;
     }
+    __syncthreads();
     if (tid == 0) {
         P.out_num[b] = k;
         DrawTask tk;
@@ -713,7 +748,8 @@ __device__ __forceinline__ void row_piece(const Params& P, int t, long v0, long 
         tk.drow = rm.d0 + k;
         tk.pos = k;
         tk.v = greedy ? 0.0f : P.uniforms[(size_t)b * (G + 2) + (k < gb ? G : G + 1)];
-        tk.pad[0] = tk.pad[1] = tk.pad[2] = 0;
+        tk.m = sh.mk;
+        tk.z32 = sh.zk;
         P.tasks[b] = tk;
     }
 }
@@ -731,7 +767,10 @@ __global__ __launch_bounds__(kThreads) void rows_split_kernel(Params P) {
     int head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(typename E::T));
     if (head > V) head = V;
     const long nvec = (V - head) / E::kPerVec;
-    row_piece<E>(P, t, (long)s * nvec / S, (long)(s + 1) * nvec / S, s, S, sh);
+    const int old = row_piece_publish<E>(P, t, (long)s * nvec / S, (long)(s + 1) * nvec / S, s, S, sh);
+    if (threadIdx.x == 0) sh.flag = (old == S - 1);
+    __syncthreads();
+    if (sh.flag) row_merge<E>(P, t, S, sh);
 }
 
 // Workgroup owning vector v when nv vectors are cut into g equal ranges
@@ -750,32 +789,36 @@ __global__ __launch_bounds__(kThreads) void rows_flat_kernel(Params P) {
     const long NV = P.flat_nv, VPR = P.flat_vpr;
     const long a = (long)w * NV / G, e = (long)(w + 1) * NV / G;
     long r = a / VPR;
+    // a row's merge is taken up only after the next piece has streamed, so the
+    // arrival counter's round trip never stalls the stream
+    int pend_t = -1, pend_np = 0, pend_old = 0;
     for (long s0 = a; s0 < e; ++r) {
         const long rs = r * VPR, re = rs + VPR;
         const long s1 = e < re ? e : re;
         const int wf = range_owner(rs, NV, G), wl = range_owner(re - 1, NV, G);
-        row_piece<E>(P, static_cast<int>(r), s0 - rs, s1 - rs, w - wf, wl - wf + 1, sh);
+        const int np = wl - wf + 1;
+        const int old = row_piece_publish<E>(P, static_cast<int>(r), s0 - rs, s1 - rs, w - wf, np, sh);
         __syncthreads();
+        if (pend_t >= 0) {
+            if (threadIdx.x == 0) sh.flag = (pend_old == pend_np - 1);
+            __syncthreads();
+            if (sh.flag) row_merge<E>(P, pend_t, pend_np, sh);
+            __syncthreads();
+        }
+        pend_t = static_cast<int>(r);
+        pend_np = np;
+        pend_old = old;
         s0 = s1;
+    }
+    if (pend_t >= 0) {
+        if (threadIdx.x == 0) sh.flag = (pend_old == pend_np - 1);
+        __syncthreads();
+        if (sh.flag) row_merge<E>(P, pend_t, pend_np, sh);
     }
 }
 
-// ----------------------------------------------------------------- draw kernel
-// The 8 tokens x0 .. x0+7 of one lane in a draw block.
-struct DrawShared {
-    RedScratch red;
-    double tab[64];
-    double w[kMaxDrawBlocks];
-    int list[kMaxDrawBlocks];
-    double sums[kWaves][3];      // per wave: se, ea, qa
-    int counts[kWaves][2];       // per wave: blocks with many marginal tokens, with any
-    double pick_before[kWaves][2];
-    int pick_block[kWaves][2];   // per wave: first crossing block, last positive block
-    int n;
-    int flag;
-};
-
-// Everything a workgroup needs to work on one request's draw row.
+// ----------------------------------------------------------------- draw blocks
+// Everything a wave needs to work on one request's draw row.
 template <typename E>
 struct DrawRow {
     int kind;            // kDrawResidual / kDrawBonus
@@ -796,77 +839,128 @@ __device__ __forceinline__ double draw_e(const DrawRow<E>& d, float l, const dou
     return exp2_nonpos(fma(static_cast<double>(l), d.c2, -d.mc2), tab);
 }
 
-// One lane's 8 tokens of a draw block as loaded (raw element bits), so that
-// several blocks can be in flight before any is decoded.
+// One lane's 8 tokens of one sub-block as loaded (raw element bits), and its
+// 32 tokens of a whole block.
 template <typename E>
-struct Raw8 {
-    v4u l[kDrawPerLane / E::kPerVec];
-    v4u q[kDrawPerLane / 4];
+struct RawSub {
+    v4u l[kSubTokens / E::kPerVec];
+    v4u q[kSubTokens / 4];
+};
+template <typename E>
+struct RawBlock {
+    RawSub<E> s[kSubBlocks];
 };
 
-// Issues the loads of tokens [x0, x0 + 8) element by element (logits past V
-// read as -inf, q as 0): the tail block and rows that are not 16-byte aligned.
+// Vector loads of this lane's tokens [x0, x0 + 8) of 16-byte aligned rows.
+template <typename E, bool kWithQ>
+__device__ __forceinline__ void issue_sub_fast(const DrawRow<E>& d, long x0, RawSub<E>& r) {
+    const v4u* lp = reinterpret_cast<const v4u*>(d.lrow + x0);
+#pragma unroll
+    for (int h = 0; h < kSubTokens / E::kPerVec; ++h) r.l[h] = __builtin_nontemporal_load(lp + h);
+    if (kWithQ) {
+        const v4u* qp = reinterpret_cast<const v4u*>(d.qrow + x0);
+#pragma unroll
+        for (int h = 0; h < kSubTokens / 4; ++h) r.q[h] = __builtin_nontemporal_load(qp + h);
+    }
+}
+
+// Loads of this lane's tokens [x0, x0 + 8) of any row: vectors where the row
+// allows, else element by element (logits past V read as -inf, q as 0).
 template <typename E>
-__device__ __forceinline__ void issue_draw8_any(const DrawRow<E>& d, long x0, int V, Raw8<E>& r) {
-    constexpr int NL = kDrawPerLane / E::kPerVec;
-    const bool full = x0 + kDrawPerLane <= V;
+__device__ __forceinline__ void issue_sub_any(const DrawRow<E>& d, long x0, int V, bool with_q, RawSub<E>& r) {
+    constexpr int NL = kSubTokens / E::kPerVec;
+    const bool full = x0 + kSubTokens <= V;
     if (full && d.lalign) {
         const v4u* lp = reinterpret_cast<const v4u*>(d.lrow + x0);
 #pragma unroll
-        for (int u = 0; u < NL; ++u) r.l[u] = __builtin_nontemporal_load(lp + u);
+        for (int h = 0; h < NL; ++h) r.l[h] = __builtin_nontemporal_load(lp + h);
     } else {
         uint32_t w[4 * NL];
 #pragma unroll
         for (int k = 0; k < 4 * NL; ++k) w[k] = 0u;
 #pragma unroll
-        for (int k = 0; k < kDrawPerLane; ++k) {
+        for (int k = 0; k < kSubTokens; ++k) {
             const uint32_t bits = (x0 + k < V) ? E::bits1(d.lrow, x0 + k) : E::kNegInfBits;
             if (E::kBits == 16) w[k >> 1] |= bits << (16 * (k & 1));
             else w[k] = bits;
         }
 #pragma unroll
-        for (int u = 0; u < NL; ++u) r.l[u] = v4u{w[4 * u], w[4 * u + 1], w[4 * u + 2], w[4 * u + 3]};
+        for (int h = 0; h < NL; ++h) r.l[h] = v4u{w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]};
     }
-    if (d.qrow) {
+    if (with_q) {
         if (full && d.qalign) {
             const v4u* qp = reinterpret_cast<const v4u*>(d.qrow + x0);
 #pragma unroll
-            for (int u = 0; u < kDrawPerLane / 4; ++u) r.q[u] = __builtin_nontemporal_load(qp + u);
+            for (int h = 0; h < kSubTokens / 4; ++h) r.q[h] = __builtin_nontemporal_load(qp + h);
         } else {
-            uint32_t w[kDrawPerLane];
+            uint32_t w[kSubTokens];
 #pragma unroll
-            for (int k = 0; k < kDrawPerLane; ++k)
-                w[k] = (x0 + k < V) ? __float_as_uint(d.qrow[x0 + k]) : 0u;
+            for (int k = 0; k < kSubTokens; ++k) w[k] = (x0 + k < V) ? __float_as_uint(d.qrow[x0 + k]) : 0u;
 #pragma unroll
-            for (int u = 0; u < kDrawPerLane / 4; ++u) r.q[u] = v4u{w[4 * u], w[4 * u + 1], w[4 * u + 2], w[4 * u + 3]};
+            for (int h = 0; h < kSubTokens / 4; ++h) r.q[h] = v4u{w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]};
         }
     } else {
 #pragma unroll
-        for (int u = 0; u < kDrawPerLane / 4; ++u) r.q[u] = v4u(0u);
+        for (int h = 0; h < kSubTokens / 4; ++h) r.q[h] = v4u(0u);
     }
 }
 
-// Vector loads of tokens [x0, x0 + 8) of a full block of 16-byte aligned rows.
-template <typename E, bool with_q>
-__device__ __forceinline__ void issue_draw8_fast(const DrawRow<E>& d, long x0, Raw8<E>& r) {
-    const v4u* lp = reinterpret_cast<const v4u*>(d.lrow + x0);
+// This lane's first token of sub-block u of the block starting at xb.
+__device__ __forceinline__ long sub_first(long xb, int u) {
+    return xb + u * kSubElems + (threadIdx.x & 63) * kSubTokens;
+}
+
+template <typename E, bool kWithQ>
+__device__ __forceinline__ void issue_block_fast(const DrawRow<E>& d, long xb, RawBlock<E>& r) {
 #pragma unroll
-    for (int u = 0; u < kDrawPerLane / E::kPerVec; ++u) r.l[u] = __builtin_nontemporal_load(lp + u);
-    if (with_q) {
-        const v4u* qp = reinterpret_cast<const v4u*>(d.qrow + x0);
+    for (int u = 0; u < kSubBlocks; ++u) issue_sub_fast<E, kWithQ>(d, sub_first(xb, u), r.s[u]);
+}
+template <typename E>
+__device__ __forceinline__ void issue_block_any(const DrawRow<E>& d, long xb, int V, bool with_q, RawBlock<E>& r) {
 #pragma unroll
-        for (int u = 0; u < kDrawPerLane / 4; ++u) r.q[u] = __builtin_nontemporal_load(qp + u);
-    }
+    for (int u = 0; u < kSubBlocks; ++u) issue_sub_any<E>(d, sub_first(xb, u), V, with_q, r.s[u]);
 }
 
 template <typename E>
-__device__ __forceinline__ void decode_draw8(const Raw8<E>& r, bool with_q, float* l, float* q) {
+__device__ __forceinline__ void decode_sub(const RawSub<E>& r, bool with_q, float* l, float* q) {
 #pragma unroll
-    for (int u = 0; u < kDrawPerLane / E::kPerVec; ++u) E::decode(r.l[u], l + u * E::kPerVec);
+    for (int h = 0; h < kSubTokens / E::kPerVec; ++h) E::decode(r.l[h], l + h * E::kPerVec);
 #pragma unroll
-    for (int u = 0; u < kDrawPerLane / 4; ++u) {
-        if (with_q) F32::decode(r.q[u], q + 4 * u);
-        else q[4 * u] = q[4 * u + 1] = q[4 * u + 2] = q[4 * u + 3] = 0.0f;
+    for (int h = 0; h < kSubTokens / 4; ++h) {
+        if (with_q) F32::decode(r.q[h], q + 4 * h);
+        else q[4 * h] = q[4 * h + 1] = q[4 * h + 2] = q[4 * h + 3] = 0.0f;
+    }
+}
+
+// Rare path of block_record: stores the block's first kMarginSlots marginal
+// tokens in token order (sub-block, then lane, then position in the lane),
+// reloading each from memory.  Kept out of line so that the common path's
+// register allocation does not carry it.
+template <typename E>
+__device__ __noinline__ void record_marginal(const typename E::T* lrow, const float* qrow, double c2, double mc2,
+                                             long xb, uint32_t mmask, const double* tab, BlockRec* rec) {
+    const int lane = threadIdx.x & 63;
+    int slot = 0;
+    for (int u = 0; u < kSubBlocks && slot < kMarginSlots; ++u) {
+        const uint32_t mu = (mmask >> (u * kSubTokens)) & 0xffu;
+        unsigned long long lanes = __ballot(mu != 0u);
+        while (lanes != 0ull && slot < kMarginSlots) {
+            const int L = __ffsll(static_cast<long long>(lanes)) - 1;
+            lanes &= lanes - 1ull;
+            uint32_t bits = static_cast<uint32_t>(rdlane(static_cast<int>(mu), L));
+            while (bits != 0u && slot < kMarginSlots) {
+                const int k = __ffs(static_cast<int>(bits)) - 1;
+                bits &= bits - 1u;
+                if (lane == 0) {
+                    const long x = xb + u * kSubElems + L * kSubTokens + k;
+                    st_coherent(&rec->mx[slot], static_cast<int>(x));
+                    st_coherent(&rec->mq[slot], qrow[x]);
+                    st_coherent(&rec->me[slot],
+                                exp2_nonpos(fma(static_cast<double>(E::load1(lrow, x)), c2, -mc2), tab));
+                }
+                ++slot;
+            }
+        }
     }
 }
 
@@ -874,37 +968,39 @@ __device__ __forceinline__ void decode_draw8(const Raw8<E>& r, bool with_q, floa
 // Residual rows split the tokens three ways with the fp32-pass normaliser:
 // clearly positive residual (e / Z32 * (1 - margin) > q: summed into ea and qa),
 // clearly non-positive (e / Z32 * (1 + margin) < q: dropped) and marginal (the
-// rest: counted, the first kMarginSlots kept inline).  Branch-free except for
-// the marginal capture, which only runs when some lane has a marginal token.
-// Wave-uniform call.
+// rest: counted, the first kMarginSlots in token order kept inline).  Branch-
+// free except for the marginal capture, which only runs when the wave has a
+// marginal token.  Wave-uniform call.
 template <typename E, bool kResidual>
-__device__ __forceinline__ void block_record(const DrawRow<E>& d, const Raw8<E>& r, long x0, double apos,
+__device__ __forceinline__ void block_record(const DrawRow<E>& d, const RawBlock<E>& r, long xb, double apos,
                                              double aneg, const double* tab, BlockRec* rec) {
     const int lane = threadIdx.x & 63;
-    constexpr bool residual = kResidual;
-    float l[kDrawPerLane], q[kDrawPerLane];
-    decode_draw8<E>(r, residual, l, q);
     double se = 0.0, ea = 0.0, qa = 0.0;
-    uint32_t mmask = 0u;
-    if (residual) {
+    uint32_t mmask = 0u;                 // bit 8u + k: token k of sub-block u is marginal
 #pragma unroll
-        for (int k = 0; k < kDrawPerLane; ++k) {
+    for (int u = 0; u < kSubBlocks; ++u) {
+        float l[kSubTokens], q[kSubTokens];
+        decode_sub<E>(r.s[u], kResidual, l, q);
+#pragma unroll
+        for (int k = 0; k < kSubTokens; ++k) {
             const double e = draw_e<E>(d, l[k], tab);
-            const double qd = static_cast<double>(q[k]);
             se += e;
-            const bool pos = e * apos > qd;
-            const bool neg = e * aneg < qd;
-            ea += pos ? e : 0.0;
-            qa += pos ? qd : 0.0;
-            mmask |= static_cast<uint32_t>(!pos && !neg && e > 0.0) << k;
+            if (kResidual) {
+                const double qd = static_cast<double>(q[k]);
+                const bool pos = e * apos > qd;
+                const bool neg = e * aneg < qd;
+                ea += pos ? e : 0.0;
+                qa += pos ? qd : 0.0;
+                mmask |= static_cast<uint32_t>(!pos && !neg && e > 0.0) << (u * kSubTokens + k);
+            }
+            // two tokens' fp64 chains at a time: enough ILP next to the other
+            // waves of the SIMD, and few registers
+            if (k & 1) __builtin_amdgcn_sched_barrier(0);
         }
-    } else {
-#pragma unroll
-        for (int k = 0; k < kDrawPerLane; ++k) se += draw_e<E>(d, l[k], tab);
     }
     se = wave_sum(se);
     int nmw = 0;
-    if (residual) {
+    if (kResidual) {
         ea = wave_sum(ea);
         qa = wave_sum(qa);
         if (__ballot(mmask != 0u) != 0ull) nmw = wave_sum_int(__popc(mmask));
@@ -915,71 +1011,25 @@ __device__ __forceinline__ void block_record(const DrawRow<E>& d, const Raw8<E>&
         st_coherent(&rec->qa, qa);
         st_coherent(&rec->nm, nmw);
     }
-    if (nmw > 0 && nmw <= kMarginSlots) {
-        // slots in token order: exclusive prefix of the per-lane counts
-        const int nm = __popc(mmask);
-        int incl = nm;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += y;
-        }
-        int slot = incl - nm;
-#pragma unroll
-        for (int k = 0; k < kDrawPerLane; ++k) {
-            if ((mmask >> k) & 1u) {
-                if (slot < kMarginSlots) {
-                    st_coherent(&rec->mx[slot], static_cast<int>(x0) + k);
-                    st_coherent(&rec->mq[slot], q[k]);
-                    st_coherent(&rec->me[slot], draw_e<E>(d, l[k], tab));
-                }
-                ++slot;
-            }
-        }
-    }
+    if (kResidual && nmw > 0 && nmw <= kMarginSlots) record_marginal<E>(d.lrow, d.qrow, d.c2, d.mc2, xb, mmask, tab, rec);
 }
 
-constexpr int kDrawInFlight = 4;         // draw blocks per wave with loads in flight together
-
 // Per-block sums of draw blocks jfirst + wave, + jstride, ... < jend, written to
-// recs.  Full blocks of aligned rows: each wave issues the vector loads of up to
-// kDrawInFlight of its blocks before it works on the first.  Other blocks: one
-// at a time, element by element.
+// recs; one block (all of its loads in flight together) per wave at a time.
 template <typename E, bool kResidual>
 __device__ __forceinline__ void draw_blocks_kind(const DrawRow<E>& d, int V, BlockRec* recs, int jfirst, int jstride,
                                                  int jend, const double* tab) {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int wv = threadIdx.x >> 6;
     const double invZ32 = 1.0 / d.z32;
     const double apos = invZ32 * (1.0 - kSignMargin), aneg = invZ32 * (1.0 + kSignMargin);
     const bool fastrow = d.lalign && (!kResidual || d.qalign);
     const int jfull = V / kBlockElems;                  // blocks entirely inside the row
-    for (int j = jfirst + wv; j < jend; j += kDrawInFlight * jstride) {
-        const int jlast = min(j + (kDrawInFlight - 1) * jstride, jend - 1);
-        if (fastrow && jlast < jfull) {
-            Raw8<E> r[kDrawInFlight];
-#pragma unroll
-            for (int s = 0; s < kDrawInFlight; ++s) {
-                // past the end: reload the wave's first block (in bounds, never recorded)
-                const int js = (j + s * jstride < jend) ? j + s * jstride : j;
-                issue_draw8_fast<E, kResidual>(d, (long)js * kBlockElems + (long)lane * kDrawPerLane, r[s]);
-            }
-#pragma unroll
-            for (int s = 0; s < kDrawInFlight; ++s) {
-                const int js = j + s * jstride;
-                if (js < jend)
-                    block_record<E, kResidual>(d, r[s], (long)js * kBlockElems + (long)lane * kDrawPerLane, apos, aneg,
-                                               tab, &recs[js]);
-            }
-        } else {
-            for (int s = 0; s < kDrawInFlight; ++s) {
-                const int js = j + s * jstride;
-                if (js >= jend) break;
-                Raw8<E> r;
-                const long x0 = (long)js * kBlockElems + (long)lane * kDrawPerLane;
-                issue_draw8_any<E>(d, x0, V, r);
-                block_record<E, kResidual>(d, r, x0, apos, aneg, tab, &recs[js]);
-            }
-        }
+    for (int j = jfirst + wv; j < jend; j += jstride) {
+        RawBlock<E> r;
+        const long xb = (long)j * kBlockElems;
+        if (fastrow && j < jfull) issue_block_fast<E, kResidual>(d, xb, r);
+        else issue_block_any<E>(d, xb, V, kResidual, r);
+        block_record<E, kResidual>(d, r, xb, apos, aneg, tab, &recs[j]);
     }
 }
 
@@ -990,211 +1040,185 @@ __device__ __forceinline__ void draw_blocks(const DrawRow<E>& d, int V, BlockRec
     else draw_blocks_kind<E, false>(d, V, recs, jfirst, jstride, jend, tab);
 }
 
-// Select for one request once all its draw blocks are recorded.  The
-// workgroup rebuilds the exact fp64 normaliser Z64 and every block's weight
-// (e / Z64 - q summed over the clearly positive tokens plus the inline marginal
-// ones; blocks with more marginal tokens than slots, or every block when the
+// Select for one request once all its draw blocks are recorded, by one wave
+// (no LDS besides the exponential table; every lane returns the token).
+// Rebuilds the exact fp64 normaliser Z64 and every block's weight (e / Z64 - q
+// summed over the clearly positive tokens plus the inline marginal ones;
+// blocks with more marginal tokens than slots, or every block when the
 // fp32-pass normaliser is off by more than half the margin, are re-evaluated
-// from their tokens), finds the block holding v * S by a block scan, and wave 0
-// finds the token with a token scan of that block.  Returns the token in wave 0
-// (other waves: unspecified).
+// from their tokens), finds the block holding v * S by a scan over blocks
+// (kSelPer consecutive blocks per lane) and the token by a scan of that block.
 template <typename E>
-__device__ __forceinline__ int draw_select(const DrawRow<E>& d, int V, int NB, const BlockRec* recs, DrawShared& sh,
-                           uint32_t* err) {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wv = tid >> 6;
-    constexpr int kPer = kMaxDrawBlocks / kThreads;    // blocks per thread (contiguous)
+__device__ __forceinline__ int draw_select_wave(const DrawRow<E>& d, int V, int NB, const BlockRec* recs,
+                                             const double* tab, uint32_t* err) {
+    const int lane = threadIdx.x & 63;
     const bool residual = (d.kind == kDrawResidual);
-    // every field of this thread's records in one round of loads
-    double se_t[kPer], ea_t[kPer], qa_t[kPer], me0_t[kPer], me1_t[kPer];
-    float mq0_t[kPer], mq1_t[kPer];
-    int nm_t[kPer];
+    // every field of this lane's records in one round of loads
+    double se_t[kSelPer], ea_t[kSelPer], qa_t[kSelPer];
+    int nm_t[kSelPer];
 #pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-        const int j = tid * kPer + r;
+    for (int r = 0; r < kSelPer; ++r) {
+        const int j = lane * kSelPer + r;
         const bool in = j < NB;
         const BlockRec* rc = &recs[in ? j : 0];
         se_t[r] = in ? ld_coherent(&rc->se) : 0.0;
-        ea_t[r] = qa_t[r] = me0_t[r] = me1_t[r] = 0.0;
-        mq0_t[r] = mq1_t[r] = 0.0f;
+        ea_t[r] = qa_t[r] = 0.0;
         nm_t[r] = 0;
         if (residual && in) {
             ea_t[r] = ld_coherent(&rc->ea);
             qa_t[r] = ld_coherent(&rc->qa);
             nm_t[r] = ld_coherent(&rc->nm);
-            me0_t[r] = ld_coherent(&rc->me[0]);
-            me1_t[r] = ld_coherent(&rc->me[1]);
-            mq0_t[r] = ld_coherent(&rc->mq[0]);
-            mq1_t[r] = ld_coherent(&rc->mq[1]);
         }
     }
-    // ---- one workgroup reduction: Z64, and the counts that pick the path
     double zpart = 0.0;
-    int nbig = 0;
 #pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-        zpart += se_t[r];
-        nbig += (nm_t[r] > kMarginSlots);
-    }
-    zpart = wave_sum(zpart);
-    nbig = wave_sum_int(nbig);
-    if (lane == 0) { sh.sums[wv][0] = zpart; sh.counts[wv][0] = nbig; }
-    __syncthreads();
-    double Z64 = 0.0;
-    int NBIG = 0;
-#pragma unroll
-    for (int k = 0; k < kWaves; ++k) { Z64 += sh.sums[k][0]; NBIG += sh.counts[k][0]; }
+    for (int r = 0; r < kSelPer; ++r) zpart += se_t[r];
+    const double Z64 = wave_sum(zpart);
     const double invZ64 = 1.0 / Z64;
     int kind = d.kind;
-    double wt[kPer];
+    double wt[kSelPer];
     if (residual) {
         const bool full = !(fabs(Z64 - d.z32) <= 0.5 * kSignMargin * Z64);
-        if (!full && NBIG == 0) {
 #pragma unroll
-            for (int r = 0; r < kPer; ++r) {
-                // a marginal slot is only meaningful when the block recorded it
-                double w = ea_t[r] * invZ64 - qa_t[r];
-                if (nm_t[r] > 0) w += fmax(me0_t[r] * invZ64 - static_cast<double>(mq0_t[r]), 0.0);
-                if (nm_t[r] > 1) w += fmax(me1_t[r] * invZ64 - static_cast<double>(mq1_t[r]), 0.0);
-                wt[r] = w;
-            }
-        } else {
-            // rare: re-evaluate the listed blocks from their tokens
-            if (tid == 0) sh.n = 0;
-            __syncthreads();
+        for (int r = 0; r < kSelPer; ++r) wt[r] = ea_t[r] * invZ64 - qa_t[r];
+        // blocks with inline marginal tokens (a slot is only meaningful when the
+        // block recorded it): one more round of loads, only when there are any
+        bool any_slots = false;
 #pragma unroll
-            for (int r = 0; r < kPer; ++r) {
-                const int j = tid * kPer + r;
-                if (j < NB) {
-                    if (!full && nm_t[r] <= kMarginSlots) {
-                        double w = ea_t[r] * invZ64 - qa_t[r];
-                        if (nm_t[r] > 0) w += fmax(me0_t[r] * invZ64 - static_cast<double>(mq0_t[r]), 0.0);
-                        if (nm_t[r] > 1) w += fmax(me1_t[r] * invZ64 - static_cast<double>(mq1_t[r]), 0.0);
-                        sh.w[j] = w;
-                    } else {
-                        sh.list[atomicAdd(&sh.n, 1)] = j;
-                    }
+        for (int r = 0; r < kSelPer; ++r) any_slots |= (nm_t[r] > 0 && nm_t[r] <= kMarginSlots);
+        if (__ballot(any_slots) != 0ull) {
+#pragma unroll
+            for (int r = 0; r < kSelPer; ++r) {
+                const int j = lane * kSelPer + r;
+                if (j < NB && nm_t[r] > 0 && nm_t[r] <= kMarginSlots) {
+                    const BlockRec* rc = &recs[j];
+                    wt[r] += fmax(ld_coherent(&rc->me[0]) * invZ64 - static_cast<double>(ld_coherent(&rc->mq[0])), 0.0);
+                    if (nm_t[r] > 1)
+                        wt[r] += fmax(ld_coherent(&rc->me[1]) * invZ64 - static_cast<double>(ld_coherent(&rc->mq[1])), 0.0);
                 }
             }
-            __syncthreads();
-            const int n_list = sh.n;
-            for (int li = wv; li < n_list; li += kWaves) {
-                const int j = sh.list[li];
-                const long x0 = (long)j * kBlockElems + (long)lane * kDrawPerLane;
-                Raw8<E> raw;
-                issue_draw8_any<E>(d, x0, V, raw);
-                float l[kDrawPerLane], q[kDrawPerLane];
-                decode_draw8<E>(raw, true, l, q);
+        }
+        // rare: blocks re-evaluated from their tokens, one at a time by the wave
+#pragma unroll
+        for (int r = 0; r < kSelPer; ++r) {
+            const int j = lane * kSelPer + r;
+            unsigned long long need = __ballot(j < NB && (full || nm_t[r] > kMarginSlots));
+            while (need != 0ull) {
+                const int L = __ffsll(static_cast<long long>(need)) - 1;
+                need &= need - 1ull;
+                const long xb = (long)(L * kSelPer + r) * kBlockElems;
+                RawBlock<E> raw;
+                issue_block_any<E>(d, xb, V, true, raw);
                 double w = 0.0;
 #pragma unroll
-                for (int k = 0; k < kDrawPerLane; ++k)
-                    w += fmax(draw_e<E>(d, l[k], sh.tab) * invZ64 - static_cast<double>(q[k]), 0.0);
-                w = wave_sum(w);
-                if (lane == 0) sh.w[j] = w;
-            }
-            __syncthreads();
+                for (int u = 0; u < kSubBlocks; ++u) {
+                    float l[kSubTokens], q[kSubTokens];
+                    decode_sub<E>(raw.s[u], true, l, q);
 #pragma unroll
-            for (int r = 0; r < kPer; ++r) {
-                const int j = tid * kPer + r;
-                wt[r] = (j < NB) ? sh.w[j] : 0.0;
+                    for (int k = 0; k < kSubTokens; ++k) {
+                        w += fmax(draw_e<E>(d, l[k], tab) * invZ64 - static_cast<double>(q[k]), 0.0);
+                        if (k & 1) __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+                w = wave_sum(w);
+                if (lane == L) wt[r] = w;
             }
         }
     } else {
 #pragma unroll
-        for (int r = 0; r < kPer; ++r) wt[r] = se_t[r];
+        for (int r = 0; r < kSelPer; ++r) wt[r] = se_t[r];
     }
-    // ---- block scan (thread-contiguous blocks)
+    // ---- block scan
     double own = 0.0;
 #pragma unroll
-    for (int r = 0; r < kPer; ++r) own += wt[r];
-    double Stot;
-    double incl = wg_inclusive_scan(own, Stot, sh.red);
+    for (int r = 0; r < kSelPer; ++r) own += wt[r];
+    double incl = wave_inclusive_scan(own);
+    double Stot = rdlane(incl, 63);
     if (residual && !(Stot > 0.0)) {
         // residual lost to rounding: draw from p itself
         kind = kDrawDegenerate;
         own = 0.0;
 #pragma unroll
-        for (int r = 0; r < kPer; ++r) { wt[r] = se_t[r]; own += wt[r]; }
-        incl = wg_inclusive_scan(own, Stot, sh.red);
+        for (int r = 0; r < kSelPer; ++r) { wt[r] = se_t[r]; own += wt[r]; }
+        incl = wave_inclusive_scan(own);
+        Stot = rdlane(incl, 63);
     }
     const double tsel = static_cast<double>(d.v) * Stot;
-    // this thread's first block whose inclusive sum passes tsel, and its last
-    // block of positive weight, each with the sum before it
+    // this lane's first block whose inclusive sum passes tsel, and its last block
+    // of positive weight, each with the sum before it
     int cand = -1, lastpos = -1;
     double cand_before = 0.0, last_before = 0.0;
     {
         double run = incl - own;
 #pragma unroll
-        for (int r = 0; r < kPer; ++r) {
-            const int j = tid * kPer + r;
+        for (int r = 0; r < kSelPer; ++r) {
+            const int j = lane * kSelPer + r;
             const double before = run;
             run += wt[r];
             if (j < NB && wt[r] > 0.0) { lastpos = j; last_before = before; }
             if (j < NB && cand < 0 && run > tsel) { cand = j; cand_before = before; }
         }
     }
-    // per wave: the lowest lane with a crossing, the highest with a positive block
-    {
-        const unsigned long long cm = __ballot(cand >= 0), lm = __ballot(lastpos >= 0);
-        const int cl = cm ? __ffsll(static_cast<long long>(cm)) - 1 : 0;
-        const int ll = lm ? 63 - __clzll(static_cast<long long>(lm)) : 0;
-        const int cw = rdlane(cand, cl);
-        const double cbw = rdlane(cand_before, cl);
-        const int lw = rdlane(lastpos, ll);
-        const double lbw = rdlane(last_before, ll);
-        if (lane == 0) {
-            sh.pick_block[wv][0] = cm ? cw : -1;
-            sh.pick_before[wv][0] = cbw;
-            sh.pick_block[wv][1] = lm ? lw : -1;
-            sh.pick_before[wv][1] = lbw;
-        }
-    }
-    __syncthreads();
-    int jsel = -1;
-    double base = 0.0;
+    const unsigned long long cm = __ballot(cand >= 0), lm = __ballot(lastpos >= 0);
+    int jsel;
+    double base;
     bool block_fallback = false;
-#pragma unroll
-    for (int k = 0; k < kWaves; ++k) {
-        if (jsel < 0 && sh.pick_block[k][0] >= 0) { jsel = sh.pick_block[k][0]; base = sh.pick_before[k][0]; }
-    }
-    if (jsel < 0) {                     // rounding left no block above v * S: the last positive one
+    if (cm != 0ull) {
+        const int L = __ffsll(static_cast<long long>(cm)) - 1;
+        jsel = rdlane(cand, L);
+        base = rdlane(cand_before, L);
+    } else if (lm != 0ull) {            // rounding left no block above v * S: the last positive one
+        const int L = 63 - __clzll(static_cast<long long>(lm));
+        jsel = rdlane(lastpos, L);
+        base = rdlane(last_before, L);
         block_fallback = true;
-#pragma unroll
-        for (int k = 0; k < kWaves; ++k) {
-            if (sh.pick_block[k][1] >= 0) { jsel = sh.pick_block[k][1]; base = sh.pick_before[k][1]; }
-        }
-    }
-    if (jsel < 0) {                     // no positive finite weight (non-finite logits)
+    } else {                            // no positive finite weight (non-finite logits)
         jsel = 0;
         base = 0.0;
-        if (tid == 0) flag_error(err, kErrNonFinite);
+        block_fallback = true;
+        if (lane == 0) flag_error(err, kErrNonFinite);
     }
-    if (wv != 0) return -1;
 
-    // ---- token scan of the selected block by wave 0: 8 tokens per lane
-    const long x0 = (long)jsel * kBlockElems + (long)lane * kDrawPerLane;
-    Raw8<E> raw;
-    issue_draw8_any<E>(d, x0, V, raw);
-    float l[kDrawPerLane], q[kDrawPerLane];
+    // ---- token scan of the selected block (token order: sub-block, lane, position)
+    const long xb = (long)jsel * kBlockElems;
     const bool res_w = (kind == kDrawResidual);
-    decode_draw8<E>(raw, res_w, l, q);
-    double w[kDrawPerLane];
-    double tsum = 0.0;
-#pragma unroll
-    for (int k = 0; k < kDrawPerLane; ++k) {
-        const double e = draw_e<E>(d, l[k], sh.tab);
-        w[k] = res_w ? fmax(e * invZ64 - static_cast<double>(q[k]), 0.0) : e;
-        if (x0 + k >= V) w[k] = 0.0;
-        tsum += w[k];
-    }
-    double run = base + (wave_inclusive_scan(tsum) - tsum);
+    double run_base = base;
     int ycand = 0x7fffffff, ylast = -1;
+    // two sub-blocks per round of loads; the second round only when the first
+    // half holds no crossing (or the rounding fallback needs the last positive
+    // token of the whole block)
 #pragma unroll
-    for (int k = 0; k < kDrawPerLane; ++k) {
-        run += w[k];
-        const int x = static_cast<int>(x0) + k;
-        if (w[k] > 0.0) ylast = x;
-        if (!block_fallback && ycand == 0x7fffffff && run > tsel) ycand = x;
+    for (int half = 0; half < 2; ++half) {
+        if (half == 1 && !block_fallback && __ballot(ycand != 0x7fffffff) != 0ull) break;
+        RawSub<E> raw[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) issue_sub_any<E>(d, sub_first(xb, 2 * half + h), V, res_w, raw[h]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float l[kSubTokens], q[kSubTokens];
+            decode_sub<E>(raw[h], res_w, l, q);
+            const long x0 = sub_first(xb, 2 * half + h);
+            double w[kSubTokens];
+            double tsum = 0.0;
+#pragma unroll
+            for (int k = 0; k < kSubTokens; ++k) {
+                const double e = draw_e<E>(d, l[k], tab);
+                w[k] = res_w ? fmax(e * invZ64 - static_cast<double>(q[k]), 0.0) : e;
+                if (x0 + k >= V) w[k] = 0.0;
+                tsum += w[k];
+                if (k & 1) __builtin_amdgcn_sched_barrier(0);
+            }
+            const double ti = wave_inclusive_scan(tsum);
+            double run = run_base + (ti - tsum);
+#pragma unroll
+            for (int k = 0; k < kSubTokens; ++k) {
+                run += w[k];
+                const int x = static_cast<int>(x0) + k;
+                if (w[k] > 0.0) ylast = x;
+                if (!block_fallback && ycand == 0x7fffffff && run > tsel) ycand = x;
+            }
+            run_base += rdlane(ti, 63);
+        }
     }
     int y = wave_min_int(ycand);
     if (y == 0x7fffffff) y = wave_max_int(ylast);
@@ -1218,8 +1242,13 @@ __device__ __forceinline__ void init_draw_row(DrawRow<E>& d, const Params& P, in
     d.qalign = (reinterpret_cast<uintptr_t>(d.qrow) & 15u) == 0;
 }
 
+struct DrawShared {
+    double tab[64];
+    int flag;
+};
+
 template <typename E>
-__global__ __launch_bounds__(kThreads) void draw_kernel(Params P) {
+__global__ __launch_bounds__(kThreads, 4) void draw_kernel(Params P) {
     __shared__ DrawShared sh;
 
     const int tid = threadIdx.x;
@@ -1236,9 +1265,8 @@ __global__ __launch_bounds__(kThreads) void draw_kernel(Params P) {
         (residual && (tk.drow < 0 || tk.drow >= P.total_draft)))
         return;                                    // only reachable with inconsistent offsets
     if (tid < 64) sh.tab[tid] = kExp2Table[tid];
-    const RowStat rs = P.rows[tk.row];
     DrawRow<E> d;
-    init_draw_row<E>(d, P, tk.kind, tk.row, tk.drow, tk.pos, tk.v, rs.m, rs.z, P.temperature[b]);
+    init_draw_row<E>(d, P, tk.kind, tk.row, tk.drow, tk.pos, tk.v, tk.m, tk.z32, P.temperature[b]);
     __syncthreads();
     BlockRec* recs = P.recs + (size_t)b * NB;
     draw_blocks<E>(d, P.vocab, recs, c * kWaves, C * kWaves, NB, sh.tab);
@@ -1246,9 +1274,9 @@ __global__ __launch_bounds__(kThreads) void draw_kernel(Params P) {
     __syncthreads();
     if (tid == 0) sh.flag = (arrive(&P.draw_cnt[b]) == static_cast<uint32_t>(C - 1));
     __syncthreads();
-    if (!sh.flag) return;
+    if (!sh.flag || tid >= 64) return;
     if (tid == 0) reset_counter(&P.draw_cnt[b]);
-    const int y = draw_select<E>(d, P.vocab, NB, recs, sh, P.err);
+    const int y = draw_select_wave<E>(d, P.vocab, NB, recs, sh.tab, P.err);
     if (tid == 0) {
         P.out_tokens[(size_t)b * (P.gamma + 1) + tk.pos] = y;
         P.tasks[b].kind = kDrawNone;               // consumed: a stale task is never replayed
