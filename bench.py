@@ -81,6 +81,61 @@ def traffic_entry(kernel: str):
     return rec.get("bytes_per_launch")
 
 
+COPY_BYTES = 1 << 30         # counter scale reference: bytes read (and written) per copy
+COPY_REPS = 3
+
+
+def read_counters(path):
+    """{kernel name: (dispatches, mean counter value per dispatch)} of one rocprofv3
+    counter_collection.csv (values of one dispatch summed over its rows)."""
+    import csv
+    per = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            key = (row["Kernel_Name"], row.get("Dispatch_Id") or row.get("Correlation_Id"))
+            per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        n, tot = out.get(name, (0, 0.0))
+        out[name] = (n + 1, tot + v)
+    return {k: (n, tot / n) for k, (n, tot) in out.items()}
+
+
+def write_traffic(fetch_csv, write_csv):
+    """Counter-derived HBM bytes per launch of every verify kernel.  FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) are each scaled by what the same counter reads for
+    the elementwise copy of COPY_BYTES (so the figure is in the copy's terms)."""
+    fetch, write = read_counters(fetch_csv), read_counters(write_csv)
+    copy = [k for k in fetch if "elementwise" in k and fetch[k][0] >= COPY_REPS]
+    if not copy:
+        raise SystemExit("no elementwise copy kernel in the counter file")
+    ck = max(copy, key=lambda k: fetch[k][1])
+    f_scale = COPY_BYTES / (fetch[ck][1] * 1024.0)
+    w_scale = COPY_BYTES / (write[ck][1] * 1024.0)
+    sha = kernel_source_sha()
+    for name in fetch:
+        short = None
+        for kn in ("rows_flat_kernel", "rows_split_kernel", "draw_kernel", "step_kernel"):
+            if kn in name:
+                short = f"{kn}<{'BF16' if 'BF16' in name else 'F32'}>"
+        if short is None or name not in write:
+            continue
+        rec = {"kernel": short, "workload": "B=64, gamma=5, V=151936, bf16 logits, fp32 q, T=0.8",
+               "dispatches": fetch[name][0],
+               "fetch_kib_per_dispatch": fetch[name][1], "write_kib_per_dispatch": write[name][1],
+               "copy_reference": {"kernel": ck, "bytes": COPY_BYTES,
+                                  "fetch_kib": fetch[ck][1], "write_kib": write[ck][1],
+                                  "fetch_scale": f_scale, "write_scale": w_scale},
+               "bytes_per_launch": int(fetch[name][1] * 1024.0 * f_scale + write[name][1] * 1024.0 * w_scale),
+               "fetch_bytes_per_launch": int(fetch[name][1] * 1024.0 * f_scale),
+               "write_bytes_per_launch": int(write[name][1] * 1024.0 * w_scale),
+               "kernel_source_sha256": sha,
+               "sources": {"fetch": os.path.relpath(fetch_csv, ROOT), "write": os.path.relpath(write_csv, ROOT)}}
+        with open(traffic_path(short), "w") as f:
+            json.dump(rec, f, indent=1)
+        print(f"{short}: {rec['bytes_per_launch'] / 1e6:.1f} MB per launch -> {traffic_path(short)}")
+
+
 def cpu_baseline(inp, budget_s=12.0):
     import oracle
     t0 = time.perf_counter()
@@ -105,7 +160,18 @@ def main():
     ap.add_argument("--seed-replicate", type=int, default=0)
     ap.add_argument("--schedule", choices=["auto", "fused", "twokernel"], default="auto",
                     help="one-launch step, rows + draw kernels, or the library's choice")
+    ap.add_argument("--profile-steps", type=int, default=200,
+                    help="steps of the per-kernel HIP-event timing pass")
+    ap.add_argument("--pmc-workload", action="store_true",
+                    help="for rocprofv3 counter passes: a plain copy of known size (the scale "
+                         "reference), then --warmup + --steps verify steps; prints no JSON")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="(CPU only) turn two counter_collection.csv files of --pmc-workload runs "
+                         "into per-kernel HBM traffic records under profiles/")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the verify step shards by "
               "request with no exchange, so N GPUs run N independent copies of this step.",
@@ -138,6 +204,13 @@ def main():
     torch.cuda.synchronize()
 
     fused = {"auto": None, "fused": True, "twokernel": False}[args.schedule]
+    if args.pmc_workload:
+        # the scale reference: an elementwise copy reading and writing COPY_BYTES each
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(COPY_REPS):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
     sv = SpecVerify(inp.batch, inp.gamma, inp.vocab, inp.dtype, device=0, fused=fused)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
@@ -166,6 +239,10 @@ def main():
     ms_per_step = total_ms / args.steps
 
     sv_schedule = sv.last_schedule()
+    if args.pmc_workload:
+        log(f"[bench] counter workload done: {args.warmup + args.steps} steps")
+        sv.close()
+        return
     tok, num = base.results()
     for c in copies[1:]:
         t2, n2 = c.results()
@@ -179,7 +256,7 @@ def main():
         step(svp, i)
     torch.cuda.synchronize()
     svp.profile_read()
-    kp = max(200, min(args.steps, 2000))
+    kp = max(1, args.profile_steps)
     for i in range(kp):
         step(svp, i)
     rows_ms, draw_ms, n_prof = svp.profile_read()

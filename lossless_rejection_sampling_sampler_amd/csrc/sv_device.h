@@ -12,22 +12,21 @@
 //                of loads in flight per thread), keeping a per-thread online max
 //                and sum of exp2((l - m) * log2(e) / T) (fp32 exponentials summed
 //                into fp64), or a running argmax for greedy rows; reduces across
-//                the 64-wide waves with cross-lane shuffles and across the four
-//                waves through LDS, and writes one partial per (row, piece).
-//                When rows are 16-byte aligned the flattened [rows x vocab]
-//                stream is cut into equal contiguous ranges, one per workgroup
-//                (a range covers pieces of one or two rows); otherwise each row
-//                is cut into equal splits with scalar head/tail handling.
-//                The last piece of a row to finish merges the pieces; the last
-//                row of a request to finish runs that request's accept tests,
-//                finds the first rejection, writes the outputs and leaves a draw
-//                task.
+//                the 64-wide waves with DPP lane moves and across the four waves
+//                through LDS, and writes one partial per (row, piece).  When
+//                rows are 16-byte aligned the flattened [rows x vocab] stream is
+//                cut into equal contiguous ranges, one per workgroup (a range
+//                covers pieces of one or two rows); otherwise each row is cut
+//                into equal splits with scalar head/tail handling.  The last
+//                piece of a row to finish merges the pieces; the last row of a
+//                request to finish runs that request's accept tests, finds the
+//                first rejection, writes the outputs and leaves a draw task.
 //   draw kernel  streams the one draw row of every sampled request (residual
-//                (p - q)_+ or bonus p) in fp64, one 512-token block per wave, and
-//                records per-block sums; the last workgroup of the request
-//                rebuilds the exact fp64 normaliser, picks the block holding
-//                v * S with an LDS block scan, rescans that block token by token
-//                and writes the token.
+//                (p - q)_+ or bonus p) in fp64, one 2048-token block per wave,
+//                and records per-block sums; the first wave of the last
+//                workgroup of the request rebuilds the exact fp64 normaliser,
+//                picks the block holding v * S with a block scan, rescans that
+//                block token by token and writes the token.
 //
 // Cross-workgroup hand-off uses per-row / per-request arrival counters; see
 // the note at wait_stores().  Counters are reset by their last arrival (rows,

@@ -168,12 +168,16 @@ def parity_check(inp, uniform_sets: Optional[list] = None, sv=None, label="", fu
     log(f"[parity] {label} B={inp.batch} gamma={inp.gamma} V={inp.vocab} {inp.dtype} sets={len(sets)} "
         f"{'fused' if fused else 'two-kernel'}: gpu")
     res, dg, sv = run_gpu(inp, sets, sv=sv, fused=fused)
-    log(f"[parity] {label}: oracle")
-    orcs = oracle.verify(inp, uniform_sets=sets)
     rep = ParityReport()
-    for (tok, num), orc, u in zip(res, orcs, sets):
-        rep.merge(compare(inp, u, tok, num, orc))
-    errs = check_diag(inp, orcs[0], dg)
+    errs = []
+    chunk = 16                      # sets per oracle call: a progress line every few seconds
+    for c0 in range(0, len(sets), chunk):
+        log(f"[parity] {label}: oracle sets {c0}..{min(c0 + chunk, len(sets)) - 1}")
+        orcs = oracle.verify(inp, uniform_sets=sets[c0:c0 + chunk])
+        for (tok, num), orc, u in zip(res[c0:c0 + chunk], orcs, sets[c0:c0 + chunk]):
+            rep.merge(compare(inp, u, tok, num, orc))
+        if c0 == 0:
+            errs = check_diag(inp, orcs[0], dg)
     log(f"[parity] {label}: requests={rep.requests} mismatched={rep.mismatched} "
         f"excused={rep.excused} unexcused={len(rep.unexcused)} diag_errors={errs}")
     return rep, errs, sv
