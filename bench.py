@@ -39,9 +39,15 @@ def traffic_path(kernel: str) -> str:
 
 
 def kernel_source_sha() -> str:
+    """Hash of the kernel sources with comments and blank lines dropped (a change
+    of wording does not void a counter record; any change of code does)."""
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        h.update(open(os.path.join(CSRC, f), "rb").read())
+        for line in open(os.path.join(CSRC, f), encoding="utf-8"):
+            code = re.sub(r"//.*", "", line).rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 
