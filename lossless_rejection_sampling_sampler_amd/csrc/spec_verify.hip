@@ -18,7 +18,6 @@
 namespace {
 
 constexpr int kRowVecsPerThread = 8;    // target 16-byte vectors per thread per row split
-constexpr int kDrawTargetWgs = 2048;    // draw-kernel workgroups to aim for per call
 constexpr int kProfileRing = 2048;      // calls between forced event folds
 
 struct Geometry {
@@ -37,11 +36,11 @@ Geometry geometry_for(int vocab, int dtype) {
     return g;
 }
 
-// One-launch geometry: pieces per row (about kPieceVecs vectors per lane each,
-// at most one per merge lane); the resident single-wave workgroups split into
-// row waves and draw waves (enough draw waves that every draw block has an
-// owner lane, and about kDrawShare of the grid otherwise).
-constexpr double kDrawShare = 0.375;
+// One-launch geometry: pieces of kPieceVecs vectors per row (at most one per
+// merge lane, else the step is not used); the resident single-wave workgroups
+// split into row waves and draw waves (enough draw waves that every draw block
+// has an owner lane, and about kDrawShare of the grid otherwise).
+constexpr double kDrawShare = 0.5;
 
 struct StepGeometry {
     int grid, row_waves, pieces, items;
@@ -50,15 +49,15 @@ struct StepGeometry {
 
 StepGeometry step_geometry(long vpr, int gamma, int batch, int nblocks, int resident) {
     StepGeometry sg;
-    long p = (vpr + 64L * sv::kPieceVecs - 1) / (64L * sv::kPieceVecs);
-    sg.pieces = static_cast<int>(std::max(1L, std::min<long>(p, sv::kMaxStepPieces)));
+    const long p = std::max(1L, (vpr + sv::kPieceVecs - 1) / sv::kPieceVecs);
+    sg.pieces = static_cast<int>(std::min<long>(p, sv::kMaxStepPieces));
     sg.items = (gamma + 1) * batch * sg.pieces;
     const long need = ((long)batch * nblocks + sv::kMaxOwnBlocks - 1) / sv::kMaxOwnBlocks;
     const long draw = std::max<long>(need, static_cast<long>(resident * kDrawShare));
     const long rows = std::min<long>(resident - draw, sg.items);
     sg.row_waves = static_cast<int>(std::max(0L, rows));
     sg.grid = static_cast<int>(std::max(0L, rows + draw));
-    sg.ok = resident > 0 && rows >= 1 && gamma <= sv::kMaxGammaStep;
+    sg.ok = resident > 0 && rows >= 1 && gamma <= sv::kMaxGammaStep && p <= sv::kMaxStepPieces;
     return sg;
 }
 
@@ -194,6 +193,7 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
             return SV_ERR_DEVICE;
         }
         ctx->resident_flat = std::max(1, cus * std::max(1, per_cu));
+
         int coop = 0, per_bf16 = 0, per_f32 = 0;
         if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, device) != hipSuccess) coop = 0;
         if (coop &&
@@ -304,8 +304,9 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
     P.vocab = a->vocab;
     P.splits = ctx->geo.splits;
     P.nblocks = ctx->geo.nblocks;
-    int C = (kDrawTargetWgs + a->batch - 1) / a->batch;
-    C = std::max(1, std::min(C, (ctx->geo.nblocks + sv::kWaves - 1) / sv::kWaves));
+    // draw workgroups per request: one block per wave (a wave with two blocks
+    // would finish its request later than a second round of workgroups does)
+    const int C = std::max(1, (ctx->geo.nblocks + sv::kWaves - 1) / sv::kWaves);
     P.draw_wgs = C;
     P.parts = ctx->parts;
     P.rows = ctx->rows;

@@ -148,6 +148,7 @@ struct F32 {
     static __device__ __forceinline__ uint32_t bits1(const void* row, long x) {
         return static_cast<const uint32_t*>(row)[x];
     }
+    static __device__ __forceinline__ float from_bits(uint32_t b) { return __uint_as_float(b); }
     static constexpr int kBits = 32;
     static constexpr uint32_t kNegInfBits = 0xff800000u;
     static constexpr uint32_t kNegInfWord = 0xff800000u;
@@ -168,6 +169,7 @@ struct BF16 {
     static __device__ __forceinline__ uint32_t bits1(const void* row, long x) {
         return static_cast<uint32_t>(static_cast<const uint16_t*>(row)[x]);
     }
+    static __device__ __forceinline__ float from_bits(uint32_t b) { return __uint_as_float(b << 16); }
     static constexpr int kBits = 16;
     static constexpr uint32_t kNegInfBits = 0xff80u;
     static constexpr uint32_t kNegInfWord = 0xff80ff80u;

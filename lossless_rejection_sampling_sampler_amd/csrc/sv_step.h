@@ -8,7 +8,8 @@
 //
 // A persistent, cooperatively launched grid of single-wave workgroups (all
 // resident at once; no workgroup barriers, latency is hidden by the other
-// waves of the CU and by a software pipeline inside each wave) runs:
+// waves of the CU and by a software pipeline inside each wave), split into row
+// waves and draw waves, runs:
 //
 //   row pieces  Every target row is cut into P <= 64 equal pieces.  Pieces are
 //               taken in position-major order (position 0 of every request,
@@ -55,8 +56,11 @@ constexpr int kSpinLimit = 1 << 20;      // bounded wait for a publication (abou
 constexpr int kTagSpin = 1 << 16;        // bounded re-reads of piece records already sent
 constexpr int kMaxGammaStep = 30;        // decided bits 0..30 of the per-request word
 constexpr int kMaxStepPieces = 64;       // pieces per row: one merge lane each
-constexpr int kPieceVecs = 6;            // target 16-byte vectors per lane per piece
-constexpr int kStepBatch = 2;            // vectors per lane per load batch
+constexpr int kStepBatch = 2;            // 16-byte vectors per lane per load batch
+constexpr int kPieceBatches = 6;         // batches per row piece: 12 vectors per lane
+constexpr int kRing = 3;                 // batches in flight per row wave
+constexpr int kPieceLaneVecs = kPieceBatches * kStepBatch;
+constexpr int kPieceVecs = 64 * kPieceLaneVecs;   // 768 vectors (12 KiB) per piece
 constexpr int kMaxDeferred = 128;        // deferred pieces per wave (LDS)
 constexpr int kMaxOwnBlocks = 64;        // draw blocks per wave: one per lane
 
@@ -148,13 +152,15 @@ __device__ __forceinline__ Cand cand_load(const StepParams& S, int j) {
     return c;
 }
 
-// An item picked for streaming, with its first loads in flight.
+// An item picked for streaming: its coordinates, its piece's vectors and the
+// request's temperature (loaded one piece ahead).
 struct Item {
     int j;                       // item index; -1: none
     int i, b, p, gb, d0;         // position, request, piece, gamma_b, first draft row
     float T;                     // temperature of the request
     int xd;                      // lane 0, piece 0 of a draft row: the drafted token
-    v4u A[kStepBatch];           // this lane's first batch of vectors
+    const v4u* base;             // the piece's first vector
+    int cnt;                     // vectors in the piece (<= kPieceVecs)
 };
 
 // Fills the item's coordinates from a candidate; false when the row does not
@@ -178,36 +184,7 @@ __device__ __forceinline__ bool item_coords(const StepParams& S, int j, int o0, 
     return it.i <= it.gb;
 }
 
-// This lane's vectors of piece p: v0 + lane + 64 n, n < count.
-__device__ __forceinline__ void piece_range(const StepParams& S, int p, long& v0, int& count) {
-    const int lane = threadIdx.x & 63;
-    v0 = (long)p * S.vpr / S.pieces;
-    const long v1 = (long)(p + 1) * S.vpr / S.pieces;
-    const long span = v1 - v0 - lane;
-    count = span > 0 ? static_cast<int>((span + 63) / 64) : 0;
-}
-
-template <typename E>
-__device__ __forceinline__ const v4u* piece_base(const StepParams& S, const Item& it) {
-    const typename E::T* row =
-        static_cast<const typename E::T*>(S.p.logits) + (size_t)((long)it.d0 + it.b + it.i) * S.p.vocab;
-    return reinterpret_cast<const v4u*>(row);
-}
-
-// Loads vectors j0 .. j0 + kStepBatch - 1 of this lane (p0 + 64 j).  Every
-// load is issued (no branches, so the compiler can count them): indexes past
-// the lane's count re-read its last vector (or the piece's first when it has
-// none), and are masked to -inf when consumed.
-template <typename E>
-__device__ __forceinline__ void load_step_batch(v4u* X, const v4u* p0, const v4u* first, int j0, int count) {
-#pragma unroll
-    for (int u = 0; u < kStepBatch; ++u) {
-        const int jj = min(j0 + u, count - 1);
-        X[u] = __builtin_nontemporal_load(jj >= 0 ? p0 + (long)jj * 64 : first);
-    }
-}
-
-// Issues the item's loads: temperature, drafted token (piece 0), first batch.
+// Issues the item's small loads (temperature, drafted token) and sets its piece.
 template <typename E>
 __device__ __forceinline__ void item_issue(const StepParams& S, Item& it) {
     const Params& P = S.p;
@@ -215,96 +192,78 @@ __device__ __forceinline__ void item_issue(const StepParams& S, Item& it) {
     it.T = P.temperature[it.b];
     it.xd = -1;
     if (lane == 0 && it.p == 0 && it.i < it.gb) it.xd = P.ids[it.d0 + it.i];
-    long v0;
-    int count;
-    piece_range(S, it.p, v0, count);
-    const v4u* base = piece_base<E>(S, it) + v0;
-    load_step_batch<E>(it.A, base + lane, base, 0, count);
+    const long t = (long)it.d0 + it.b + it.i;
+    const long v0 = (long)it.p * kPieceVecs;
+    it.base = reinterpret_cast<const v4u*>(static_cast<const typename E::T*>(P.logits) + (size_t)t * P.vocab) + v0;
+    it.cnt = static_cast<int>(min((long)kPieceVecs, S.vpr - v0));
 }
 
-// Streams the item's piece (first batch already in it.A): returns the wave's
-// (max, sum) or (argmax value, argmax) in every lane.
-template <typename E>
-__device__ __forceinline__ void stream_item(const StepParams& S, Item& it, bool greedy, float c, const double* tab,
-                                            float& m_out, int& g_out, double& z_out) {
-    constexpr int U = kStepBatch;
+// Loads batch e of the item's piece into X: lane L takes vectors L + 64 n.
+// Every load is issued (no branches, so the compiler can count them); vectors
+// past the piece re-read its last one and are masked when consumed.
+__device__ __forceinline__ void issue_batch(const Item& it, int e, v4u* X) {
     const int lane = threadIdx.x & 63;
-    long v0;
-    int n;
-    piece_range(S, it.p, v0, n);
-    const v4u* base = piece_base<E>(S, it) + v0;
-    const v4u* p0 = base + lane;
-    // batches are wave-uniform: lane 0 has the most vectors
-    const int nb = (rdlane(n, 0) + U - 1) / U;
-    float mt = -INFINITY;
-    double st = 0.0;
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    auto consume = [&](v4u* X, int j0) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) X[u] = (j0 + u < n) ? X[u] : v4u(E::kNegInfWord);
-        if (!greedy) {
-            // max pass, then the exponential pass decodes again (cheaper than
-            // keeping the whole decoded batch in registers)
-            float bm = -INFINITY;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float f[E::kPerVec];
-                E::decode(X[u], f);
-#pragma unroll
-                for (int k = 0; k < E::kPerVec; ++k) bm = fmaxf(bm, f[k]);
-            }
-            if (bm > mt) {
-                if (mt > -INFINITY)
-                    st *= exp2_nonpos((static_cast<double>(mt) - static_cast<double>(bm)) * static_cast<double>(c), tab);
-                mt = bm;
-            }
-            if (mt > -INFINITY) {
-                float acc = 0.0f;
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    v4u x = X[u];
-                    asm volatile("" : "+v"(x));       // decode afresh, do not keep the first pass
-                    float f[E::kPerVec];
-                    E::decode(x, f);
-#pragma unroll
-                    for (int k = 0; k < E::kPerVec; ++k) acc += __builtin_amdgcn_exp2f((f[k] - mt) * c);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                st += static_cast<double>(acc);
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float f[E::kPerVec];
-                E::decode(X[u], f);
-                const int x0 = static_cast<int>((v0 + lane + (long)(j0 + u) * 64) * E::kPerVec);
-#pragma unroll
-                for (int k = 0; k < E::kPerVec; ++k) argmax_merge(bv, bi, f[k], x0 + k);
-            }
-        }
-    };
-    v4u B[U];
-    for (int bk = 0; bk < nb; bk += 2) {
-        if (bk + 1 < nb) load_step_batch<E>(B, p0, base, (bk + 1) * U, n);
-        consume(it.A, bk * U);
-        if (bk + 1 >= nb) break;
-        if (bk + 2 < nb) load_step_batch<E>(it.A, p0, base, (bk + 2) * U, n);
-        consume(B, (bk + 1) * U);
+    for (int u = 0; u < kStepBatch; ++u) {
+        const int v = min((e * kStepBatch + u) * 64 + lane, it.cnt - 1);
+        X[u] = __builtin_nontemporal_load(it.base + v);
     }
+}
+
+// Per-lane running state of one piece.
+struct PieceAcc {
+    float mt;            // sampled: running max;  greedy: best value
+    int bi;              // greedy: best index
+    double st;           // sampled: running sum of exp2((l - mt) * c)
+};
+
+// Consumes batch e of the item's piece from X.
+template <typename E>
+__device__ __forceinline__ void consume_batch(const Item& it, int e, v4u* X, bool greedy, float c, const double* tab,
+                                              PieceAcc& acc) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int u = 0; u < kStepBatch; ++u)
+        X[u] = ((e * kStepBatch + u) * 64 + lane < it.cnt) ? X[u] : v4u(E::kNegInfWord);
     if (!greedy) {
-        const float M = wave_max(mt);
-        double zs = 0.0;
-        if (mt > -INFINITY)
-            zs = st * exp2_nonpos((static_cast<double>(mt) - static_cast<double>(M)) * static_cast<double>(c), tab);
-        z_out = wave_sum(zs);
-        m_out = M;
-        g_out = -1;
+        // max pass, then the exponential pass decodes again (cheaper than
+        // keeping the decoded batch in registers)
+        float bm = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kStepBatch; ++u) {
+            float f[E::kPerVec];
+            E::decode(X[u], f);
+#pragma unroll
+            for (int k = 0; k < E::kPerVec; ++k) bm = fmaxf(bm, f[k]);
+        }
+        if (bm > acc.mt) {
+            if (acc.mt > -INFINITY)
+                acc.st *= exp2_nonpos((static_cast<double>(acc.mt) - static_cast<double>(bm)) * static_cast<double>(c), tab);
+            acc.mt = bm;
+        }
+        if (acc.mt > -INFINITY) {
+            float sum = 0.0f;
+#pragma unroll
+            for (int u = 0; u < kStepBatch; ++u) {
+                v4u x = X[u];
+                asm volatile("" : "+v"(x));       // decode afresh, do not keep the first pass
+                float f[E::kPerVec];
+                E::decode(x, f);
+#pragma unroll
+                for (int k = 0; k < E::kPerVec; ++k) sum += __builtin_amdgcn_exp2f((f[k] - acc.mt) * c);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            acc.st += static_cast<double>(sum);
+        }
     } else {
-        wave_argmax(bv, bi);
-        m_out = bv;
-        g_out = bi;
-        z_out = 0.0;
+#pragma unroll
+        for (int u = 0; u < kStepBatch; ++u) {
+            float f[E::kPerVec];
+            E::decode(X[u], f);
+            const int x0 = (it.p * kPieceVecs + (e * kStepBatch + u) * 64 + lane) * E::kPerVec;
+#pragma unroll
+            for (int k = 0; k < E::kPerVec; ++k) argmax_merge(acc.mt, acc.bi, f[k], x0 + k);
+        }
     }
 }
 
@@ -474,34 +433,38 @@ __device__ __forceinline__ void finish_arrival(const StepParams& S, const Arriva
     step_resolve(S, b, gb, d0, k, T, mk, zk, gk);
 }
 
-// Streams the item's piece, stores its record and counts it on the row's
-// arrival counter; returns the arrival (its result is read one piece later).
+// Ends a streamed piece: wave reductions, the tagged record (with the drafted
+// token's logit and q for piece 0 of a draft row, gathered while the piece
+// streamed) and the arrival on the row's counter, whose result is read one
+// piece later.
 template <typename E>
-__device__ __forceinline__ Arrival step_piece(const StepParams& S, Item& it, const double* tab) {
+__device__ __forceinline__ Arrival item_finish(const StepParams& S, const Item& it, bool greedy, float c,
+                                               const PieceAcc& acc, float lx, float qx, const double* tab) {
     const Params& P = S.p;
     const int lane = threadIdx.x & 63;
-    const float T = it.T;
-    const bool greedy = !(T > 0.0f);
-    const float c = greedy ? 0.0f : static_cast<float>(kLog2e / static_cast<double>(T));
     const long t = (long)it.d0 + it.b + it.i;
-    // piece 0 of a draft row gathers the drafted token's logit and q for the accept test
-    float lx = 0.0f, qx = 0.0f;
-    if (lane == 0 && it.xd >= 0 && it.xd < P.vocab && !greedy) {
-        const typename E::T* row = static_cast<const typename E::T*>(P.logits) + (size_t)t * P.vocab;
-        lx = E::load1(row, it.xd);
-        qx = P.q[(size_t)(it.d0 + it.i) * P.vocab + it.xd];
-    }
     float pm;
     int pg;
-    double pz;
-    stream_item<E>(S, it, greedy, c, tab, pm, pg, pz);
+    double pz = 0.0;
+    if (!greedy) {
+        pm = wave_max(acc.mt);
+        double zs = 0.0;
+        if (acc.mt > -INFINITY)
+            zs = acc.st * exp2_nonpos((static_cast<double>(acc.mt) - static_cast<double>(pm)) * static_cast<double>(c), tab);
+        pz = wave_sum(zs);
+        pg = -1;
+    } else {
+        pm = acc.mt;
+        pg = acc.bi;
+        wave_argmax(pm, pg);
+    }
     Arrival a;
     a.valid = true;
     a.i = it.i;
     a.b = it.b;
     a.gb = it.gb;
     a.d0 = it.d0;
-    a.T = T;
+    a.T = it.T;
     a.old = 0u;
     if (lane == 0) {
         PieceRec* pr = &S.precs[(size_t)t * kMaxStepPieces + it.p];
@@ -552,16 +515,20 @@ __device__ __forceinline__ void step_block(const StepParams& S, int cid, unsigne
     }
 }
 
-// Row waves: pieces in position-major order, software-pipelined.
+// Row waves: pieces in position-major order as one continuous stream.  Three
+// batches (six vectors per lane) are always in flight: while the current
+// piece's batch e is consumed, batch e + 3 is issued, which for the piece's
+// last three batches is the next piece's first three.
 template <typename E>
 __device__ __forceinline__ void row_wave(const StepParams& S, int w, int R, const double* tab, int* defer) {
+    const Params& P = S.p;
     const int lane = threadIdx.x & 63;
     // candidates w, w + R, ... with their request words loaded two ahead
     Cand c0 = cand_load(S, w);
     Cand c1 = cand_load(S, w + R);
     int nd = 0, qd = 0;                       // deferred pieces: count, next
     // picks the next item to stream (deferring pieces of resolved requests) and
-    // issues its loads; it.j = -1 when there is none
+    // issues its small loads; it.j = -1 when there is none
     auto pick = [&](Item& it) {
         while (c0.j < S.items) {
             const Cand c = c0;
@@ -581,10 +548,10 @@ __device__ __forceinline__ void row_wave(const StepParams& S, int w, int R, cons
             __syncthreads();
             const int j = defer[qd++];
             int o0 = 0, o1 = 0;
-            if (S.p.offsets) {
-                const int b = (j / S.pieces) % S.p.batch;
-                o0 = S.p.offsets[b];
-                o1 = S.p.offsets[b + 1];
+            if (P.offsets) {
+                const int b = (j / S.pieces) % P.batch;
+                o0 = P.offsets[b];
+                o1 = P.offsets[b + 1];
             }
             if (!item_coords(S, j, o0, o1, it)) continue;
             item_issue<E>(S, it);
@@ -592,16 +559,56 @@ __device__ __forceinline__ void row_wave(const StepParams& S, int w, int R, cons
         }
         it.j = -1;
     };
-    Item nxt;
+    Item cur, nxt;
+    pick(cur);
+    if (cur.j < 0) return;
     pick(nxt);
+    v4u R0[kStepBatch], R1[kStepBatch], R2[kStepBatch];
+    issue_batch(cur, 0, R0);
+    issue_batch(cur, 1, R1);
+    issue_batch(cur, 2, R2);
     Arrival arr;
     arr.valid = false;
-    while (nxt.j >= 0) {
-        Item cur = nxt;
-        pick(nxt);                            // the next piece's loads fly while this one streams
-        const Arrival a = step_piece<E>(S, cur, tab);
+    while (cur.j >= 0) {
+        const float T = cur.T;
+        const bool greedy = !(T > 0.0f);
+        const float c = greedy ? 0.0f : static_cast<float>(kLog2e / static_cast<double>(T));
+        // piece 0 of a draft row gathers the drafted token's logit and q; every
+        // lane loads (an in-range element when it has nothing to gather), so
+        // no branch makes the compiler wait for the loads in flight
+        const bool gather = cur.xd >= 0 && cur.xd < P.vocab && !greedy;
+        const long tcur = (long)cur.d0 + cur.b + cur.i;
+        const int xg = gather ? cur.xd : 0;
+        const uint32_t lx_bits = E::bits1(static_cast<const typename E::T*>(P.logits) + (size_t)tcur * P.vocab, xg);
+        const float* qp = gather ? P.q + (size_t)(cur.d0 + cur.i) * P.vocab + xg : P.uniforms;
+        const float qx_raw = *qp;
+        PieceAcc acc;
+        acc.mt = -INFINITY;
+        acc.bi = 0x7fffffff;
+        acc.st = 0.0;
+        // with no next piece, the last three issues re-read this piece (never consumed)
+        const Item& nx = (nxt.j >= 0) ? nxt : cur;
+        consume_batch<E>(cur, 0, R0, greedy, c, tab, acc);
+        issue_batch(cur, 3, R0);
+        consume_batch<E>(cur, 1, R1, greedy, c, tab, acc);
+        issue_batch(cur, 4, R1);
+        consume_batch<E>(cur, 2, R2, greedy, c, tab, acc);
+        issue_batch(cur, 5, R2);
+        // the previous piece's arrival has had a few batches' worth of time to return
         if (arr.valid) finish_arrival<E>(S, arr, tab);
-        arr = a;
+        arr.valid = false;
+        consume_batch<E>(cur, 3, R0, greedy, c, tab, acc);
+        issue_batch(nx, 0, R0);
+        consume_batch<E>(cur, 4, R1, greedy, c, tab, acc);
+        issue_batch(nx, 1, R1);
+        consume_batch<E>(cur, 5, R2, greedy, c, tab, acc);
+        issue_batch(nx, 2, R2);
+        const float lx = gather ? E::from_bits(lx_bits) : 0.0f;
+        const float qx = gather ? qx_raw : 0.0f;
+        arr = item_finish<E>(S, cur, greedy, c, acc, lx, qx, tab);
+        const bool more = nxt.j >= 0;
+        cur = nxt;
+        if (more) pick(nxt);
     }
     if (arr.valid) finish_arrival<E>(S, arr, tab);
 }
@@ -644,7 +651,7 @@ __device__ __forceinline__ void draw_wave(const StepParams& S, int dw, int D, co
     }
 }
 
-// Workgroups [0, rows_waves) are row waves, the rest draw waves.
+// Workgroups [0, row_waves) are row waves, the rest draw waves.
 template <typename E>
 __global__ __launch_bounds__(kStepLanes, 3) void step_kernel(StepParams S) {
     __shared__ double tab[64];
