@@ -29,7 +29,7 @@ PEAK_HBM_GBPS = 8000.0
 CONFIG_ID = 3
 KDT = "BF16"
 CSRC = os.path.join(ROOT, "lossless_rejection_sampling_sampler_amd", "csrc")
-KERNEL_SOURCES = ("sv_device.h", "sv_step.h", "spec_verify.hip")
+KERNEL_SOURCES = ("sv_device.h", "spec_verify.hip")
 
 
 def traffic_path(kernel: str) -> str:
@@ -164,7 +164,7 @@ def main():
     ap.add_argument("--rotate", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed-replicate", type=int, default=0)
-    ap.add_argument("--schedule", choices=["auto", "fused", "twokernel"], default="auto",
+    ap.add_argument("--schedule", choices=["auto", "onelaunch", "twokernel"], default="auto",
                     help="one-launch step, rows + draw kernels, or the library's choice")
     ap.add_argument("--profile-steps", type=int, default=200,
                     help="steps of the per-kernel HIP-event timing pass")
@@ -188,7 +188,7 @@ def main():
     import torch
 
     from lossless_rejection_sampling_sampler_amd import SpecVerify, upload
-    from lossless_rejection_sampling_sampler_amd._lib import SV_SCHEDULE_FLAT, SV_SCHEDULE_ONE_LAUNCH, SV_SCHEDULE_SPLIT
+    from lossless_rejection_sampling_sampler_amd._lib import SCHEDULE_NAMES, SV_SCHEDULE_ONE_LAUNCH
     from synth import CONFIGS, make_config
 
     spec = CONFIGS[CONFIG_ID]
@@ -209,7 +209,7 @@ def main():
         copies.append(c)
     torch.cuda.synchronize()
 
-    fused = {"auto": None, "fused": True, "twokernel": False}[args.schedule]
+    schedule = None if args.schedule == "auto" else args.schedule
     if args.pmc_workload:
         # the scale reference: an elementwise copy reading and writing COPY_BYTES each
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
@@ -217,7 +217,7 @@ def main():
         for _ in range(COPY_REPS):
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
-    sv = SpecVerify(inp.batch, inp.gamma, inp.vocab, inp.dtype, device=0, fused=fused)
+    sv = SpecVerify(inp.batch, inp.gamma, inp.vocab, inp.dtype, device=0, schedule=schedule)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     # argument blocks are built once so the timed loop is one C call per step
@@ -257,7 +257,7 @@ def main():
     step_bytes = rows_b + draw_b
 
     # ---- per-kernel durations: HIP events recorded by the library on this stream
-    svp = SpecVerify(inp.batch, inp.gamma, inp.vocab, inp.dtype, device=0, profile=True, fused=fused)
+    svp = SpecVerify(inp.batch, inp.gamma, inp.vocab, inp.dtype, device=0, profile=True, schedule=schedule)
     for i in range(args.warmup):
         step(svp, i)
     torch.cuda.synchronize()
@@ -270,8 +270,7 @@ def main():
     rows_avg_ms, draw_avg_ms = rows_ms / n_prof, draw_ms / n_prof
     svp.close()
 
-    one_launch = svp_schedule == SV_SCHEDULE_ONE_LAUNCH
-    if one_launch:
+    if svp_schedule == SV_SCHEDULE_ONE_LAUNCH:
         # one kernel does the whole step: its bytes are the step's
         kname, kbytes = f"step_kernel<{KDT}>", step_bytes
     else:
@@ -299,8 +298,7 @@ def main():
         "hbm_gbps": round(step_gbps, 1),
         "frac_of_peak": round(step_gbps / PEAK_HBM_GBPS, 4),
         "algorithmic_bytes_per_step": step_bytes,
-        "schedule": {SV_SCHEDULE_ONE_LAUNCH: "one-launch", SV_SCHEDULE_FLAT: "rows+draw",
-                     SV_SCHEDULE_SPLIT: "rows-split+draw"}.get(sv_schedule, "none"),
+        "schedule": SCHEDULE_NAMES.get(sv_schedule, "none"),
         "kernels": {"rows_ms": round(rows_avg_ms, 6), "draw_ms": round(draw_avg_ms, 6),
                     "rows_bytes": rows_b, "draw_bytes": draw_b, "events_over_steps": n_prof},
         "acceptance": {"mean_accepted": float(num.mean()),

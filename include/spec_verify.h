@@ -66,9 +66,12 @@ enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 };
 enum sv_flags {
     SV_FLAG_PROFILE = 1u,      /* record per-kernel HIP events (see spec_verify_profile_read) */
     SV_FLAG_TWO_KERNEL = 2u,   /* schedule: rows kernel, then draw kernel */
-    SV_FLAG_ONE_LAUNCH = 4u    /* schedule: one cooperative launch (rows must be 16-byte aligned,
-                                  else the two-kernel schedule is used); with neither flag the
-                                  library picks the faster schedule for the shape */
+    SV_FLAG_ONE_LAUNCH = 4u    /* schedule: one launch whose workgroups stream their rows, then
+                                  turn to draw blocks (rows must be 16-byte aligned, else the
+                                  two-kernel schedule is used).  The grid is sized to what the
+                                  device holds at once, so its workgroups wait on each other: it
+                                  needs the device to itself (see SV_DEVERR_STALLED).  With no
+                                  schedule flag the library picks the faster schedule */
 };
 
 /* Device-side contract violations, OR-ed into a sticky per-context word. */
@@ -79,9 +82,9 @@ enum sv_device_error {
                                   are unspecified (no access leaves the buffers' bounds) */
     SV_DEVERR_NONFINITE = 4u,  /* a draw row without positive finite mass (a target row with no
                                   finite logit, or NaN logits); that token is unspecified */
-    SV_DEVERR_STALLED = 8u     /* one-launch schedule: a bounded wait for data another workgroup
-                                  had already sent expired (never expected); that call's outputs
-                                  are unspecified */
+    SV_DEVERR_STALLED = 8u     /* one-launch schedule: a bounded wait (seconds) for a draw task
+                                  expired, e.g. because other work kept part of the grid from
+                                  becoming resident; that call's outputs are unspecified */
 };
 
 /* Limits fixed at creation.  max_gamma <= SV_MAX_GAMMA. */
@@ -175,7 +178,7 @@ enum sv_schedule {
     SV_SCHEDULE_NONE = 0,       /* no call yet, or the last call had batch == 0 */
     SV_SCHEDULE_SPLIT = 1,      /* rows kernel with per-row pieces (unaligned rows), draw kernel */
     SV_SCHEDULE_FLAT = 2,       /* rows kernel over the flattened rows, draw kernel */
-    SV_SCHEDULE_ONE_LAUNCH = 3  /* one cooperative launch */
+    SV_SCHEDULE_ONE_LAUNCH = 3  /* one launch: rows, then draws, per workgroup */
 };
 
 /* Writes the sv_schedule of the last successful run to *schedule.  Host-only

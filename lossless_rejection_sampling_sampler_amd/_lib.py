@@ -36,6 +36,10 @@ SV_SCHEDULE_SPLIT = 1
 SV_SCHEDULE_FLAT = 2
 SV_SCHEDULE_ONE_LAUNCH = 3
 
+SCHEDULE_FLAGS = {None: 0, "auto": 0, "twokernel": SV_FLAG_TWO_KERNEL, "onelaunch": SV_FLAG_ONE_LAUNCH}
+SCHEDULE_NAMES = {SV_SCHEDULE_NONE: "none", SV_SCHEDULE_SPLIT: "rows-split+draw", SV_SCHEDULE_FLAT: "rows+draw",
+                  SV_SCHEDULE_ONE_LAUNCH: "one-launch"}
+
 EXPORTS = (
     "spec_verify_create",
     "spec_verify_run",
@@ -132,7 +136,7 @@ class SpecVerify:
     """
 
     def __init__(self, max_batch: int, max_gamma: int, vocab: int, logits_dtype: str = "bf16",
-                 device: int = 0, profile: bool = False, fused: Optional[bool] = None):
+                 device: int = 0, profile: bool = False, schedule: Optional[str] = None):
         self._lib = load_library()
         self.vocab = int(vocab)
         self.device = int(device)
@@ -140,7 +144,7 @@ class SpecVerify:
         cfg = SVConfig(int(max_batch), int(max_gamma), int(vocab),
                        SV_BF16 if logits_dtype == "bf16" else SV_F32,
                        (SV_FLAG_PROFILE if profile else 0)
-                       | (0 if fused is None else (SV_FLAG_ONE_LAUNCH if fused else SV_FLAG_TWO_KERNEL)))
+                       | SCHEDULE_FLAGS[schedule])
         handle = ctypes.c_void_p()
         st = self._lib.spec_verify_create(ctypes.byref(cfg), self.device, ctypes.byref(handle))
         if st != SV_OK:

@@ -13,12 +13,12 @@
 
 #include "spec_verify.h"
 #include "sv_device.h"
-#include "sv_step.h"
 
 namespace {
 
 constexpr int kRowVecsPerThread = 8;    // target 16-byte vectors per thread per row split
 constexpr int kProfileRing = 2048;      // calls between forced event folds
+constexpr int kDrawBlocksPerWave = 2;   // draw kernel: blocks per wave (the kernel takes at most 2)
 
 struct Geometry {
     int splits;          // split rows kernel: workgroups per row
@@ -34,31 +34,6 @@ Geometry geometry_for(int vocab, int dtype) {
     g.splits = static_cast<int>(s);
     g.nblocks = (vocab + sv::kBlockElems - 1) / sv::kBlockElems;
     return g;
-}
-
-// One-launch geometry: pieces of kPieceVecs vectors per row (at most one per
-// merge lane, else the step is not used); the resident single-wave workgroups
-// split into row waves and draw waves (enough draw waves that every draw block
-// has an owner lane, and about kDrawShare of the grid otherwise).
-constexpr double kDrawShare = 0.5;
-
-struct StepGeometry {
-    int grid, row_waves, pieces, items;
-    bool ok;
-};
-
-StepGeometry step_geometry(long vpr, int gamma, int batch, int nblocks, int resident) {
-    StepGeometry sg;
-    const long p = std::max(1L, (vpr + sv::kPieceVecs - 1) / sv::kPieceVecs);
-    sg.pieces = static_cast<int>(std::min<long>(p, sv::kMaxStepPieces));
-    sg.items = (gamma + 1) * batch * sg.pieces;
-    const long need = ((long)batch * nblocks + sv::kMaxOwnBlocks - 1) / sv::kMaxOwnBlocks;
-    const long draw = std::max<long>(need, static_cast<long>(resident * kDrawShare));
-    const long rows = std::min<long>(resident - draw, sg.items);
-    sg.row_waves = static_cast<int>(std::max(0L, rows));
-    sg.grid = static_cast<int>(std::max(0L, rows + draw));
-    sg.ok = resident > 0 && rows >= 1 && gamma <= sv::kMaxGammaStep && p <= sv::kMaxStepPieces;
-    return sg;
 }
 
 // Workgroups for the flat rows kernel: all resident at once, at least one batch
@@ -82,13 +57,10 @@ struct sv_ctx {
     Geometry geo{};
     int max_rows = 0;
     int resident_flat = 0;     // rows-flat workgroups resident at once on the device
-    int resident_step = 0;     // one-launch (single-wave) workgroups resident at once (0: no cooperative launch)
-    uint32_t epoch = 0;        // tag of the one-launch step's publication words
+    int resident_step = 0;     // one-launch workgroups resident at once
+    uint32_t epoch = 0;        // tag of the one-launch step's draw tasks
     int last_schedule = SV_SCHEDULE_NONE;
-    sv::PieceRec* precs = nullptr;
-    sv::DrawParams* dparams = nullptr;
-    unsigned long long* words = nullptr;
-    unsigned long long* state = nullptr;
+    uint32_t* task_tag = nullptr;
     // device scratch (one allocation)
     void* scratch = nullptr;
     sv::Piece* parts = nullptr;
@@ -194,12 +166,10 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
         }
         ctx->resident_flat = std::max(1, cus * std::max(1, per_cu));
 
-        int coop = 0, per_bf16 = 0, per_f32 = 0;
-        if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, device) != hipSuccess) coop = 0;
-        if (coop &&
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_bf16, sv::step_kernel<sv::BF16>, sv::kStepLanes, 0) ==
+        int per_bf16 = 0, per_f32 = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_bf16, sv::step_kernel<sv::BF16>, sv::kThreads, 0) ==
                 hipSuccess &&
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_f32, sv::step_kernel<sv::F32>, sv::kStepLanes, 0) ==
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_f32, sv::step_kernel<sv::F32>, sv::kThreads, 0) ==
                 hipSuccess)
             ctx->resident_step = cus * std::min(per_bf16, per_f32);
         (void)hipGetLastError();
@@ -212,10 +182,7 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
     const size_t o_tasks = off; off = align_up(off + n_b * sizeof(sv::DrawTask), 256);
     const size_t o_recs = off;  off = align_up(off + n_b * ctx->geo.nblocks * sizeof(sv::BlockRec), 256);
     const size_t o_cnt = off;   off = align_up(off + (n_rows + 2 * n_b + 1) * sizeof(uint32_t), 256);
-    const size_t o_fp = off;    off = align_up(off + n_rows * sv::kMaxStepPieces * sizeof(sv::PieceRec), 256);
-    const size_t o_dp = off;    off = align_up(off + n_b * sizeof(sv::DrawParams), 256);
-    const size_t o_wd = off;    off = align_up(off + n_b * sizeof(unsigned long long), 256);
-    const size_t o_st = off;    off = align_up(off + n_b * sizeof(unsigned long long), 256);
+    const size_t o_tag = off;   off = align_up(off + n_b * sizeof(uint32_t), 256);
     const size_t total = off;
     if (hipMalloc(&ctx->scratch, total) != hipSuccess) {
         (void)hipGetLastError();
@@ -231,10 +198,7 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
     ctx->req_cnt = ctx->row_cnt + n_rows;
     ctx->draw_cnt = ctx->req_cnt + n_b;
     ctx->err = ctx->draw_cnt + n_b;
-    ctx->precs = reinterpret_cast<sv::PieceRec*>(base + o_fp);
-    ctx->dparams = reinterpret_cast<sv::DrawParams*>(base + o_dp);
-    ctx->words = reinterpret_cast<unsigned long long*>(base + o_wd);
-    ctx->state = reinterpret_cast<unsigned long long*>(base + o_st);
+    ctx->task_tag = reinterpret_cast<uint32_t*>(base + o_tag);
     if (hipMemset(ctx->scratch, 0, total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         free_ctx(ctx);
         return SV_ERR_DEVICE;
@@ -304,9 +268,10 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
     P.vocab = a->vocab;
     P.splits = ctx->geo.splits;
     P.nblocks = ctx->geo.nblocks;
-    // draw workgroups per request: one block per wave (a wave with two blocks
-    // would finish its request later than a second round of workgroups does)
-    const int C = std::max(1, (ctx->geo.nblocks + sv::kWaves - 1) / sv::kWaves);
+    // draw workgroups per request: at most kDrawBlocksPerWave blocks per wave,
+    // all of a wave's loads in flight together, and one round of workgroups
+    const int C = std::max(1, (ctx->geo.nblocks + sv::kWaves * kDrawBlocksPerWave - 1) /
+                                  (sv::kWaves * kDrawBlocksPerWave));
     P.draw_wgs = C;
     P.parts = ctx->parts;
     P.rows = ctx->rows;
@@ -316,6 +281,8 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
     P.req_cnt = ctx->req_cnt;
     P.draw_cnt = ctx->draw_cnt;
     P.err = ctx->err;
+    P.task_tag = nullptr;
+    P.epoch = 0;
 
     const long rows = (long)a->total_draft + a->batch;
     // rows start on 16-byte boundaries: stream the flattened rows in equal ranges
@@ -324,10 +291,9 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
     P.flat_vpr = (long)a->vocab * (long)esize / 16;
     P.flat_nv = rows * P.flat_vpr;
 
-    const StepGeometry sg = step_geometry(P.flat_vpr, a->gamma, a->batch, ctx->geo.nblocks, ctx->resident_step);
     // the one-launch step is opt-in until it beats the two-kernel schedule
-    const bool want_fused = (cfg.flags & SV_FLAG_ONE_LAUNCH) && !(cfg.flags & SV_FLAG_TWO_KERNEL);
-    const bool fused = aligned && want_fused && sg.ok;
+    const bool one_launch = aligned && (cfg.flags & SV_FLAG_ONE_LAUNCH) && !(cfg.flags & SV_FLAG_TWO_KERNEL) &&
+                            ctx->resident_step > 0;
 
     const bool prof = (cfg.flags & SV_FLAG_PROFILE) != 0;
     if (prof && ctx->prof_n == kProfileRing) {
@@ -336,25 +302,17 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
     }
     hipEvent_t* ev = prof ? &ctx->events[3 * ctx->prof_n] : nullptr;
     if (prof && hipEventRecord(ev[0], stream) != hipSuccess) return SV_ERR_DEVICE;
-    if (fused) {
+    if (one_launch) {
         if (++ctx->epoch == 0) ctx->epoch = 1;
-        sv::StepParams S;
-        S.p = P;
-        S.p.parts = nullptr;
-        S.vpr = P.flat_vpr;
-        S.pieces = sg.pieces;
-        S.items = sg.items;
-        S.epoch = ctx->epoch;
-        S.row_waves = sg.row_waves;
-        S.precs = ctx->precs;
-        S.dparams = ctx->dparams;
-        S.words = ctx->words;
-        S.state = ctx->state;
-        void* kargs[] = {&S};
-        const void* fn = (cfg.logits_dtype == SV_BF16) ? reinterpret_cast<const void*>(&sv::step_kernel<sv::BF16>)
-                                                        : reinterpret_cast<const void*>(&sv::step_kernel<sv::F32>);
-        if (hipLaunchCooperativeKernel(fn, dim3(sg.grid), dim3(sv::kStepLanes), kargs, 0, stream) != hipSuccess)
-            return SV_ERR_DEVICE;
+        P.task_tag = ctx->task_tag;
+        P.epoch = ctx->epoch;
+        const int grid = flat_workgroups(P.flat_nv, P.flat_vpr, ctx->resident_step);
+        // an ordinary launch: the grid never exceeds what the device holds at once
+        // (a cooperative launch would guarantee it, at a cost of microseconds per call)
+        if (cfg.logits_dtype == SV_BF16)
+            hipLaunchKernelGGL(sv::step_kernel<sv::BF16>, dim3((unsigned)grid), dim3(sv::kThreads), 0, stream, P);
+        else
+            hipLaunchKernelGGL(sv::step_kernel<sv::F32>, dim3((unsigned)grid), dim3(sv::kThreads), 0, stream, P);
         if (prof && hipEventRecord(ev[1], stream) != hipSuccess) return SV_ERR_DEVICE;
     } else {
         const long grid1 = aligned ? flat_workgroups(P.flat_nv, P.flat_vpr, ctx->resident_flat) : rows * P.splits;
@@ -381,7 +339,7 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
         ctx->prof_n++;
     }
     if (hipGetLastError() != hipSuccess) return SV_ERR_DEVICE;
-    ctx->last_schedule = fused ? SV_SCHEDULE_ONE_LAUNCH : (aligned ? SV_SCHEDULE_FLAT : SV_SCHEDULE_SPLIT);
+    ctx->last_schedule = one_launch ? SV_SCHEDULE_ONE_LAUNCH : (aligned ? SV_SCHEDULE_FLAT : SV_SCHEDULE_SPLIT);
     return SV_OK;
 }
 
@@ -400,7 +358,6 @@ int spec_verify_device_errors(sv_ctx* ctx, uint32_t* bits, int clear) {
         // also drop arrival counts a call with inconsistent offsets may have left behind
         const size_t n = (size_t)ctx->max_rows + 2 * (size_t)ctx->cfg.max_batch + 1;
         if (hipMemset(ctx->row_cnt, 0, n * sizeof(uint32_t)) != hipSuccess ||
-            hipMemset(ctx->state, 0, (size_t)ctx->cfg.max_batch * sizeof(unsigned long long)) != hipSuccess ||
             hipDeviceSynchronize() != hipSuccess)
             return SV_ERR_DEVICE;
     }

@@ -92,6 +92,9 @@ struct DrawTask {        // written by the resolving workgroup, read by the draw
     double z32;          // the draw row's normaliser (fp32 exponentials)
 };
 
+__device__ __forceinline__ void store_task(DrawTask* p, const DrawTask& t);
+__device__ __forceinline__ DrawTask load_task(const DrawTask* p);
+
 struct BlockRec {        // per (request, draw block) sums
     double se;           // sum of e = exp((l - m) / T) in fp64
     double ea;           // sum of e over tokens whose residual is clearly positive
@@ -132,6 +135,10 @@ struct Params {
     uint32_t* req_cnt;
     uint32_t* draw_cnt;
     uint32_t* err;
+    // phased one-launch step: request b's draw task is complete once
+    // task_tag[b] == epoch (nonzero, new every call)
+    uint32_t* task_tag;
+    uint32_t epoch;
 };
 
 // ----------------------------------------------------------------- element types
@@ -198,52 +205,64 @@ __device__ __forceinline__ uint32_t arrive(uint32_t* cnt) {
     wait_stores();
     return __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint32_t arrive_n(uint32_t* cnt, uint32_t n) {
+    wait_stores();
+    return __hip_atomic_fetch_add(cnt, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void reset_counter(uint32_t* cnt) {
     __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void flag_error(uint32_t* err, uint32_t bits) {
     __hip_atomic_fetch_or(err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void store_task(DrawTask* p, const DrawTask& t) {
+    st_coherent(&p->kind, t.kind);
+    st_coherent(&p->row, t.row);
+    st_coherent(&p->drow, t.drow);
+    st_coherent(&p->pos, t.pos);
+    st_coherent(&p->v, t.v);
+    st_coherent(&p->m, t.m);
+    st_coherent(&p->z32, t.z32);
+}
+__device__ __forceinline__ DrawTask load_task(const DrawTask* p) {
+    DrawTask t;
+    t.kind = ld_coherent(&p->kind);
+    t.row = ld_coherent(&p->row);
+    t.drow = ld_coherent(&p->drow);
+    t.pos = ld_coherent(&p->pos);
+    t.v = ld_coherent(&p->v);
+    t.m = ld_coherent(&p->m);
+    t.z32 = ld_coherent(&p->z32);
+    return t;
+}
 
 // ----------------------------------------------------------------- fp64 exp2
-// 2^(j/64) for j = 0..63, each the double nearest the exact value (computed with
-// 50-digit decimal arithmetic).
-__constant__ double kExp2Table[64] = {
-    1.0, 1.0108892860517005, 1.0218971486541166, 1.0330248790212284,
-    1.0442737824274138, 1.0556451783605572, 1.0671404006768237, 1.0787607977571199,
-    1.0905077326652577, 1.102382583307841, 1.1143867425958924, 1.1265216186082418,
-    1.1387886347566916, 1.1511892299529827, 1.1637248587775775, 1.1763969916502812,
-    1.189207115002721, 1.202156731452703, 1.215247359980469, 1.22848053610687,
-    1.241857812073484, 1.255380757024691, 1.2690509571917332, 1.2828700160787783,
-    1.2968395546510096, 1.3109612115247644, 1.3252366431597413, 1.339667524053303,
-    1.3542555469368927, 1.3690024229745905, 1.383909881963832, 1.3989796725383112,
-    1.4142135623730951, 1.42961333839197, 1.4451808069770467, 1.460917794180647,
-    1.4768261459394993, 1.4929077282912648, 1.5091644275934228, 1.5255981507445384,
-    1.5422108254079407, 1.559004400237837, 1.5759808451078865, 1.593142151342267,
-    1.6104903319492543, 1.6280274218573478, 1.645755478153965, 1.6636765803267364,
-    1.681792830507429, 1.7001063537185235, 1.718619298122478, 1.7373338352737062,
-    1.7562521603732995, 1.7753764925265212, 1.7947090750031072, 1.8142521755003989,
-    1.8340080864093424, 1.8539791250833855, 1.8741676341103, 1.8945759815869656,
-    1.9152065613971474, 1.9360617934922943, 1.9571441241754002, 1.978456026387951,
-};
+// kExp2Table[j] = 2^(j/256), j = 0..255 (generated by gen_exp2_table.py).
+#include "sv_exp2_table.h"
+constexpr int kExp2TableSize = 256;
+// Adding 1.5 * 2^52 to a double of magnitude below 2^51 rounds it to an integer
+// (to nearest, ties to even) that then sits in the low bits of the mantissa.
+constexpr double kRoundMagic = 6755399441055744.0;
 
-// 2^y for y <= 0 (y = -inf allowed), relative error about 3e-16: y = k/64 + r
-// with |r| <= 1/128 exactly, 2^r by its Taylor series in r*ln2 to degree 5
-// (truncation below 4e-17), 2^(j/64) from the table (kept in LDS by the
-// caller), and the power of two by ldexp.  y is clamped at -1080 first, whose
-// power of two is below the smallest double, so such results (and NaN inputs)
-// are 0.
-__device__ __forceinline__ double exp2_nonpos(double y, const double* tab) {
-    y = fmax(y, -1080.0);
-    const double kf = rint(y * 64.0);
-    const double r = fma(kf, -0.015625, y);
-    double p = fma(r, 0.0013333558146428443, 0.009618129107628477);
-    p = fma(r, p, 0.05550410866482158);
-    p = fma(r, p, 0.24022650695910072);
-    p = fma(r, p, 0.6931471805599453);
+// 2^(s/256) for s <= 0 (s = -inf allowed), relative error about 2e-16: s = k + r
+// with |r| <= 1/2 exactly (k rounded by the magic addition, whose low word is k
+// itself), 2^(r/256) by its Taylor series in r*ln2/256 to degree 4 (truncation
+// below 4e-17; the coefficients are (ln2)^i / i! scaled by 2^(-8i), exactly),
+// 2^((k mod 256)/256) from the table (kept in LDS by the caller) and 2^(k div 256)
+// by ldexp.  s is clamped at -276480 = 256 * -1080 first, whose power of two is
+// below the smallest double, so such results (and NaN inputs) are 0.  Taking s
+// already scaled by 256 (folded into the caller's coefficients, exactly) keeps
+// the rounding to one add.
+__device__ __forceinline__ double exp2_256(double s, const double* tab) {
+    s = fmax(s, -276480.0);
+    const double t = s + kRoundMagic;
+    const int k = __double2loint(t);
+    const double r = s - (t - kRoundMagic);
+    double p = fma(r, 2.239395190875157e-12, 3.3083026805413713e-09);
+    p = fma(r, p, 3.665565596910106e-06);
+    p = fma(r, p, 0.0027076061740622863);
     p = fma(r, p, 1.0);
-    const int k = static_cast<int>(kf);
-    return ldexp(tab[k & 63] * p, k >> 6);
+    return ldexp(tab[k & (kExp2TableSize - 1)] * p, k >> 8);
 }
 
 // ----------------------------------------------------------------- reductions
@@ -738,7 +757,10 @@ __device__ __forceinline__ void row_merge(const Params& P, int t, int npieces, R
         int tok = -1;
         if (tid < k) tok = xj;
         else if (tid == k && greedy) tok = ld_coherent(&P.rows[t0 + k].g);
-        P.out_tokens[(size_t)b * (G + 1) + tid] = tok;
+        // in a one-launch step the drawn token is stored by the select of the
+        // same launch, possibly on another XCD: a store here as well could land
+        // after it when the L2s write back, so that slot is left to the select
+        if (!(P.task_tag && tid == k && !greedy)) P.out_tokens[(size_t)b * (G + 1) + tid] = tok;
     }
     __syncthreads();
     if (tid == 0) {
@@ -751,7 +773,12 @@ __device__ __forceinline__ void row_merge(const Params& P, int t, int npieces, R
         tk.v = greedy ? 0.0f : P.uniforms[(size_t)b * (G + 2) + (k < gb ? G : G + 1)];
         tk.m = sh.mk;
         tk.z32 = sh.zk;
-        P.tasks[b] = tk;
+        store_task(&P.tasks[b], tk);
+        reset_counter(&P.req_cnt[b]);        // every row of b has arrived: ready for the next call
+        if (P.task_tag) {
+            wait_stores();                   // the task is complete before its tag
+            st_coherent(&P.task_tag[b], P.epoch);
+        }
     }
 }
 
@@ -782,9 +809,10 @@ __device__ __forceinline__ int range_owner(long v, long nv, int g) {
 
 // Aligned rows kernel: the flattened [rows x vectors-per-row] stream is cut into
 // gridDim.x equal contiguous ranges; a range covers pieces of one or more rows.
+// Aligned rows: the flattened [rows x vectors-per-row] stream is cut into
+// gridDim.x equal contiguous ranges; a range covers pieces of one or more rows.
 template <typename E>
-__global__ __launch_bounds__(kThreads) void rows_flat_kernel(Params P) {
-    __shared__ RowShared sh;
+__device__ __forceinline__ void rows_flat_range(const Params& P, RowShared& sh) {
     const int w = blockIdx.x;
     const int G = gridDim.x;
     const long NV = P.flat_nv, VPR = P.flat_vpr;
@@ -818,6 +846,12 @@ __global__ __launch_bounds__(kThreads) void rows_flat_kernel(Params P) {
     }
 }
 
+template <typename E>
+__global__ __launch_bounds__(kThreads) void rows_flat_kernel(Params P) {
+    __shared__ RowShared sh;
+    rows_flat_range<E>(P, sh);
+}
+
 // ----------------------------------------------------------------- draw blocks
 // Everything a wave needs to work on one request's draw row.
 template <typename E>
@@ -826,8 +860,8 @@ struct DrawRow {
     int pos;             // output column
     float v;             // uniform of the draw
     double m;            // row max (raw logits)
-    double c2;           // log2(e) / T
-    double mc2;          // m * c2
+    double c2;           // 256 log2(e) / T
+    double mc2;          // m * c2 (both exactly 256 times their unscaled roundings)
     double z32;          // normaliser from the fp32-exponential pass
     const typename E::T* lrow;
     const float* qrow;   // residual: q row, else nullptr
@@ -837,7 +871,7 @@ struct DrawRow {
 // e = exp((l - m) / T) of one token, in fp64 (the same expression everywhere).
 template <typename E>
 __device__ __forceinline__ double draw_e(const DrawRow<E>& d, float l, const double* tab) {
-    return exp2_nonpos(fma(static_cast<double>(l), d.c2, -d.mc2), tab);
+    return exp2_256(fma(static_cast<double>(l), d.c2, -d.mc2), tab);
 }
 
 // One lane's 8 tokens of one sub-block as loaded (raw element bits), and its
@@ -851,19 +885,6 @@ template <typename E>
 struct RawBlock {
     RawSub<E> s[kSubBlocks];
 };
-
-// Vector loads of this lane's tokens [x0, x0 + 8) of 16-byte aligned rows.
-template <typename E, bool kWithQ>
-__device__ __forceinline__ void issue_sub_fast(const DrawRow<E>& d, long x0, RawSub<E>& r) {
-    const v4u* lp = reinterpret_cast<const v4u*>(d.lrow + x0);
-#pragma unroll
-    for (int h = 0; h < kSubTokens / E::kPerVec; ++h) r.l[h] = __builtin_nontemporal_load(lp + h);
-    if (kWithQ) {
-        const v4u* qp = reinterpret_cast<const v4u*>(d.qrow + x0);
-#pragma unroll
-        for (int h = 0; h < kSubTokens / 4; ++h) r.q[h] = __builtin_nontemporal_load(qp + h);
-    }
-}
 
 // Loads of this lane's tokens [x0, x0 + 8) of any row: vectors where the row
 // allows, else element by element (logits past V read as -inf, q as 0).
@@ -911,11 +932,6 @@ __device__ __forceinline__ long sub_first(long xb, int u) {
     return xb + u * kSubElems + (threadIdx.x & 63) * kSubTokens;
 }
 
-template <typename E, bool kWithQ>
-__device__ __forceinline__ void issue_block_fast(const DrawRow<E>& d, long xb, RawBlock<E>& r) {
-#pragma unroll
-    for (int u = 0; u < kSubBlocks; ++u) issue_sub_fast<E, kWithQ>(d, sub_first(xb, u), r.s[u]);
-}
 template <typename E>
 __device__ __forceinline__ void issue_block_any(const DrawRow<E>& d, long xb, int V, bool with_q, RawBlock<E>& r) {
 #pragma unroll
@@ -931,6 +947,20 @@ __device__ __forceinline__ void decode_sub(const RawSub<E>& r, bool with_q, floa
         if (with_q) F32::decode(r.q[h], q + 4 * h);
         else q[4 * h] = q[4 * h + 1] = q[4 * h + 2] = q[4 * h + 3] = 0.0f;
     }
+}
+
+// Token k (0..7) of a lane's loaded sub-block, decoded on its own: logit and q.
+template <typename E>
+__device__ __forceinline__ float sub_logit(const RawSub<E>& r, int k) {
+    if (E::kBits == 16) {
+        const uint32_t w = r.l[0][k >> 1];
+        return __uint_as_float((k & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+    return __uint_as_float(r.l[k >> 2][k & 3]);
+}
+template <typename E>
+__device__ __forceinline__ float sub_q(const RawSub<E>& r, int k) {
+    return __uint_as_float(r.q[k >> 2][k & 3]);
 }
 
 // Rare path of block_record: stores the block's first kMarginSlots marginal
@@ -957,7 +987,7 @@ __device__ __noinline__ void record_marginal(const typename E::T* lrow, const fl
                     st_coherent(&rec->mx[slot], static_cast<int>(x));
                     st_coherent(&rec->mq[slot], qrow[x]);
                     st_coherent(&rec->me[slot],
-                                exp2_nonpos(fma(static_cast<double>(E::load1(lrow, x)), c2, -mc2), tab));
+                                exp2_256(fma(static_cast<double>(E::load1(lrow, x)), c2, -mc2), tab));
                 }
                 ++slot;
             }
@@ -965,46 +995,80 @@ __device__ __noinline__ void record_marginal(const typename E::T* lrow, const fl
     }
 }
 
-// Sums of one loaded block, written to its record with device-scope stores.
-// Residual rows split the tokens three ways with the fp32-pass normaliser:
-// clearly positive residual (e / Z32 * (1 - margin) > q: summed into ea and qa),
-// clearly non-positive (e / Z32 * (1 + margin) < q: dropped) and marginal (the
-// rest: counted, the first kMarginSlots in token order kept inline).  Branch-
-// free except for the marginal capture, which only runs when the wave has a
-// marginal token.  Wave-uniform call.
+// Block sums: residual rows split the tokens three ways with the fp32-pass
+// normaliser: clearly positive residual (e / Z32 * (1 - margin) > q: summed
+// into ea and qa), clearly non-positive (e / Z32 * (1 + margin) <= q: dropped)
+// and marginal (the rest: counted, the first kMarginSlots in token order kept
+// inline).  Branch-free except for the marginal capture, which only runs when
+// the wave has a marginal token.
+struct BlockSums {
+    double se = -0.0, ea = -0.0, qa = -0.0;   // -0.0 + x is x: the first adds fold away
+    uint32_t mmask = 0u;                      // bit 8u + k: token k of sub-block u is marginal
+};
+
+// Adds one lane's 8 decoded tokens of sub-block u, two at a time.
 template <typename E, bool kResidual>
-__device__ __forceinline__ void block_record(const DrawRow<E>& d, const RawBlock<E>& r, long xb, double apos,
-                                             double aneg, const double* tab, BlockRec* rec) {
-    const int lane = threadIdx.x & 63;
-    double se = 0.0, ea = 0.0, qa = 0.0;
-    uint32_t mmask = 0u;                 // bit 8u + k: token k of sub-block u is marginal
-#pragma unroll
-    for (int u = 0; u < kSubBlocks; ++u) {
-        float l[kSubTokens], q[kSubTokens];
-        decode_sub<E>(r.s[u], kResidual, l, q);
-#pragma unroll
-        for (int k = 0; k < kSubTokens; ++k) {
-            const double e = draw_e<E>(d, l[k], tab);
-            se += e;
-            if (kResidual) {
-                const double qd = static_cast<double>(q[k]);
-                const bool pos = e * apos > qd;
-                const bool neg = e * aneg < qd;
-                ea += pos ? e : 0.0;
-                qa += pos ? qd : 0.0;
-                mmask |= static_cast<uint32_t>(!pos && !neg && e > 0.0) << (u * kSubTokens + k);
-            }
-            // two tokens' fp64 chains at a time: enough ILP next to the other
-            // waves of the SIMD, and few registers
-            if (k & 1) __builtin_amdgcn_sched_barrier(0);
-        }
+__device__ __forceinline__ void accumulate_token(const DrawRow<E>& d, float l, float q, int bit, double apos,
+                                                 double aneg, const double* tab, BlockSums& b) {
+    const double e = draw_e<E>(d, l, tab);
+    b.se += e;
+    if (kResidual) {
+        const double qd = static_cast<double>(q);
+        const bool pos = e * apos > qd;
+        const bool marg = !pos && e * aneg > qd;
+        const double wpos = pos ? 1.0 : 0.0;
+        b.ea = fma(e, wpos, b.ea);
+        b.qa = fma(qd, wpos, b.qa);
+        b.mmask |= static_cast<uint32_t>(marg) << bit;
     }
-    se = wave_sum(se);
+}
+
+template <typename E, bool kResidual>
+__device__ __forceinline__ void accumulate_sub(const DrawRow<E>& d, const float* l, const float* q, int u, double apos,
+                                               double aneg, const double* tab, BlockSums& b) {
+#pragma unroll
+    for (int k = 0; k < kSubTokens; k += 2) {
+        float la = l[k], lb = l[k + 1];
+        // each pair starts once the previous pair is summed: the unrolled
+        // chains would otherwise be interleaved before scheduling, with every
+        // token's temporaries live at once
+        if (k > 0) asm volatile("" : "+v"(la), "+v"(lb) : "v"(b.se));
+        accumulate_token<E, kResidual>(d, la, q[k], u * kSubTokens + k, apos, aneg, tab, b);
+        accumulate_token<E, kResidual>(d, lb, q[k + 1], u * kSubTokens + k + 1, apos, aneg, tab, b);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The same sums taken straight from a loaded sub-block, two tokens at a time,
+// with no decoded copy of the sub-block held in registers.
+template <typename E, bool kResidual>
+__device__ __forceinline__ void accumulate_raw(const DrawRow<E>& d, const RawSub<E>& r, int u, double apos,
+                                               double aneg, const double* tab, BlockSums& b) {
+#pragma unroll
+    for (int k = 0; k < kSubTokens; k += 2) {
+        float la = sub_logit<E>(r, k), lb = sub_logit<E>(r, k + 1);
+        if (k > 0) asm volatile("" : "+v"(la), "+v"(lb) : "v"(b.se));
+        accumulate_token<E, kResidual>(d, la, kResidual ? sub_q<E>(r, k) : 0.0f, u * kSubTokens + k, apos, aneg,
+                                       tab, b);
+        accumulate_token<E, kResidual>(d, lb, kResidual ? sub_q<E>(r, k + 1) : 0.0f, u * kSubTokens + k + 1, apos,
+                                       aneg, tab, b);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Wave totals of a block's sums, written to its record with device-scope
+// stores (plus the inline marginal tokens).  Wave-uniform call.
+template <typename E, bool kResidual>
+__device__ __forceinline__ void store_record(const DrawRow<E>& d, long xb, BlockSums b, const double* tab,
+                                             BlockRec* rec) {
+    const int lane = threadIdx.x & 63;
+    const double se = wave_sum(b.se);
+    double ea = 0.0, qa = 0.0;
     int nmw = 0;
     if (kResidual) {
-        ea = wave_sum(ea);
-        qa = wave_sum(qa);
-        if (__ballot(mmask != 0u) != 0ull) nmw = wave_sum_int(__popc(mmask));
+        ea = wave_sum(b.ea);
+        qa = wave_sum(b.qa);
+        if (__ballot(b.mmask != 0u) != 0ull) nmw = wave_sum_int(__popc(b.mmask));
     }
     if (lane == 0) {
         st_coherent(&rec->se, se);
@@ -1012,33 +1076,180 @@ __device__ __forceinline__ void block_record(const DrawRow<E>& d, const RawBlock
         st_coherent(&rec->qa, qa);
         st_coherent(&rec->nm, nmw);
     }
-    if (kResidual && nmw > 0 && nmw <= kMarginSlots) record_marginal<E>(d.lrow, d.qrow, d.c2, d.mc2, xb, mmask, tab, rec);
+    if (kResidual && nmw > 0 && nmw <= kMarginSlots)
+        record_marginal<E>(d.lrow, d.qrow, d.c2, d.mc2, xb, b.mmask, tab, rec);
 }
 
-// Per-block sums of draw blocks jfirst + wave, + jstride, ... < jend, written to
-// recs; one block (all of its loads in flight together) per wave at a time.
+// Sums of one loaded block (any row layout).
 template <typename E, bool kResidual>
+__device__ __forceinline__ void block_record(const DrawRow<E>& d, const RawBlock<E>& r, long xb, double apos,
+                                             double aneg, const double* tab, BlockRec* rec) {
+    BlockSums b;
+#pragma unroll
+    for (int u = 0; u < kSubBlocks; ++u) {
+        float l[kSubTokens], q[kSubTokens];
+        decode_sub<E>(r.s[u], kResidual, l, q);
+        accumulate_sub<E, kResidual>(d, l, q, u, apos, aneg, tab, b);
+    }
+    store_record<E, kResidual>(d, xb, b, tab, rec);
+}
+
+// Loads of this lane's tokens [x0, x0 + 8) of a block lying wholly inside a
+// 16-byte aligned row (and q row): plain vector loads.
+template <typename E, bool kWithQ>
+__device__ __forceinline__ void issue_sub_full(const DrawRow<E>& d, int x0, RawSub<E>& r) {
+    const v4u* lp = reinterpret_cast<const v4u*>(d.lrow + x0);
+#pragma unroll
+    for (int h = 0; h < kSubTokens / E::kPerVec; ++h) r.l[h] = __builtin_nontemporal_load(lp + h);
+    if (kWithQ) {
+        const v4u* qp = reinterpret_cast<const v4u*>(d.qrow + x0);
+#pragma unroll
+        for (int h = 0; h < kSubTokens / 4; ++h) r.q[h] = __builtin_nontemporal_load(qp + h);
+    }
+}
+
+// This lane's first token of sub-block u of the block starting at xb (32-bit:
+// rows hold at most 2^19 tokens).
+__device__ __forceinline__ int sub_first32(int xb, int u) {
+    return xb + u * kSubElems + (threadIdx.x & 63) * kSubTokens;
+}
+
+// Sums of one block of a whole-vector row whose loads are in r; once a
+// sub-block's tokens are summed, its registers are refilled with that sub-block
+// of block xn (kRefill), so the wave keeps about a block's loads in flight.
+// No calls: a call would leave the compiler unable to wait for one refill
+// while the later ones stay in flight.
+template <typename E, bool kResidual, bool kRefill>
+__device__ __forceinline__ BlockSums block_stream(const DrawRow<E>& d, RawBlock<E>& r, int xb, int xn, int V,
+                                                  double apos, double aneg, const double* tab) {
+    BlockSums b;
+#pragma unroll
+    for (int u = 0; u < kSubBlocks; ++u) {
+        accumulate_raw<E, kResidual>(d, r.s[u], u, apos, aneg, tab, b);
+        if (kRefill) issue_sub_full<E, kResidual>(d, sub_first32(xn, u), r.s[u]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    return b;
+}
+
+// Wave totals of one streamed block, stored to its record; a block with inline
+// marginal tokens is remembered (at most two per stream; further ones are left
+// for the select to re-evaluate from their tokens) and captured after the
+// stream has ended.
+struct StreamCaps {
+    int n = 0;                    // wave-uniform
+    int j0 = 0, j1 = 0;           // blocks to capture
+    uint32_t m0 = 0u, m1 = 0u;    // their marginal masks (per lane)
+};
+
+template <bool kResidual>
+__device__ __forceinline__ void stream_finish(const BlockSums& b, int j, BlockRec* recs, StreamCaps& c) {
+    const int lane = threadIdx.x & 63;
+    const double se = wave_sum(b.se);
+    double ea = 0.0, qa = 0.0;
+    int nm = 0;
+    if (kResidual) {
+        ea = wave_sum(b.ea);
+        qa = wave_sum(b.qa);
+        if (__ballot(b.mmask != 0u) != 0ull) nm = wave_sum_int(__popc(b.mmask));
+    }
+    if (kResidual && nm > 0 && nm <= kMarginSlots) {
+        // selects rather than branches, so the fields stay in registers
+        const bool first = (c.n == 0), second = (c.n == 1);
+        c.j0 = first ? j : c.j0;
+        c.m0 = first ? b.mmask : c.m0;
+        c.j1 = second ? j : c.j1;
+        c.m1 = second ? b.mmask : c.m1;
+        if (c.n >= 2) nm = kMarginSlots + 1;
+        c.n = min(c.n + 1, 2);
+    }
+    if (lane == 0) {
+        BlockRec* rec = &recs[j];
+        st_coherent(&rec->se, se);
+        st_coherent(&rec->ea, ea);
+        st_coherent(&rec->qa, qa);
+        st_coherent(&rec->nm, nm);
+    }
+}
+
+// Blocks jfirst and, if n == 2, jfirst + jstride of a whole-vector row, all of
+// their loads issued before the first is summed.  Straight-line code: with a
+// loop around it the compiler's allocation spills.
+template <typename E, bool kResidual>
+__device__ __forceinline__ void draw_blocks_upto2(const DrawRow<E>& d, int V, BlockRec* recs, int j, int jstride,
+                                                  int n, double apos, double aneg, const double* tab,
+                                                  StreamCaps& c) {
+    RawBlock<E> r;
+#pragma unroll
+    for (int u = 0; u < kSubBlocks; ++u) issue_sub_full<E, kResidual>(d, sub_first32(j * kBlockElems, u), r.s[u]);
+    if (n >= 2) {
+        const int j2 = j + jstride;
+        const BlockSums b1 = block_stream<E, kResidual, true>(d, r, j * kBlockElems, j2 * kBlockElems, V, apos, aneg,
+                                                             tab);
+        stream_finish<kResidual>(b1, j, recs, c);
+        const BlockSums b2 = block_stream<E, kResidual, false>(d, r, j2 * kBlockElems, 0, V, apos, aneg, tab);
+        stream_finish<kResidual>(b2, j2, recs, c);
+    } else {
+        const BlockSums b = block_stream<E, kResidual, false>(d, r, j * kBlockElems, 0, V, apos, aneg, tab);
+        stream_finish<kResidual>(b, j, recs, c);
+    }
+}
+
+template <typename E, bool kResidual>
+__device__ __forceinline__ void capture_marginals(const DrawRow<E>& d, BlockRec* recs, const StreamCaps& c,
+                                                  const double* tab) {
+    if (kResidual && c.n > 0)
+        record_marginal<E>(d.lrow, d.qrow, d.c2, d.mc2, (long)c.j0 * kBlockElems, c.m0, tab, &recs[c.j0]);
+    if (kResidual && c.n > 1)
+        record_marginal<E>(d.lrow, d.qrow, d.c2, d.mc2, (long)c.j1 * kBlockElems, c.m1, tab, &recs[c.j1]);
+}
+
+// Per-block sums of draw blocks jfirst, jfirst + jstride, ... < jend, written to
+// recs.  In 16-byte aligned rows, blocks lying wholly inside the row are taken
+// two at a time with all of their loads in flight together (kUpTo2: the caller
+// guarantees at most two blocks, and no loop is generated around them); the
+// row's ragged last block, and every block of other rows, is taken on its own.
+template <typename E, bool kResidual, bool kUpTo2>
 __device__ __forceinline__ void draw_blocks_kind(const DrawRow<E>& d, int V, BlockRec* recs, int jfirst, int jstride,
                                                  int jend, const double* tab) {
-    const int wv = threadIdx.x >> 6;
     const double invZ32 = 1.0 / d.z32;
     const double apos = invZ32 * (1.0 - kSignMargin), aneg = invZ32 * (1.0 + kSignMargin);
     const bool fastrow = d.lalign && (!kResidual || d.qalign);
-    const int jfull = V / kBlockElems;                  // blocks entirely inside the row
-    for (int j = jfirst + wv; j < jend; j += jstride) {
+    int jany = jfirst;                             // first block taken on its own
+    if (fastrow) {
+        const int jfull = V / kBlockElems;         // blocks wholly inside the row
+        const int jend_full = jend < jfull ? jend : jfull;
+        StreamCaps c;
+        int j = jfirst;
+        if (kUpTo2) {
+            if (j < jend_full) {
+                const int n = j + jstride < jend_full ? 2 : 1;
+                draw_blocks_upto2<E, kResidual>(d, V, recs, j, jstride, n, apos, aneg, tab, c);
+                j += n * jstride;
+            }
+        } else {
+            while (j < jend_full) {
+                const int n = j + jstride < jend_full ? 2 : 1;
+                draw_blocks_upto2<E, kResidual>(d, V, recs, j, jstride, n, apos, aneg, tab, c);
+                j += n * jstride;
+            }
+        }
+        capture_marginals<E, kResidual>(d, recs, c, tab);
+        jany = j;
+    }
+    for (int j = jany; j < jend; j += jstride) {
         RawBlock<E> r;
         const long xb = (long)j * kBlockElems;
-        if (fastrow && j < jfull) issue_block_fast<E, kResidual>(d, xb, r);
-        else issue_block_any<E>(d, xb, V, kResidual, r);
+        issue_block_any<E>(d, xb, V, kResidual, r);
         block_record<E, kResidual>(d, r, xb, apos, aneg, tab, &recs[j]);
     }
 }
 
-template <typename E>
+template <typename E, bool kUpTo2 = false>
 __device__ __forceinline__ void draw_blocks(const DrawRow<E>& d, int V, BlockRec* recs, int jfirst, int jstride, int jend,
                             const double* tab) {
-    if (d.kind == kDrawResidual) draw_blocks_kind<E, true>(d, V, recs, jfirst, jstride, jend, tab);
-    else draw_blocks_kind<E, false>(d, V, recs, jfirst, jstride, jend, tab);
+    if (d.kind == kDrawResidual) draw_blocks_kind<E, true, kUpTo2>(d, V, recs, jfirst, jstride, jend, tab);
+    else draw_blocks_kind<E, false, kUpTo2>(d, V, recs, jfirst, jstride, jend, tab);
 }
 
 // Select for one request once all its draw blocks are recorded, by one wave
@@ -1234,7 +1445,7 @@ __device__ __forceinline__ void init_draw_row(DrawRow<E>& d, const Params& P, in
     d.pos = pos;
     d.v = v;
     d.m = static_cast<double>(m);
-    d.c2 = kLog2e / static_cast<double>(T);
+    d.c2 = 256.0 * (kLog2e / static_cast<double>(T));
     d.mc2 = d.m * d.c2;
     d.z32 = z32;
     d.lrow = static_cast<const typename E::T*>(P.logits) + (size_t)row * P.vocab;
@@ -1244,7 +1455,7 @@ __device__ __forceinline__ void init_draw_row(DrawRow<E>& d, const Params& P, in
 }
 
 struct DrawShared {
-    double tab[64];
+    double tab[kExp2TableSize];
     int flag;
 };
 
@@ -1258,19 +1469,19 @@ __global__ __launch_bounds__(kThreads, 4) void draw_kernel(Params P) {
     const int c = blockIdx.x - b * C;
     const int NB = P.nblocks;
 
-    if (c == 0 && tid == 0) reset_counter(&P.req_cnt[b]);     // ready for the next call
     const DrawTask tk = P.tasks[b];
     if (tk.kind == kDrawNone) return;
     const bool residual = (tk.kind == kDrawResidual);
     if (tk.row < 0 || tk.row >= P.total_draft + P.batch || tk.pos < 0 || tk.pos > P.gamma ||
         (residual && (tk.drow < 0 || tk.drow >= P.total_draft)))
         return;                                    // only reachable with inconsistent offsets
-    if (tid < 64) sh.tab[tid] = kExp2Table[tid];
+    for (int j = tid; j < kExp2TableSize; j += kThreads) sh.tab[j] = kExp2Table[j];
     DrawRow<E> d;
     init_draw_row<E>(d, P, tk.kind, tk.row, tk.drow, tk.pos, tk.v, tk.m, tk.z32, P.temperature[b]);
     __syncthreads();
     BlockRec* recs = P.recs + (size_t)b * NB;
-    draw_blocks<E>(d, P.vocab, recs, c * kWaves, C * kWaves, NB, sh.tab);
+    // the grid gives every wave at most two blocks (checked by the host)
+    draw_blocks<E, true>(d, P.vocab, recs, c * kWaves + (tid >> 6), C * kWaves, NB, sh.tab);
     wait_stores();                 // every wave's record stores complete before the arrival
     __syncthreads();
     if (tid == 0) sh.flag = (arrive(&P.draw_cnt[b]) == static_cast<uint32_t>(C - 1));
@@ -1282,6 +1493,83 @@ __global__ __launch_bounds__(kThreads, 4) void draw_kernel(Params P) {
         P.out_tokens[(size_t)b * (P.gamma + 1) + tk.pos] = y;
         P.tasks[b].kind = kDrawNone;               // consumed: a stale task is never replayed
     }
+}
+
+// ----------------------------------------------------------------- one-launch step
+// One launch of at most as many workgroups as the device holds at once (so all
+// of them are resident together on an otherwise idle device; every wait below
+// is bounded, and an expired wait is reported as a stall): every workgroup first streams
+// its range of the flattened rows exactly as the flat rows kernel does (merges
+// and resolves included; a resolve publishes its request's draw task with this
+// call's epoch), then its waves work through its share of the call's draw
+// blocks (request-major), each wave on its own: a wave waits only for the task
+// of the request whose blocks it holds, so draws of early requests overlap the
+// streaming of late ones.  The wave that lands a request's last block record
+// runs that request's select.
+constexpr int kPhaseSpinLimit = 1 << 20;   // bounded wait for a draw task (seconds)
+
+// Lane 0 waits until request b's task carries this call's epoch.  Gives up when
+// a row was rejected for inconsistent offsets (its request never resolves;
+// looked at every 16th poll) or when the wait limit expires (flagged as a
+// stall).  Polls are spaced out so that waiting waves add little traffic next
+// to the merges they wait for.
+__device__ __forceinline__ bool wait_task(const Params& P, int b) {
+    int ok = 1;
+    if ((threadIdx.x & 63) == 0) {
+        int spins = 0;
+        while (ld_coherent(&P.task_tag[b]) != P.epoch) {
+            if ((spins & 15) == 15 && (ld_coherent(P.err) & kErrOffsets) != 0u) { ok = 0; break; }
+            if (++spins >= kPhaseSpinLimit) { flag_error(P.err, kErrStalled); ok = 0; break; }
+            __builtin_amdgcn_s_sleep(8);
+        }
+    }
+    return __builtin_amdgcn_readfirstlane(ok) != 0;
+}
+
+// This wave's draw blocks: blocks g = first, first + kWaves, ... of the call's
+// request-major block list that fall in the workgroup's range [gridDim.x-th share).
+template <typename E>
+__device__ __forceinline__ void draw_phase(const Params& P, const double* tab) {
+    const int lane = threadIdx.x & 63;
+    const int NB = P.nblocks;
+    const long DB = (long)P.batch * NB;
+    const long g1 = (long)(blockIdx.x + 1) * DB / gridDim.x;
+    long g = (long)blockIdx.x * DB / gridDim.x + (threadIdx.x >> 6);
+    while (g < g1) {
+        const int b = static_cast<int>(g / NB);
+        const long gb0 = (long)b * NB;
+        const long gend = g1 < gb0 + NB ? g1 : gb0 + NB;
+        const int j0 = static_cast<int>(g - gb0), j1 = static_cast<int>(gend - gb0);
+        const int n = (j1 - j0 + kWaves - 1) / kWaves;          // this wave's blocks of request b
+        g += (long)n * kWaves;
+        if (!wait_task(P, b)) continue;
+        const DrawTask tk = load_task(&P.tasks[b]);
+        const bool residual = (tk.kind == kDrawResidual);
+        if (tk.kind == kDrawNone || tk.row < 0 || tk.row >= P.total_draft + P.batch || tk.pos < 0 ||
+            tk.pos > P.gamma || (residual && (tk.drow < 0 || tk.drow >= P.total_draft)))
+            continue;
+        DrawRow<E> d;
+        init_draw_row<E>(d, P, tk.kind, tk.row, tk.drow, tk.pos, tk.v, tk.m, tk.z32, P.temperature[b]);
+        BlockRec* recs = P.recs + (size_t)b * NB;
+        draw_blocks<E>(d, P.vocab, recs, j0, kWaves, j1, tab);
+        uint32_t old = 0;
+        if (lane == 0) old = arrive_n(&P.draw_cnt[b], static_cast<uint32_t>(n));
+        old = __builtin_amdgcn_readfirstlane(old);
+        if (old + static_cast<uint32_t>(n) != static_cast<uint32_t>(NB)) continue;
+        if (lane == 0) reset_counter(&P.draw_cnt[b]);
+        const int y = draw_select_wave<E>(d, P.vocab, NB, recs, tab, P.err);
+        if (lane == 0) P.out_tokens[(size_t)b * (P.gamma + 1) + tk.pos] = y;
+    }
+}
+
+template <typename E>
+__global__ __launch_bounds__(kThreads, 3) void step_kernel(Params P) {
+    __shared__ RowShared sh;
+    __shared__ double tab[kExp2TableSize];
+    for (int j = threadIdx.x; j < kExp2TableSize; j += kThreads) tab[j] = kExp2Table[j];
+    rows_flat_range<E>(P, sh);
+    __syncthreads();
+    draw_phase<E>(P, tab);
 }
 
 }  // namespace sv

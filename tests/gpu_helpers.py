@@ -52,17 +52,19 @@ def upload_inputs(inp, device="cuda:0", diag=True):
                   gamma=inp.gamma, draft_offsets=inp.offsets, device=device, diag=diag)
 
 
-def make_verifier(inp, max_batch=None, max_gamma=None, profile=False, fused=True):
+def make_verifier(inp, max_batch=None, max_gamma=None, profile=False, schedule=None):
+    """A context for ``inp``; schedule None is the library's choice, else "onelaunch"
+    or "twokernel"."""
     from lossless_rejection_sampling_sampler_amd import SpecVerify
     return SpecVerify(max_batch or inp.batch, inp.gamma if max_gamma is None else max_gamma,
-                      inp.vocab, inp.dtype, device=0, profile=profile, fused=fused)
+                      inp.vocab, inp.dtype, device=0, profile=profile, schedule=schedule)
 
 
-def run_gpu(inp, uniform_sets: Optional[list] = None, sv=None, diag=True, fused=True):
+def run_gpu(inp, uniform_sets: Optional[list] = None, sv=None, diag=True, schedule=None):
     """Run the HIP path; returns (list of (tokens, num_accepted), diag dict)."""
     import torch
     if sv is None:
-        sv = make_verifier(inp, fused=fused)
+        sv = make_verifier(inp, schedule=schedule)
     db = upload_inputs(inp, diag=diag)
     sets = uniform_sets if uniform_sets is not None else [inp.uniforms]
     results = []
@@ -162,12 +164,12 @@ def check_diag(inp, orc, dg) -> List[str]:
     return errs
 
 
-def parity_check(inp, uniform_sets: Optional[list] = None, sv=None, label="", fused=True):
+def parity_check(inp, uniform_sets: Optional[list] = None, sv=None, label="", schedule=None):
     """Run GPU and oracle on ``inp`` (optionally many uniform sets); returns the report."""
     sets = uniform_sets if uniform_sets is not None else [inp.uniforms]
     log(f"[parity] {label} B={inp.batch} gamma={inp.gamma} V={inp.vocab} {inp.dtype} sets={len(sets)} "
-        f"{'fused' if fused else 'two-kernel'}: gpu")
-    res, dg, sv = run_gpu(inp, sets, sv=sv, fused=fused)
+        f"schedule={schedule or 'auto'}: gpu")
+    res, dg, sv = run_gpu(inp, sets, sv=sv, schedule=schedule)
     rep = ParityReport()
     errs = []
     chunk = 16                      # sets per oracle call: a progress line every few seconds

@@ -74,14 +74,18 @@ def test_zero_batch_leaves_outputs_untouched():
     assert torch.all(db.out_tokens == -7) and torch.all(db.out_num_accepted == -7)
 
 
-def test_out_of_range_draft_id_sets_error_word():
+SCHEDULES = ["onelaunch", "twokernel"]
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_out_of_range_draft_id_sets_error_word(schedule):
     import torch
     from lossless_rejection_sampling_sampler_amd._lib import SV_DEVERR_DRAFT_ID
     inp = make_config(2, replicate=1, vocab=1000, batch=4)
     inp.draft_ids[0] = 1000
     inp.draft_ids[6] = -3
-    log("[api] out-of-range draft ids")
-    res, _, sv = run_gpu(inp, diag=False)
+    log(f"[api] out-of-range draft ids, schedule={schedule}")
+    res, _, sv = run_gpu(inp, diag=False, schedule=schedule)
     assert sv.device_errors(clear=True) & SV_DEVERR_DRAFT_ID
     assert sv.device_errors() == 0
     tok, num = res[0]
@@ -89,18 +93,19 @@ def test_out_of_range_draft_id_sets_error_word():
     assert np.all((tok >= -1) & (tok < 1000))
 
 
-def test_bad_offsets_set_error_word_without_faulting():
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_bad_offsets_set_error_word_without_faulting(schedule):
     from lossless_rejection_sampling_sampler_amd._lib import SV_DEVERR_OFFSETS
     inp = make_config(5, replicate=1, vocab=600, batch=8)
     inp.offsets[3] = inp.offsets[4] + 3      # gamma_3 negative, gamma_4 too large
-    log("[api] inconsistent offsets")
-    res, _, sv = run_gpu(inp, diag=False)
+    log(f"[api] inconsistent offsets, schedule={schedule}")
+    res, _, sv = run_gpu(inp, diag=False, schedule=schedule)
     assert sv.device_errors(clear=True) & SV_DEVERR_OFFSETS
     assert sv.device_errors() == 0
     # a following valid call on the same context is exact again
     good = make_config(5, replicate=1, vocab=600, batch=8)
     res2, _, _ = run_gpu(good, sv=sv)
-    res3, _, _ = run_gpu(good)
+    res3, _, _ = run_gpu(good, schedule=schedule)
     assert np.array_equal(res2[0][0], res3[0][0]) and np.array_equal(res2[0][1], res3[0][1])
 
 

@@ -45,18 +45,22 @@ def _aligned(inp) -> bool:
     return inp.vocab * esize % 16 == 0
 
 
-@pytest.mark.parametrize("fused", [True, False], ids=["fused", "twokernel"])
+SCHEDULES = ["onelaunch", "twokernel"]
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
-def test_small_parity(name, kw, fused):
+def test_small_parity(name, kw, schedule):
     kw = dict(kw)
     n = kw.pop("n")
     inp = make_config(n, replicate=7, **kw)
     sets = [inp.uniforms] + [uniforms_from_seed(inp.uniforms.shape, s) for s in range(15)]
-    rep, errs, sv = parity_check(inp, sets, label=name, fused=fused)
+    rep, errs, sv = parity_check(inp, sets, label=name, schedule=schedule)
     _assert_ok(rep, errs)
     from lossless_rejection_sampling_sampler_amd._lib import (SV_SCHEDULE_FLAT, SV_SCHEDULE_ONE_LAUNCH,
                                                               SV_SCHEDULE_SPLIT)
-    want = SV_SCHEDULE_SPLIT if not _aligned(inp) else (SV_SCHEDULE_ONE_LAUNCH if fused else SV_SCHEDULE_FLAT)
+    aligned_want = {"onelaunch": SV_SCHEDULE_ONE_LAUNCH, "twokernel": SV_SCHEDULE_FLAT}[schedule]
+    want = aligned_want if _aligned(inp) else SV_SCHEDULE_SPLIT
     assert sv.last_schedule() == want
 
 
@@ -108,11 +112,12 @@ def test_full_workload_parity(n, nsets):
     _assert_ok(rep, errs, min_requests=20000)
 
 
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("n", [3, 5], ids=["config3", "config5"])
-def test_full_workload_two_kernel_schedule(n):
-    """The two-kernel schedule on the full workloads (fewer uniform sets)."""
-    log(f"[full-2k] config {n} seed={1000 * n}")
+def test_full_workload_each_schedule(n, schedule):
+    """Every schedule on the full workloads (fewer uniform sets)."""
+    log(f"[full-{schedule}] config {n} seed={1000 * n}")
     inp = make_config(n)
     sets = [inp.uniforms] + [uniforms_from_seed(inp.uniforms.shape, 500 + s) for s in range(19)]
-    rep, errs, _ = parity_check(inp, sets, label=f"config{n}-2k", fused=False)
+    rep, errs, _ = parity_check(inp, sets, label=f"config{n}-{schedule}", schedule=schedule)
     _assert_ok(rep, errs)
