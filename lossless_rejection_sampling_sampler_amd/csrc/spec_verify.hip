@@ -19,6 +19,8 @@ namespace {
 constexpr int kRowVecsPerThread = 8;    // target 16-byte vectors per thread per row split
 constexpr int kProfileRing = 2048;      // calls between forced event folds
 constexpr int kDrawBlocksPerWave = 2;   // draw kernel: blocks per wave (the kernel takes at most 2)
+constexpr int kStepSlices = 1;          // one-launch step: request slices
+constexpr int kDrawPerCU = 3;           // draw kernel: workgroups per CU aimed at
 
 struct Geometry {
     int splits;          // split rows kernel: workgroups per row
@@ -57,6 +59,7 @@ struct sv_ctx {
     Geometry geo{};
     int max_rows = 0;
     int resident_flat = 0;     // rows-flat workgroups resident at once on the device
+    int cus = 0;               // compute units of the device
     int resident_step = 0;     // one-launch workgroups resident at once
     uint32_t epoch = 0;        // tag of the one-launch step's draw tasks
     int last_schedule = SV_SCHEDULE_NONE;
@@ -164,7 +167,9 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
             delete ctx;
             return SV_ERR_DEVICE;
         }
-        ctx->resident_flat = std::max(1, cus * std::max(1, per_cu));
+        // at most three rows workgroups per CU: more make each CU's last one finish later
+        ctx->resident_flat = std::max(1, cus * std::min(3, std::max(1, per_cu)));
+        ctx->cus = std::max(1, cus);
 
         int per_bf16 = 0, per_f32 = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_bf16, sv::step_kernel<sv::BF16>, sv::kThreads, 0) ==
@@ -268,10 +273,13 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
     P.vocab = a->vocab;
     P.splits = ctx->geo.splits;
     P.nblocks = ctx->geo.nblocks;
-    // draw workgroups per request: at most kDrawBlocksPerWave blocks per wave,
-    // all of a wave's loads in flight together, and one round of workgroups
-    const int C = std::max(1, (ctx->geo.nblocks + sv::kWaves * kDrawBlocksPerWave - 1) /
-                                  (sv::kWaves * kDrawBlocksPerWave));
+    // draw workgroups per request: three per CU over the call where that keeps
+    // between one and kDrawBlocksPerWave (the most a draw wave takes) blocks per
+    // wave; an even count per CU balances the fp64 work across the SIMDs
+    const int c_min = std::max(1, (ctx->geo.nblocks + sv::kWaves * kDrawBlocksPerWave - 1) /
+                                      (sv::kWaves * kDrawBlocksPerWave));
+    const int c_max = std::max(1, (ctx->geo.nblocks + sv::kWaves - 1) / sv::kWaves);
+    const int C = std::max(c_min, std::min(c_max, kDrawPerCU * ctx->cus / a->batch));
     P.draw_wgs = C;
     P.parts = ctx->parts;
     P.rows = ctx->rows;
@@ -283,6 +291,7 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
     P.err = ctx->err;
     P.task_tag = nullptr;
     P.epoch = 0;
+    P.slices = 1;
 
     const long rows = (long)a->total_draft + a->batch;
     // rows start on 16-byte boundaries: stream the flattened rows in equal ranges
@@ -306,7 +315,19 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
         if (++ctx->epoch == 0) ctx->epoch = 1;
         P.task_tag = ctx->task_tag;
         P.epoch = ctx->epoch;
-        const int grid = flat_workgroups(P.flat_nv, P.flat_vpr, ctx->resident_step);
+        P.slices = std::max(1, std::min(kStepSlices, a->batch));
+        // every slice is split over the whole grid: about one batch of loads per
+        // thread per slice, and no row cut into more than kMaxPieces pieces even
+        // in the smallest slice the offsets allow (a request has at least one row)
+        const long rows_per_req_min = a->draft_offsets ? 1 : (long)a->gamma + 1;
+        const long slice_min_nv = (long)(a->batch / P.slices) * rows_per_req_min * P.flat_vpr;
+        long grid = std::min<long>(ctx->resident_step,
+                                   std::max<long>(1, P.flat_nv / ((long)P.slices * sv::kThreads * sv::kRowUnroll)));
+        while (grid > 1) {
+            const long lmin = slice_min_nv / grid;
+            if (lmin > 0 && (P.flat_vpr + lmin - 1) / lmin + 1 <= sv::kMaxPieces) break;
+            --grid;
+        }
         // an ordinary launch: the grid never exceeds what the device holds at once
         // (a cooperative launch would guarantee it, at a cost of microseconds per call)
         if (cfg.logits_dtype == SV_BF16)

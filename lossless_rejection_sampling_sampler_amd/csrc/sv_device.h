@@ -45,7 +45,7 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));   // one 16-byte load
 constexpr int kThreads = 256;            // 4 waves of 64
 constexpr int kWaves = kThreads / 64;
 constexpr int kRowUnroll = 4;            // 16-byte vectors per thread per batch (two batches in flight)
-constexpr int kMaxPieces = 16;           // partials per row
+constexpr int kMaxPieces = 64;           // partials per row (at most one per merging thread)
 // A draw block is 2048 consecutive tokens of a draw row, worked on by one wave:
 // four sub-blocks of 512 tokens, lane L holding tokens 8L .. 8L+7 of each, so
 // every 16-byte load instruction of the wave reads one contiguous span.
@@ -139,6 +139,7 @@ struct Params {
     // task_tag[b] == epoch (nonzero, new every call)
     uint32_t* task_tag;
     uint32_t epoch;
+    int slices;          // one-launch step: request slices
 };
 
 // ----------------------------------------------------------------- element types
@@ -509,23 +510,32 @@ struct RowShared {
     double zk;
 };
 
-// Per-thread online max / sum over one batch of decoded logits.
+// Per-thread online max and sum over one batch of decoded logits.  The sum is
+// kept against a reference kref, an integer in log2 units, as
+// st = sum 2^(l c - kref): kref moves up (to ceil of the batch max times c)
+// only when the batch max times c passes it by more than kRefSlack, and the sum
+// is then rescaled by an exact power of two.  Terms are at most 2^kRefSlack, and
+// the common path is one fma, one exp2 and one add per logit.  mt is the exact
+// running max.  kRefStart makes the first finite batch set the reference, and
+// turns -inf logits into zero terms.
+constexpr float kRefSlack = 8.0f;
+constexpr float kRefStart = -1e30f;
 template <int N>
-__device__ __forceinline__ void accumulate_batch(const float* f, float c, float& mt, double& st) {
+__device__ __forceinline__ void accumulate_batch(const float* f, float c, float& mt, float& kref, double& st) {
     float bm = f[0];
 #pragma unroll
     for (int k = 1; k < N; ++k) bm = fmaxf(bm, f[k]);
-    if (bm > mt) {
-        if (mt > -INFINITY)
-            st *= exp2((static_cast<double>(mt) - static_cast<double>(bm)) * static_cast<double>(c));
-        mt = bm;
+    mt = fmaxf(mt, bm);
+    const float bmc = bm * c;
+    if (bmc > kref + kRefSlack) {
+        const float knew = ceilf(bmc);
+        st = ldexp(st, static_cast<int>(fmaxf(kref - knew, -2048.0f)));
+        kref = knew;
     }
-    if (mt > -INFINITY) {
-        float acc = 0.0f;
+    float acc = 0.0f;
 #pragma unroll
-        for (int k = 0; k < N; ++k) acc += __builtin_amdgcn_exp2f((f[k] - mt) * c);
-        st += static_cast<double>(acc);
-    }
+    for (int k = 0; k < N; ++k) acc += __builtin_amdgcn_exp2f(fmaf(f[k], c, -kref));
+    st += static_cast<double>(acc);
 }
 
 template <typename E>
@@ -574,7 +584,7 @@ __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0
     int gloc = -1;       // argmax (greedy)
     double zloc = 0.0;   // piece sum (sampled)
     if (!greedy) {
-        float mt = -INFINITY;
+        float mt = -INFINITY, kref = kRefStart;
         double st = 0.0;
         v4u A[kRowUnroll], Bf[kRowUnroll];
         if (n > 0) load_batch<E>(A, vp, first, n);
@@ -585,7 +595,7 @@ __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0
                 float f[EB];
 #pragma unroll
                 for (int u = 0; u < kRowUnroll; ++u) E::decode(A[u], f + u * E::kPerVec);
-                accumulate_batch<EB>(f, c, mt, st);
+                accumulate_batch<EB>(f, c, mt, kref, st);
             }
             if (jb + kRowUnroll >= n) break;
             if (jb + 2 * kRowUnroll < n)
@@ -594,19 +604,19 @@ __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0
                 float f[EB];
 #pragma unroll
                 for (int u = 0; u < kRowUnroll; ++u) E::decode(Bf[u], f + u * E::kPerVec);
-                accumulate_batch<EB>(f, c, mt, st);
+                accumulate_batch<EB>(f, c, mt, kref, st);
             }
         }
         // unaligned head (piece 0) and tail (last piece): at most 7 scalars each
         float fx = -INFINITY;
         if (piece == 0 && tid < head) fx = E::load1(row, tid);
         if (piece == npieces - 1 && tid >= 64 && tid - 64 < tail) fx = E::load1(row, head + nvec * E::kPerVec + (tid - 64));
-        accumulate_batch<1>(&fx, c, mt, st);
+        accumulate_batch<1>(&fx, c, mt, kref, st);
 
         mloc = wg_max(mt, sh.red);
         double zs = 0.0;
         if (mt > -INFINITY)
-            zs = st * exp2((static_cast<double>(mt) - static_cast<double>(mloc)) * static_cast<double>(c));
+            zs = st * exp2(static_cast<double>(kref) - static_cast<double>(mloc) * static_cast<double>(c));
         zloc = wg_sum(zs, sh.red);
     } else {
         float bv = -INFINITY;
@@ -638,6 +648,12 @@ __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0
     // ---- publish the piece
     int old = 0;
     if (tid == 0) {
+        // the launch geometry keeps piece < kMaxPieces for rows laid out as the
+        // offsets promise; inconsistent offsets can break that, and are flagged
+        if (piece >= kMaxPieces || npieces > kMaxPieces) {
+            flag_error(P.err, kErrOffsets);
+            return -1;
+        }
         Piece* pp = &P.parts[(size_t)t * kMaxPieces + piece];
         st_coherent(&pp->m, mloc);
         st_coherent(&pp->g, gloc);
@@ -809,41 +825,55 @@ __device__ __forceinline__ int range_owner(long v, long nv, int g) {
 
 // Aligned rows kernel: the flattened [rows x vectors-per-row] stream is cut into
 // gridDim.x equal contiguous ranges; a range covers pieces of one or more rows.
-// Aligned rows: the flattened [rows x vectors-per-row] stream is cut into
-// gridDim.x equal contiguous ranges; a range covers pieces of one or more rows.
+// A published piece whose arrival count is looked at later, so that the
+// counter's round trip overlaps further work.
+struct PendingMerge {
+    int t = -1, np = 0, old = 0;   // row, its pieces, arrival count before this piece (thread 0)
+};
+
+// Runs row t's merge if the pending piece was its last to arrive.  Uniform call.
 template <typename E>
-__device__ __forceinline__ void rows_flat_range(const Params& P, RowShared& sh) {
+__device__ __forceinline__ void settle_merge(const Params& P, PendingMerge& pm, RowShared& sh) {
+    if (pm.t < 0) return;
+    if (threadIdx.x == 0) sh.flag = (pm.old == pm.np - 1);
+    __syncthreads();
+    if (sh.flag) row_merge<E>(P, pm.t, pm.np, sh);
+    __syncthreads();
+    pm.t = -1;
+}
+
+// This workgroup's share of the aligned rows [r0, r1): their flattened [rows x
+// vectors-per-row] stream is cut into gridDim.x equal contiguous ranges (a range
+// covers pieces of one or more rows).  A piece's merge check waits until the
+// next piece has streamed; the last one is left in pm.
+template <typename E>
+__device__ __forceinline__ void rows_share(const Params& P, long r0, long r1, PendingMerge& pm, RowShared& sh) {
     const int w = blockIdx.x;
     const int G = gridDim.x;
-    const long NV = P.flat_nv, VPR = P.flat_vpr;
+    const long VPR = P.flat_vpr, NV = (r1 - r0) * VPR;
     const long a = (long)w * NV / G, e = (long)(w + 1) * NV / G;
     long r = a / VPR;
-    // a row's merge is taken up only after the next piece has streamed, so the
-    // arrival counter's round trip never stalls the stream
-    int pend_t = -1, pend_np = 0, pend_old = 0;
     for (long s0 = a; s0 < e; ++r) {
         const long rs = r * VPR, re = rs + VPR;
         const long s1 = e < re ? e : re;
         const int wf = range_owner(rs, NV, G), wl = range_owner(re - 1, NV, G);
         const int np = wl - wf + 1;
-        const int old = row_piece_publish<E>(P, static_cast<int>(r), s0 - rs, s1 - rs, w - wf, np, sh);
+        const int old = row_piece_publish<E>(P, static_cast<int>(r0 + r), s0 - rs, s1 - rs, w - wf, np, sh);
         __syncthreads();
-        if (pend_t >= 0) {
-            if (threadIdx.x == 0) sh.flag = (pend_old == pend_np - 1);
-            __syncthreads();
-            if (sh.flag) row_merge<E>(P, pend_t, pend_np, sh);
-            __syncthreads();
-        }
-        pend_t = static_cast<int>(r);
-        pend_np = np;
-        pend_old = old;
+        settle_merge<E>(P, pm, sh);
+        pm.t = static_cast<int>(r0 + r);
+        pm.np = np;
+        pm.old = old;
         s0 = s1;
     }
-    if (pend_t >= 0) {
-        if (threadIdx.x == 0) sh.flag = (pend_old == pend_np - 1);
-        __syncthreads();
-        if (sh.flag) row_merge<E>(P, pend_t, pend_np, sh);
-    }
+}
+
+// Aligned rows, all of them: one share per workgroup.
+template <typename E>
+__device__ __forceinline__ void rows_flat_range(const Params& P, RowShared& sh) {
+    PendingMerge pm;
+    rows_share<E>(P, 0, P.flat_nv / P.flat_vpr, pm, sh);
+    settle_merge<E>(P, pm, sh);
 }
 
 template <typename E>
@@ -1498,14 +1528,16 @@ __global__ __launch_bounds__(kThreads, 4) void draw_kernel(Params P) {
 // ----------------------------------------------------------------- one-launch step
 // One launch of at most as many workgroups as the device holds at once (so all
 // of them are resident together on an otherwise idle device; every wait below
-// is bounded, and an expired wait is reported as a stall): every workgroup first streams
-// its range of the flattened rows exactly as the flat rows kernel does (merges
-// and resolves included; a resolve publishes its request's draw task with this
-// call's epoch), then its waves work through its share of the call's draw
-// blocks (request-major), each wave on its own: a wave waits only for the task
-// of the request whose blocks it holds, so draws of early requests overlap the
-// streaming of late ones.  The wave that lands a request's last block record
-// runs that request's select.
+// is bounded, and an expired wait is reported as a stall).  The requests are cut
+// into P.slices consecutive slices.  Every workgroup streams its share of slice
+// 0's rows, then of slice 1's, then takes its share of slice 0's draw blocks,
+// then slice 2's rows, slice 1's draw blocks, and so on: the fp64 draw work of
+// early requests runs beside the memory-bound stream of later ones, and only the
+// last slice's draws are left once the stream ends.  Merges and resolves work
+// as in the rows kernel; a resolve publishes its request's draw task with this
+// call's epoch, and a wave waits only for the task of the request whose blocks
+// it holds.  The wave that lands a request's last block record runs that
+// request's select.
 constexpr int kPhaseSpinLimit = 1 << 20;   // bounded wait for a draw task (seconds)
 
 // Lane 0 waits until request b's task carries this call's epoch.  Gives up when
@@ -1526,22 +1558,24 @@ __device__ __forceinline__ bool wait_task(const Params& P, int b) {
     return __builtin_amdgcn_readfirstlane(ok) != 0;
 }
 
-// This wave's draw blocks: blocks g = first, first + kWaves, ... of the call's
-// request-major block list that fall in the workgroup's range [gridDim.x-th share).
+// This wave's draw blocks among those of requests [b0, b1): blocks g = first,
+// first + kWaves, ... of their request-major list that fall in the workgroup's
+// gridDim.x-th share.
 template <typename E>
-__device__ __forceinline__ void draw_phase(const Params& P, const double* tab) {
+__device__ __forceinline__ void draw_share(const Params& P, int b0, int b1, const double* tab) {
     const int lane = threadIdx.x & 63;
     const int NB = P.nblocks;
-    const long DB = (long)P.batch * NB;
+    const long DB = (long)(b1 - b0) * NB;
     const long g1 = (long)(blockIdx.x + 1) * DB / gridDim.x;
     long g = (long)blockIdx.x * DB / gridDim.x + (threadIdx.x >> 6);
     while (g < g1) {
-        const int b = static_cast<int>(g / NB);
-        const long gb0 = (long)b * NB;
+        const int bi = static_cast<int>(g / NB);
+        const long gb0 = (long)bi * NB;
         const long gend = g1 < gb0 + NB ? g1 : gb0 + NB;
         const int j0 = static_cast<int>(g - gb0), j1 = static_cast<int>(gend - gb0);
         const int n = (j1 - j0 + kWaves - 1) / kWaves;          // this wave's blocks of request b
         g += (long)n * kWaves;
+        const int b = b0 + bi;
         if (!wait_task(P, b)) continue;
         const DrawTask tk = load_task(&P.tasks[b]);
         const bool residual = (tk.kind == kDrawResidual);
@@ -1562,14 +1596,42 @@ __device__ __forceinline__ void draw_phase(const Params& P, const double* tab) {
     }
 }
 
+// First request of slice s, and the first target row of request b (the row
+// count for b == batch), clamped so that slices cover the rows once, in order,
+// whatever the offsets hold.
+__device__ __forceinline__ int slice_first_request(const Params& P, int s) {
+    return static_cast<int>((long)s * P.batch / P.slices);
+}
+__device__ __forceinline__ long request_first_row(const Params& P, int b) {
+    const long total = (long)P.total_draft + P.batch;
+    if (b >= P.batch) return total;
+    const long t = P.offsets ? (long)P.offsets[b] + b : (long)b * (P.gamma + 1);
+    return t < 0 ? 0 : (t > total ? total : t);
+}
+
 template <typename E>
 __global__ __launch_bounds__(kThreads, 3) void step_kernel(Params P) {
     __shared__ RowShared sh;
     __shared__ double tab[kExp2TableSize];
     for (int j = threadIdx.x; j < kExp2TableSize; j += kThreads) tab[j] = kExp2Table[j];
-    rows_flat_range<E>(P, sh);
     __syncthreads();
-    draw_phase<E>(P, tab);
+    const int S = P.slices;
+    PendingMerge pm;
+    long r0 = 0;
+    for (int s = 0; s < S; ++s) {
+        long r1 = request_first_row(P, slice_first_request(P, s + 1));
+        if (r1 < r0) r1 = r0;
+        rows_share<E>(P, r0, r1, pm, sh);
+        // a merge still pending from an earlier slice (this workgroup had no
+        // piece of slice s) is settled before waiting on that slice's tasks,
+        // which may depend on it
+        if (pm.t >= 0 && pm.t < r0) settle_merge<E>(P, pm, sh);
+        if (s > 0) draw_share<E>(P, slice_first_request(P, s - 1), slice_first_request(P, s), tab);
+        __syncthreads();
+        settle_merge<E>(P, pm, sh);
+        r0 = r1;
+    }
+    draw_share<E>(P, slice_first_request(P, S - 1), slice_first_request(P, S), tab);
 }
 
 }  // namespace sv
