@@ -1282,17 +1282,28 @@ __device__ __forceinline__ void draw_blocks(const DrawRow<E>& d, int V, BlockRec
     else draw_blocks_kind<E, false, kUpTo2>(d, V, recs, jfirst, jstride, jend, tab);
 }
 
-// Select for one request once all its draw blocks are recorded, by one wave
-// (no LDS besides the exponential table; every lane returns the token).
-// Rebuilds the exact fp64 normaliser Z64 and every block's weight (e / Z64 - q
-// summed over the clearly positive tokens plus the inline marginal ones;
-// blocks with more marginal tokens than slots, or every block when the
-// fp32-pass normaliser is off by more than half the margin, are re-evaluated
-// from their tokens), finds the block holding v * S by a scan over blocks
-// (kSelPer consecutive blocks per lane) and the token by a scan of that block.
+// The select for one request, once all its draw blocks are recorded: the block
+// holding the draw, then the token inside it.
+//
+// Block choice, by one wave (no LDS besides the exponential table; every lane
+// gets the result).  Rebuilds the exact fp64 normaliser Z64 and every block's
+// weight (e / Z64 - q summed over the clearly positive tokens plus the inline
+// marginal ones; blocks with more marginal tokens than slots, or every block
+// when the fp32-pass normaliser is off by more than half the margin, are
+// re-evaluated from their tokens) and finds the block holding v * S by a scan
+// over blocks (kSelPer consecutive blocks per lane).
+struct SelBlock {
+    int jsel;            // selected block
+    double base;         // weight of the blocks before it
+    double tsel;         // v * S
+    double invZ64;
+    bool res_w;          // token weights are residuals (else e)
+    bool fallback;       // rounding left no crossing: take the block's last positive token
+};
+
 template <typename E>
-__device__ __forceinline__ int draw_select_wave(const DrawRow<E>& d, int V, int NB, const BlockRec* recs,
-                                             const double* tab, uint32_t* err) {
+__device__ __forceinline__ SelBlock select_block(const DrawRow<E>& d, int V, int NB, const BlockRec* recs,
+                                                 const double* tab, uint32_t* err) {
     const int lane = threadIdx.x & 63;
     const bool residual = (d.kind == kDrawResidual);
     // every field of this lane's records in one round of loads
@@ -1420,52 +1431,125 @@ __device__ __forceinline__ int draw_select_wave(const DrawRow<E>& d, int V, int 
         block_fallback = true;
         if (lane == 0) flag_error(err, kErrNonFinite);
     }
+    SelBlock sb;
+    sb.jsel = jsel;
+    sb.base = base;
+    sb.tsel = tsel;
+    sb.invZ64 = invZ64;
+    sb.res_w = (kind == kDrawResidual);
+    sb.fallback = block_fallback;
+    return sb;
+}
 
-    // ---- token scan of the selected block (token order: sub-block, lane, position)
-    const long xb = (long)jsel * kBlockElems;
-    const bool res_w = (kind == kDrawResidual);
-    double run_base = base;
+// Token weights of one lane's 8 tokens of sub-block u of the selected block, and
+// their sum (tokens past the row's end weigh nothing).
+template <typename E>
+__device__ __forceinline__ double sub_weights(const DrawRow<E>& d, const RawSub<E>& raw, long x0, int V,
+                                              const SelBlock& sb, const double* tab, double* w) {
+    float l[kSubTokens], q[kSubTokens];
+    decode_sub<E>(raw, sb.res_w, l, q);
+    double tsum = 0.0;
+#pragma unroll
+    for (int k = 0; k < kSubTokens; ++k) {
+        const double e = draw_e<E>(d, l[k], tab);
+        w[k] = sb.res_w ? fmax(e * sb.invZ64 - static_cast<double>(q[k]), 0.0) : e;
+        if (x0 + k >= V) w[k] = 0.0;
+        tsum += w[k];
+        if (k & 1) __builtin_amdgcn_sched_barrier(0);
+    }
+    return tsum;
+}
+
+// Walks one lane's weights in token order from run (the sum before its first
+// token): the first token whose running sum passes tsel, and the last token of
+// positive weight.
+__device__ __forceinline__ void sub_find(const double* w, long x0, double run, const SelBlock& sb, int& ycand,
+                                         int& ylast) {
+#pragma unroll
+    for (int k = 0; k < kSubTokens; ++k) {
+        run += w[k];
+        const int x = static_cast<int>(x0) + k;
+        if (w[k] > 0.0) ylast = x;
+        if (!sb.fallback && ycand == 0x7fffffff && run > sb.tsel) ycand = x;
+    }
+}
+
+// The token, given the first crossing and the last positive token found.
+__device__ __forceinline__ int select_token(int ycand, int ylast, int V, int jsel) {
+    int y = ycand;
+    if (y == 0x7fffffff) y = ylast;
+    if (y < 0) y = min(V - 1, jsel * kBlockElems + kBlockElems - 1);
+    return y;
+}
+
+// Token scan of the selected block by one wave (token order: sub-block, lane,
+// position); every lane returns the token.
+template <typename E>
+__device__ __forceinline__ int draw_select_wave(const DrawRow<E>& d, int V, int NB, const BlockRec* recs,
+                                                const double* tab, uint32_t* err) {
+    const SelBlock sb = select_block<E>(d, V, NB, recs, tab, err);
+    const long xb = (long)sb.jsel * kBlockElems;
+    double run_base = sb.base;
     int ycand = 0x7fffffff, ylast = -1;
     // two sub-blocks per round of loads; the second round only when the first
     // half holds no crossing (or the rounding fallback needs the last positive
     // token of the whole block)
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-        if (half == 1 && !block_fallback && __ballot(ycand != 0x7fffffff) != 0ull) break;
+        if (half == 1 && !sb.fallback && __ballot(ycand != 0x7fffffff) != 0ull) break;
         RawSub<E> raw[2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) issue_sub_any<E>(d, sub_first(xb, 2 * half + h), V, res_w, raw[h]);
+        for (int h = 0; h < 2; ++h) issue_sub_any<E>(d, sub_first(xb, 2 * half + h), V, sb.res_w, raw[h]);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            float l[kSubTokens], q[kSubTokens];
-            decode_sub<E>(raw[h], res_w, l, q);
             const long x0 = sub_first(xb, 2 * half + h);
             double w[kSubTokens];
-            double tsum = 0.0;
-#pragma unroll
-            for (int k = 0; k < kSubTokens; ++k) {
-                const double e = draw_e<E>(d, l[k], tab);
-                w[k] = res_w ? fmax(e * invZ64 - static_cast<double>(q[k]), 0.0) : e;
-                if (x0 + k >= V) w[k] = 0.0;
-                tsum += w[k];
-                if (k & 1) __builtin_amdgcn_sched_barrier(0);
-            }
+            const double tsum = sub_weights<E>(d, raw[h], x0, V, sb, tab, w);
             const double ti = wave_inclusive_scan(tsum);
-            double run = run_base + (ti - tsum);
-#pragma unroll
-            for (int k = 0; k < kSubTokens; ++k) {
-                run += w[k];
-                const int x = static_cast<int>(x0) + k;
-                if (w[k] > 0.0) ylast = x;
-                if (!block_fallback && ycand == 0x7fffffff && run > tsel) ycand = x;
-            }
+            sub_find(w, x0, run_base + (ti - tsum), sb, ycand, ylast);
             run_base += rdlane(ti, 63);
         }
     }
-    int y = wave_min_int(ycand);
-    if (y == 0x7fffffff) y = wave_max_int(ylast);
-    if (y < 0) y = min(V - 1, jsel * kBlockElems + kBlockElems - 1);
-    return y;
+    return select_token(wave_min_int(ycand), wave_max_int(ylast), V, sb.jsel);
+}
+
+// The same select by a whole workgroup: every wave makes the (identical) block
+// choice, then wave u scans sub-block u, so the block is loaded in one round;
+// the sub-block sums and each wave's finds meet in LDS.  Every thread returns
+// the token.  Uniform call.
+static_assert(kSubBlocks == kWaves, "one sub-block per wave");
+struct SelShared {
+    double tot[kWaves];
+    int yc[kWaves], yl[kWaves];
+};
+
+template <typename E>
+__device__ __forceinline__ int draw_select_wg(const DrawRow<E>& d, int V, int NB, const BlockRec* recs,
+                                              const double* tab, uint32_t* err, SelShared& ss) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const SelBlock sb = select_block<E>(d, V, NB, recs, tab, err);
+    const long x0 = sub_first((long)sb.jsel * kBlockElems, wv);
+    RawSub<E> raw;
+    issue_sub_any<E>(d, x0, V, sb.res_w, raw);
+    double w[kSubTokens];
+    const double tsum = sub_weights<E>(d, raw, x0, V, sb, tab, w);
+    const double ti = wave_inclusive_scan(tsum);
+    if (lane == 63) ss.tot[wv] = ti;
+    __syncthreads();
+    // the sums before this sub-block, added in sub-block order
+    double run_base = sb.base;
+#pragma unroll
+    for (int u = 0; u < kWaves; ++u) run_base += (u < wv) ? ss.tot[u] : 0.0;
+    int ycand = 0x7fffffff, ylast = -1;
+    sub_find(w, x0, run_base + (ti - tsum), sb, ycand, ylast);
+    ycand = wave_min_int(ycand);
+    ylast = wave_max_int(ylast);
+    if (lane == 0) { ss.yc[wv] = ycand; ss.yl[wv] = ylast; }
+    __syncthreads();
+    int yc = ss.yc[0], yl = ss.yl[0];
+#pragma unroll
+    for (int u = 1; u < kWaves; ++u) { yc = min(yc, ss.yc[u]); yl = max(yl, ss.yl[u]); }
+    return select_token(yc, yl, V, sb.jsel);
 }
 
 template <typename E>
@@ -1486,6 +1570,7 @@ __device__ __forceinline__ void init_draw_row(DrawRow<E>& d, const Params& P, in
 
 struct DrawShared {
     double tab[kExp2TableSize];
+    SelShared sel;
     int flag;
 };
 
@@ -1516,9 +1601,9 @@ __global__ __launch_bounds__(kThreads, 4) void draw_kernel(Params P) {
     __syncthreads();
     if (tid == 0) sh.flag = (arrive(&P.draw_cnt[b]) == static_cast<uint32_t>(C - 1));
     __syncthreads();
-    if (!sh.flag || tid >= 64) return;
+    if (!sh.flag) return;
     if (tid == 0) reset_counter(&P.draw_cnt[b]);
-    const int y = draw_select_wave<E>(d, P.vocab, NB, recs, sh.tab, P.err);
+    const int y = draw_select_wg<E>(d, P.vocab, NB, recs, sh.tab, P.err, sh.sel);
     if (tid == 0) {
         P.out_tokens[(size_t)b * (P.gamma + 1) + tk.pos] = y;
         P.tasks[b].kind = kDrawNone;               // consumed: a stale task is never replayed
