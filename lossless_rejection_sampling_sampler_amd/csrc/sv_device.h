@@ -545,26 +545,27 @@ __device__ __forceinline__ void load_batch(v4u* buf, const v4u* vp, long first, 
         buf[u] = (u < count) ? __builtin_nontemporal_load(vp + first + (long)u * kThreads) : v4u(E::kNegInfWord);
 }
 
+// The drafted token of a target row, read by every piece of the row (thread 0)
+// so that whichever workgroup merges the row has it at hand: its id, logit and
+// q (x = -1: no drafted token here, or an id outside the vocabulary).
+struct DraftTok {
+    int x = -1;
+    float lx = 0.0f, qx = 0.0f;
+};
+
 // Streams vectors [v0, v1) of target row t (vectors counted from the row's first
 // 16-byte aligned element), adds the scalar head (piece 0) and tail (last piece)
 // and publishes the piece.  Returns, in thread 0, the row's arrival count before
 // this piece (-1 for a row outside the request layout); the caller decides when
 // to look at it, so the counter's round trip can overlap further streaming.
+// The first batch of loads is issued before the request lookup, and the
+// drafted token's logit and q are read once the stream has been taken in, both
+// so that their round trips overlap other work.
 template <typename E>
 __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0, long v1, int piece, int npieces,
-                                                 RowShared& sh) {
+                                                 RowShared& sh, DraftTok& dt) {
     const int tid = threadIdx.x;
     const int V = P.vocab;
-
-    const RowMap rm = map_row(P, t, sh.red);
-    if (!rm.ok) {
-        if (tid == 0 && piece == 0) flag_error(P.err, kErrOffsets);
-        return -1;
-    }
-    const int b = rm.b, i = rm.i, gb = rm.gb;
-    const float T = P.temperature[b];
-    const bool greedy = !(T > 0.0f);
-    const float c = greedy ? 0.0f : static_cast<float>(kLog2e / static_cast<double>(T));
 
     const typename E::T* row = static_cast<const typename E::T*>(P.logits) + (size_t)t * V;
     const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
@@ -579,6 +580,20 @@ __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0
     const int n = span > 0 ? static_cast<int>((span + kThreads - 1) / kThreads) : 0;
     const long first = v0 + tid;
     constexpr int EB = kRowUnroll * E::kPerVec;
+    v4u A[kRowUnroll];
+    if (n > 0) load_batch<E>(A, vp, first, n);
+
+    const RowMap rm = map_row(P, t, sh.red);
+    if (!rm.ok) {
+        if (tid == 0 && piece == 0) flag_error(P.err, kErrOffsets);
+        return -1;
+    }
+    const int b = rm.b, i = rm.i, gb = rm.gb;
+    const float T = P.temperature[b];
+    const bool greedy = !(T > 0.0f);
+    const float c = greedy ? 0.0f : static_cast<float>(kLog2e / static_cast<double>(T));
+    int xd = -1;
+    if (tid == 0 && !greedy && i < gb) xd = P.ids[rm.d0 + i];
 
     float mloc;          // piece max (sampled) / argmax value (greedy)
     int gloc = -1;       // argmax (greedy)
@@ -586,8 +601,7 @@ __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0
     if (!greedy) {
         float mt = -INFINITY, kref = kRefStart;
         double st = 0.0;
-        v4u A[kRowUnroll], Bf[kRowUnroll];
-        if (n > 0) load_batch<E>(A, vp, first, n);
+        v4u Bf[kRowUnroll];
         for (int jb = 0; jb < n; jb += 2 * kRowUnroll) {
             if (jb + kRowUnroll < n)
                 load_batch<E>(Bf, vp, first + (long)(jb + kRowUnroll) * kThreads, n - jb - kRowUnroll);
@@ -607,6 +621,12 @@ __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0
                 accumulate_batch<EB>(f, c, mt, kref, st);
             }
         }
+        dt.x = -1;
+        if (tid == 0 && xd >= 0 && xd < V) {
+            dt.x = xd;
+            dt.lx = E::load1(row, xd);
+            dt.qx = P.q[(size_t)(rm.d0 + i) * V + xd];
+        }
         // unaligned head (piece 0) and tail (last piece): at most 7 scalars each
         float fx = -INFINITY;
         if (piece == 0 && tid < head) fx = E::load1(row, tid);
@@ -621,9 +641,9 @@ __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0
     } else {
         float bv = -INFINITY;
         int bi = 0x7fffffff;
+        dt.x = -1;
         for (int jb = 0; jb < n; jb += kRowUnroll) {
-            v4u A[kRowUnroll];
-            load_batch<E>(A, vp, first + (long)jb * kThreads, n - jb);
+            if (jb > 0) load_batch<E>(A, vp, first + (long)jb * kThreads, n - jb);
 #pragma unroll
             for (int u = 0; u < kRowUnroll; ++u) {
                 float f[E::kPerVec];
@@ -667,7 +687,7 @@ __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0
 // the drafted token's logit and q, and, when it is the request's last row to
 // finish, the request's resolve (accept tests, first rejection, outputs, draw task).
 template <typename E>
-__device__ __forceinline__ void row_merge(const Params& P, int t, int npieces, RowShared& sh) {
+__device__ __forceinline__ void row_merge(const Params& P, int t, int npieces, const DraftTok& dt, RowShared& sh) {
     const int tid = threadIdx.x;
     const int V = P.vocab;
     const RowMap rm = map_row(P, t, sh.red);
@@ -676,9 +696,6 @@ __device__ __forceinline__ void row_merge(const Params& P, int t, int npieces, R
     const float T = P.temperature[b];
     const bool greedy = !(T > 0.0f);
     const float c = greedy ? 0.0f : static_cast<float>(kLog2e / static_cast<double>(T));
-    int xdraft = -1;
-    if (tid == 0 && !greedy && i < gb) xdraft = P.ids[rm.d0 + i];
-    const typename E::T* row = static_cast<const typename E::T*>(P.logits) + (size_t)t * V;
     if (tid == 0) reset_counter(&P.row_cnt[t]);
 
     RowStat st;
@@ -707,11 +724,10 @@ __device__ __forceinline__ void row_merge(const Params& P, int t, int npieces, R
     st.lx = 0.0f; st.qx = 0.0f; st.x = -1;
     if (tid == 0) {
         if (!greedy && i < gb) {
-            const int x = xdraft;
-            if (x >= 0 && x < V) {
-                st.x = x;
-                st.lx = E::load1(row, x);
-                st.qx = P.q[(size_t)(rm.d0 + i) * V + x];
+            if (dt.x >= 0) {
+                st.x = dt.x;
+                st.lx = dt.lx;
+                st.qx = dt.qx;
             } else {
                 flag_error(P.err, kErrDraftId);
             }
@@ -811,10 +827,11 @@ __global__ __launch_bounds__(kThreads) void rows_split_kernel(Params P) {
     int head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(typename E::T));
     if (head > V) head = V;
     const long nvec = (V - head) / E::kPerVec;
-    const int old = row_piece_publish<E>(P, t, (long)s * nvec / S, (long)(s + 1) * nvec / S, s, S, sh);
+    DraftTok dt;
+    const int old = row_piece_publish<E>(P, t, (long)s * nvec / S, (long)(s + 1) * nvec / S, s, S, sh, dt);
     if (threadIdx.x == 0) sh.flag = (old == S - 1);
     __syncthreads();
-    if (sh.flag) row_merge<E>(P, t, S, sh);
+    if (sh.flag) row_merge<E>(P, t, S, dt, sh);
 }
 
 // Workgroup owning vector v when nv vectors are cut into g equal ranges
@@ -829,6 +846,7 @@ __device__ __forceinline__ int range_owner(long v, long nv, int g) {
 // counter's round trip overlaps further work.
 struct PendingMerge {
     int t = -1, np = 0, old = 0;   // row, its pieces, arrival count before this piece (thread 0)
+    DraftTok dt;                   // the row's drafted token (thread 0)
 };
 
 // Runs row t's merge if the pending piece was its last to arrive.  Uniform call.
@@ -837,7 +855,7 @@ __device__ __forceinline__ void settle_merge(const Params& P, PendingMerge& pm, 
     if (pm.t < 0) return;
     if (threadIdx.x == 0) sh.flag = (pm.old == pm.np - 1);
     __syncthreads();
-    if (sh.flag) row_merge<E>(P, pm.t, pm.np, sh);
+    if (sh.flag) row_merge<E>(P, pm.t, pm.np, pm.dt, sh);
     __syncthreads();
     pm.t = -1;
 }
@@ -858,12 +876,14 @@ __device__ __forceinline__ void rows_share(const Params& P, long r0, long r1, Pe
         const long s1 = e < re ? e : re;
         const int wf = range_owner(rs, NV, G), wl = range_owner(re - 1, NV, G);
         const int np = wl - wf + 1;
-        const int old = row_piece_publish<E>(P, static_cast<int>(r0 + r), s0 - rs, s1 - rs, w - wf, np, sh);
+        DraftTok dt;
+        const int old = row_piece_publish<E>(P, static_cast<int>(r0 + r), s0 - rs, s1 - rs, w - wf, np, sh, dt);
         __syncthreads();
         settle_merge<E>(P, pm, sh);
         pm.t = static_cast<int>(r0 + r);
         pm.np = np;
         pm.old = old;
+        pm.dt = dt;
         s0 = s1;
     }
 }
@@ -1568,6 +1588,7 @@ __device__ __forceinline__ void init_draw_row(DrawRow<E>& d, const Params& P, in
     d.qalign = (reinterpret_cast<uintptr_t>(d.qrow) & 15u) == 0;
 }
 
+static_assert(kExp2TableSize == kThreads, "one table entry per draw thread");
 struct DrawShared {
     double tab[kExp2TableSize];
     SelShared sel;
@@ -1584,15 +1605,18 @@ __global__ __launch_bounds__(kThreads, 4) void draw_kernel(Params P) {
     const int c = blockIdx.x - b * C;
     const int NB = P.nblocks;
 
+    // the task, the temperature and the exponential table in one round of loads
+    const double tv = kExp2Table[tid];
     const DrawTask tk = P.tasks[b];
+    const float T = P.temperature[b];
+    sh.tab[tid] = tv;
     if (tk.kind == kDrawNone) return;
     const bool residual = (tk.kind == kDrawResidual);
     if (tk.row < 0 || tk.row >= P.total_draft + P.batch || tk.pos < 0 || tk.pos > P.gamma ||
         (residual && (tk.drow < 0 || tk.drow >= P.total_draft)))
         return;                                    // only reachable with inconsistent offsets
-    for (int j = tid; j < kExp2TableSize; j += kThreads) sh.tab[j] = kExp2Table[j];
     DrawRow<E> d;
-    init_draw_row<E>(d, P, tk.kind, tk.row, tk.drow, tk.pos, tk.v, tk.m, tk.z32, P.temperature[b]);
+    init_draw_row<E>(d, P, tk.kind, tk.row, tk.drow, tk.pos, tk.v, tk.m, tk.z32, T);
     __syncthreads();
     BlockRec* recs = P.recs + (size_t)b * NB;
     // the grid gives every wave at most two blocks (checked by the host)
