@@ -39,9 +39,12 @@ Geometry geometry_for(int vocab, int dtype) {
 }
 
 // Workgroups for the flat rows kernel: all resident at once, at least one batch
-// of loads per thread, and no row cut into more than kMaxPieces pieces.
+// of loads per thread or else one workgroup per row (a small call is
+// latency-bound: its rows' merge chains then run side by side), and no row cut
+// into more than kMaxPieces pieces.
 int flat_workgroups(long nv, long vpr, int resident) {
-    long g = std::min<long>(resident, std::max<long>(1, nv / ((long)sv::kThreads * sv::kRowUnroll)));
+    const long rows = vpr > 0 ? nv / vpr : 1;
+    long g = std::min<long>(resident, std::max<long>(rows, nv / ((long)sv::kThreads * sv::kRowUnroll)));
     while (g > 1) {
         const long lmin = nv / g;
         const long pmax = (vpr + lmin - 1) / lmin + 1;
