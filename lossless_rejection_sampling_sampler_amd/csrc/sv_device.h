@@ -538,11 +538,49 @@ __device__ __forceinline__ void accumulate_batch(const float* f, float c, float&
     st += static_cast<double>(acc);
 }
 
+// Argmax over one loaded batch (vectors jb .. jb + kRowUnroll - 1 of this
+// thread's n), element indices counted from the row start.
+template <typename E>
+__device__ __forceinline__ void argmax_batch(const v4u* buf, int jb, int n, long first, int head, float& bv, int& bi) {
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+        float f[E::kPerVec];
+        E::decode(buf[u], f);
+        const int x0 = head + static_cast<int>((first + (long)(jb + u) * kThreads) * E::kPerVec);
+        if (jb + u < n) {
+#pragma unroll
+            for (int k = 0; k < E::kPerVec; ++k) argmax_merge(bv, bi, f[k], x0 + k);
+        }
+    }
+}
+
+// One batch: vectors first + u * kThreads for u < count (count >= 1).  Every
+// load is issued, the ones past the range from vector `first` itself, so that
+// no branch surrounds a load and the compiler can wait for exactly one batch;
+// the consumer replaces the surplus values (mask_batch) when it takes the batch
+// in, after the next batch's loads are on their way.
 template <typename E>
 __device__ __forceinline__ void load_batch(v4u* buf, const v4u* vp, long first, int count) {
 #pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+        const long idx = (u < count) ? first + (long)u * kThreads : first;
+        buf[u] = __builtin_nontemporal_load(vp + idx);
+    }
+}
+template <typename E>
+__device__ __forceinline__ void mask_batch(v4u* buf, int count) {
+#pragma unroll
     for (int u = 0; u < kRowUnroll; ++u)
-        buf[u] = (u < count) ? __builtin_nontemporal_load(vp + first + (long)u * kThreads) : v4u(E::kNegInfWord);
+        if (u >= count) buf[u] = v4u(E::kNegInfWord);
+}
+// Takes a loaded batch (count of its vectors in range) into the running sums.
+template <typename E>
+__device__ __forceinline__ void take_batch(v4u* buf, int count, float c, float& mt, float& kref, double& st) {
+    mask_batch<E>(buf, count);
+    float f[kRowUnroll * E::kPerVec];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) E::decode(buf[u], f + u * E::kPerVec);
+    accumulate_batch<kRowUnroll * E::kPerVec>(f, c, mt, kref, st);
 }
 
 // The drafted token of a target row, read by every piece of the row (thread 0)
@@ -602,24 +640,24 @@ __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0
         float mt = -INFINITY, kref = kRefStart;
         double st = 0.0;
         v4u Bf[kRowUnroll];
-        for (int jb = 0; jb < n; jb += 2 * kRowUnroll) {
-            if (jb + kRowUnroll < n)
-                load_batch<E>(Bf, vp, first + (long)(jb + kRowUnroll) * kThreads, n - jb - kRowUnroll);
-            {
-                float f[EB];
-#pragma unroll
-                for (int u = 0; u < kRowUnroll; ++u) E::decode(A[u], f + u * E::kPerVec);
-                accumulate_batch<EB>(f, c, mt, kref, st);
-            }
-            if (jb + kRowUnroll >= n) break;
-            if (jb + 2 * kRowUnroll < n)
-                load_batch<E>(A, vp, first + (long)(jb + 2 * kRowUnroll) * kThreads, n - jb - 2 * kRowUnroll);
-            {
-                float f[EB];
-#pragma unroll
-                for (int u = 0; u < kRowUnroll; ++u) E::decode(Bf[u], f + u * E::kPerVec);
-                accumulate_batch<EB>(f, c, mt, kref, st);
-            }
+        // batch j holds this thread's vectors j * kRowUnroll ...; A holds batch 0.
+        // Steady state: two batches at a time with every load unconditional, so
+        // the next batch is always in flight while one is taken in; then the
+        // last one or two batches.
+        const int nb = (n + kRowUnroll - 1) / kRowUnroll;
+        int j = 0;
+        for (; j + 2 < nb; j += 2) {
+            load_batch<E>(Bf, vp, first + (long)(j + 1) * kRowUnroll * kThreads, n - (j + 1) * kRowUnroll);
+            take_batch<E>(A, n - j * kRowUnroll, c, mt, kref, st);
+            load_batch<E>(A, vp, first + (long)(j + 2) * kRowUnroll * kThreads, n - (j + 2) * kRowUnroll);
+            take_batch<E>(Bf, n - (j + 1) * kRowUnroll, c, mt, kref, st);
+        }
+        if (j + 1 < nb) {
+            load_batch<E>(Bf, vp, first + (long)(j + 1) * kRowUnroll * kThreads, n - (j + 1) * kRowUnroll);
+            take_batch<E>(A, n - j * kRowUnroll, c, mt, kref, st);
+            take_batch<E>(Bf, n - (j + 1) * kRowUnroll, c, mt, kref, st);
+        } else if (j < nb) {
+            take_batch<E>(A, n - j * kRowUnroll, c, mt, kref, st);
         }
         dt.x = -1;
         if (tid == 0 && xd >= 0 && xd < V) {
@@ -642,18 +680,22 @@ __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0
         float bv = -INFINITY;
         int bi = 0x7fffffff;
         dt.x = -1;
-        for (int jb = 0; jb < n; jb += kRowUnroll) {
-            if (jb > 0) load_batch<E>(A, vp, first + (long)jb * kThreads, n - jb);
-#pragma unroll
-            for (int u = 0; u < kRowUnroll; ++u) {
-                float f[E::kPerVec];
-                E::decode(A[u], f);
-                const int x0 = head + static_cast<int>((first + (long)(jb + u) * kThreads) * E::kPerVec);
-                if (jb + u < n) {
-#pragma unroll
-                    for (int k = 0; k < E::kPerVec; ++k) argmax_merge(bv, bi, f[k], x0 + k);
-                }
-            }
+        // two batches at a time, as in the sampled stream
+        v4u Bf[kRowUnroll];
+        const int nb = (n + kRowUnroll - 1) / kRowUnroll;
+        int j = 0;
+        for (; j + 2 < nb; j += 2) {
+            load_batch<E>(Bf, vp, first + (long)(j + 1) * kRowUnroll * kThreads, n - (j + 1) * kRowUnroll);
+            argmax_batch<E>(A, j * kRowUnroll, n, first, head, bv, bi);
+            load_batch<E>(A, vp, first + (long)(j + 2) * kRowUnroll * kThreads, n - (j + 2) * kRowUnroll);
+            argmax_batch<E>(Bf, (j + 1) * kRowUnroll, n, first, head, bv, bi);
+        }
+        if (j + 1 < nb) {
+            load_batch<E>(Bf, vp, first + (long)(j + 1) * kRowUnroll * kThreads, n - (j + 1) * kRowUnroll);
+            argmax_batch<E>(A, j * kRowUnroll, n, first, head, bv, bi);
+            argmax_batch<E>(Bf, (j + 1) * kRowUnroll, n, first, head, bv, bi);
+        } else if (j < nb) {
+            argmax_batch<E>(A, j * kRowUnroll, n, first, head, bv, bi);
         }
         if (piece == 0 && tid < head) argmax_merge(bv, bi, E::load1(row, tid), tid);
         if (piece == npieces - 1 && tid >= 64 && tid - 64 < tail) {
