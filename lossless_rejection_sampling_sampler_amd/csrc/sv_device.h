@@ -573,10 +573,11 @@ __device__ __forceinline__ void mask_batch(v4u* buf, int count) {
     for (int u = 0; u < kRowUnroll; ++u)
         if (u >= count) buf[u] = v4u(E::kNegInfWord);
 }
-// Takes a loaded batch (count of its vectors in range) into the running sums.
-template <typename E>
+// Takes a loaded batch (count of its vectors in range) into the running sums;
+// kFull: the caller knows every vector of the batch is in range (no masking).
+template <typename E, bool kFull = false>
 __device__ __forceinline__ void take_batch(v4u* buf, int count, float c, float& mt, float& kref, double& st) {
-    mask_batch<E>(buf, count);
+    if (!kFull) mask_batch<E>(buf, count);
     float f[kRowUnroll * E::kPerVec];
 #pragma unroll
     for (int u = 0; u < kRowUnroll; ++u) E::decode(buf[u], f + u * E::kPerVec);
@@ -646,11 +647,12 @@ __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0
         // last one or two batches.
         const int nb = (n + kRowUnroll - 1) / kRowUnroll;
         int j = 0;
+        // (batches j and j + 1 come before the last batch here, so they are full)
         for (; j + 2 < nb; j += 2) {
             load_batch<E>(Bf, vp, first + (long)(j + 1) * kRowUnroll * kThreads, n - (j + 1) * kRowUnroll);
-            take_batch<E>(A, n - j * kRowUnroll, c, mt, kref, st);
+            take_batch<E, true>(A, kRowUnroll, c, mt, kref, st);
             load_batch<E>(A, vp, first + (long)(j + 2) * kRowUnroll * kThreads, n - (j + 2) * kRowUnroll);
-            take_batch<E>(Bf, n - (j + 1) * kRowUnroll, c, mt, kref, st);
+            take_batch<E, true>(Bf, kRowUnroll, c, mt, kref, st);
         }
         if (j + 1 < nb) {
             load_batch<E>(Bf, vp, first + (long)(j + 1) * kRowUnroll * kThreads, n - (j + 1) * kRowUnroll);
