@@ -31,6 +31,11 @@
  *   - The uniforms are an input, [B, gamma + 2] fp32 in [0, 1): columns
  *     0 .. gamma_b - 1 drive the accept tests, column gamma the residual draw,
  *     column gamma + 1 the bonus draw (gamma = the padded width below).
+ *   - A draft made without a draft model (prompt lookup, page section 7)
+ *     proposes x_i with certainty: q_i is the point mass at x_i, so x_i is
+ *     accepted with probability p_i(x_i) and the residual is p_i with x_i
+ *     removed.  A sparse q (top-k (id, prob) lists) is the same q stored
+ *     without its zeros.
  *   - A draw with weights w and uniform v returns min{x : C_x > v * S} where
  *     C_x is the running sum of w in ascending token id and S = C_{V-1}
  *     (zero-weight tokens are never returned).  If rounding leaves the
@@ -82,10 +87,31 @@ enum sv_device_error {
                                   are unspecified (no access leaves the buffers' bounds) */
     SV_DEVERR_NONFINITE = 4u,  /* a draw row without positive finite mass (a target row with no
                                   finite logit, or NaN logits); that token is unspecified */
-    SV_DEVERR_STALLED = 8u     /* one-launch schedule: a bounded wait (seconds) for a draw task
+    SV_DEVERR_STALLED = 8u,    /* one-launch schedule: a bounded wait (seconds) for a draw task
                                   expired, e.g. because other work kept part of the grid from
                                   becoming resident; that call's outputs are unspecified */
+    SV_DEVERR_TOPK = 16u       /* sparse q: an entry id outside [-1, vocab), or the drafted token
+                                  listed twice in its row; such entries are ignored (the
+                                  request's outputs are unspecified, no access leaves the buffers) */
 };
+
+/* Largest number of (id, prob) entries per draft row of a sparse q. */
+#define SV_MAX_TOPK 64
+
+/* Acceptance counters (optional sv_args.stats, uint32, accumulated with
+ * device-scope atomics and never cleared by the library; the caller zeroes
+ * them when it wants a fresh count).  For a call with padded width gamma:
+ *   [0]                         requests verified
+ *   [1]                         drafts proposed (sum of gamma_b)
+ *   [2]                         drafts accepted (sum of num_accepted)
+ *   [3]                         requests with every draft accepted (a bonus token)
+ *   [4 + k], k = 0..gamma       requests with num_accepted == k
+ *   [5 + gamma + i], i < gamma  requests whose draft i was tested (i < gamma_b, i <= k)
+ *   [5 + 2 gamma + i]           requests whose draft i was accepted (i < k)
+ * They feed acceptance-rate monitoring (the spec-decoding page's section 6.2
+ * log of acceptance rate and accepted tokens per step) without a host copy of
+ * the outputs. */
+#define SV_STATS_LEN(gamma) (5 + 3 * (gamma))
 
 /* Limits fixed at creation.  max_gamma <= SV_MAX_GAMMA. */
 #define SV_MAX_GAMMA 128
@@ -108,7 +134,16 @@ typedef struct sv_config {
  *   draft_probs    [total_draft, vocab] fp32 q; request b's rows are
  *                  off[b] .. off[b] + gamma_b - 1.  Used as given (not
  *                  renormalised).  Only the gathered q(x_i) and the one residual
- *                  row per rejected request are read.
+ *                  row per rejected request are read.  NULL selects a sparse q
+ *                  (draft_topk > 0) or point-mass drafts (draft_topk == 0).
+ *   draft_topk_ids / draft_topk_probs  [total_draft, draft_topk] int32 / fp32,
+ *                  when draft_probs is NULL and draft_topk > 0: q of draft row d
+ *                  is draft_topk_probs[d, s] at token draft_topk_ids[d, s] and 0
+ *                  at every token not listed; id -1 marks an unused entry; the
+ *                  ids of a row are distinct.  A residual draw then reads the
+ *                  logits row and these entries only.
+ *   draft_topk == 0 with draft_probs NULL: q_i is 1 at x_i and 0 elsewhere
+ *                  (drafts proposed without a draft model); no q memory is read.
  *   draft_ids      [total_draft] int32 x_i, in [0, vocab).
  *   temperature    [batch] fp32; > 0 sampled, otherwise greedy.
  *   uniforms       [batch, gamma + 2] fp32 in [0, 1) (see the column map above).
@@ -139,6 +174,10 @@ typedef struct sv_args {
     float   *diag_row_max;
     double  *diag_row_norm;
     float   *diag_ratio;
+    int32_t  draft_topk;            /* entries per sparse q row, 0 .. SV_MAX_TOPK (see above) */
+    const int32_t *draft_topk_ids;  /* [total_draft, draft_topk] or NULL */
+    const float   *draft_topk_probs;/* [total_draft, draft_topk] or NULL */
+    uint32_t *stats;                /* [SV_STATS_LEN(gamma)] acceptance counters, or NULL */
 } sv_args;
 
 typedef struct sv_ctx sv_ctx;    /* opaque; owns the device scratch of one stream */

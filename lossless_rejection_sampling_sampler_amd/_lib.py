@@ -30,7 +30,14 @@ SV_DEVERR_DRAFT_ID = 1
 SV_DEVERR_OFFSETS = 2
 SV_DEVERR_NONFINITE = 4
 SV_DEVERR_STALLED = 8
+SV_DEVERR_TOPK = 16
 SV_MAX_GAMMA = 128
+SV_MAX_TOPK = 64
+
+
+def stats_len(gamma: int) -> int:
+    """Length of the acceptance-counter array for padded width ``gamma`` (SV_STATS_LEN)."""
+    return 5 + 3 * int(gamma)
 SV_SCHEDULE_NONE = 0
 SV_SCHEDULE_SPLIT = 1
 SV_SCHEDULE_FLAT = 2
@@ -78,6 +85,10 @@ class SVArgs(ctypes.Structure):
         ("diag_row_max", ctypes.c_void_p),
         ("diag_row_norm", ctypes.c_void_p),
         ("diag_ratio", ctypes.c_void_p),
+        ("draft_topk", ctypes.c_int32),
+        ("draft_topk_ids", ctypes.c_void_p),
+        ("draft_topk_probs", ctypes.c_void_p),
+        ("stats", ctypes.c_void_p),
     ]
 
 
@@ -153,7 +164,10 @@ class SpecVerify:
 
     def run(self, *, target_logits, draft_probs, draft_ids, temperature, uniforms,
             out_tokens, out_num_accepted, gamma: int, draft_offsets=None, total_draft=None,
-            diag_row_max=None, diag_row_norm=None, diag_ratio=None, stream=None) -> None:
+            diag_row_max=None, diag_row_norm=None, diag_ratio=None, draft_topk: int = 0,
+            draft_topk_ids=None, draft_topk_probs=None, stats=None, stream=None) -> None:
+        """draft_probs None selects a sparse q (draft_topk > 0 entries per row in
+        draft_topk_ids / draft_topk_probs) or point-mass drafts (draft_topk == 0)."""
         import torch
         batch = int(temperature.shape[0])
         if total_draft is None:
@@ -161,7 +175,8 @@ class SpecVerify:
         args = SVArgs(batch, int(gamma), int(total_draft), self.vocab,
                       _ptr(draft_offsets), _ptr(target_logits), _ptr(draft_probs), _ptr(draft_ids),
                       _ptr(temperature), _ptr(uniforms), _ptr(out_tokens), _ptr(out_num_accepted),
-                      _ptr(diag_row_max), _ptr(diag_row_norm), _ptr(diag_ratio))
+                      _ptr(diag_row_max), _ptr(diag_row_norm), _ptr(diag_ratio),
+                      int(draft_topk), _ptr(draft_topk_ids), _ptr(draft_topk_probs), _ptr(stats))
         if stream is None:
             stream = torch.cuda.current_stream(self.device)
         handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)

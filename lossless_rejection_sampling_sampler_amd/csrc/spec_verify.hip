@@ -249,7 +249,18 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
     if (!a->draft_offsets && a->total_draft != a->batch * a->gamma) return SV_ERR_INVALID_ARG;
     if (!a->target_logits || !a->temperature || !a->uniforms || !a->out_tokens || !a->out_num_accepted)
         return SV_ERR_INVALID_ARG;
-    if (a->total_draft > 0 && (!a->draft_probs || !a->draft_ids)) return SV_ERR_INVALID_ARG;
+    if (a->total_draft > 0 && !a->draft_ids) return SV_ERR_INVALID_ARG;
+    // q: dense rows, sparse (id, prob) entries, or point masses at the drafted tokens
+    int qmode = sv::kQDense;
+    if (!a->draft_probs) {
+        if (a->draft_topk < 0 || a->draft_topk > SV_MAX_TOPK) return SV_ERR_INVALID_ARG;
+        qmode = a->draft_topk > 0 ? sv::kQSparse : sv::kQPoint;
+        if (qmode == sv::kQSparse && a->total_draft > 0 && (!a->draft_topk_ids || !a->draft_topk_probs))
+            return SV_ERR_INVALID_ARG;
+        if (reinterpret_cast<uintptr_t>(a->draft_topk_ids) % 4 || reinterpret_cast<uintptr_t>(a->draft_topk_probs) % 4)
+            return SV_ERR_INVALID_ARG;
+    }
+    if (reinterpret_cast<uintptr_t>(a->stats) % 4) return SV_ERR_INVALID_ARG;
     const size_t esize = (cfg.logits_dtype == SV_BF16) ? 2 : 4;
     if (reinterpret_cast<uintptr_t>(a->target_logits) % esize) return SV_ERR_INVALID_ARG;
     if (reinterpret_cast<uintptr_t>(a->draft_probs) % 4 || reinterpret_cast<uintptr_t>(a->draft_ids) % 4)
@@ -270,6 +281,11 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
     P.diag_m = a->diag_row_max;
     P.diag_z = a->diag_row_norm;
     P.diag_r = a->diag_ratio;
+    P.qmode = qmode;
+    P.topk = qmode == sv::kQSparse ? a->draft_topk : 0;
+    P.topk_ids = qmode == sv::kQSparse ? a->draft_topk_ids : nullptr;
+    P.topk_probs = qmode == sv::kQSparse ? a->draft_topk_probs : nullptr;
+    P.stats = a->stats;
     P.batch = a->batch;
     P.gamma = a->gamma;
     P.total_draft = a->total_draft;

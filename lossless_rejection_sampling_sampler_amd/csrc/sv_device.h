@@ -64,7 +64,11 @@ constexpr double kQFloor = 1e-10;        // page section 5.2: q.clamp(min=1e-10)
 constexpr double kSignMargin = 1e-5;
 
 enum : int { kDrawNone = 0, kDrawResidual = 1, kDrawBonus = 2, kDrawDegenerate = 3 };
-enum : uint32_t { kErrDraftId = 1u, kErrOffsets = 2u, kErrNonFinite = 4u, kErrStalled = 8u };
+enum : uint32_t { kErrDraftId = 1u, kErrOffsets = 2u, kErrNonFinite = 4u, kErrStalled = 8u, kErrTopk = 16u };
+// How q is given: dense rows [D, V]; sparse (id, prob) entries [D, topk] with q = 0
+// off the list; or a point mass at the drafted token (q(x_i) = 1, a draft proposed
+// without a draft model).
+enum : int { kQDense = 0, kQSparse = 1, kQPoint = 2 };
 
 struct Piece {           // one (row, piece) partial
     float m;             // piece max of the raw logits (or the argmax value)
@@ -119,6 +123,11 @@ struct Params {
     float* diag_m;
     double* diag_z;
     float* diag_r;
+    int qmode;                 // kQ*
+    int topk;                  // entries per sparse q row
+    const int32_t* topk_ids;   // [D, topk]
+    const float* topk_probs;   // [D, topk]
+    uint32_t* stats;           // optional acceptance counters
     int batch, gamma, total_draft, vocab;
     // launch geometry
     int splits;          // split rows kernel: workgroups per row
@@ -212,6 +221,10 @@ __device__ __forceinline__ uint32_t arrive_n(uint32_t* cnt, uint32_t n) {
 }
 __device__ __forceinline__ void reset_counter(uint32_t* cnt) {
     __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// A counter bumped at the device-coherent level (its result is not used).
+__device__ __forceinline__ void count_add(uint32_t* p, uint32_t v) {
+    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void flag_error(uint32_t* err, uint32_t bits) {
     __hip_atomic_fetch_or(err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -618,7 +631,6 @@ __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0
     const long span = v1 - v0 - tid;
     const int n = span > 0 ? static_cast<int>((span + kThreads - 1) / kThreads) : 0;
     const long first = v0 + tid;
-    constexpr int EB = kRowUnroll * E::kPerVec;
     v4u A[kRowUnroll];
     if (n > 0) load_batch<E>(A, vp, first, n);
 
@@ -665,7 +677,21 @@ __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0
         if (tid == 0 && xd >= 0 && xd < V) {
             dt.x = xd;
             dt.lx = E::load1(row, xd);
-            dt.qx = P.q[(size_t)(rm.d0 + i) * V + xd];
+            dt.qx = (P.qmode == kQDense) ? P.q[(size_t)(rm.d0 + i) * V + xd] : 1.0f;
+        }
+        if (P.qmode == kQSparse && i < gb && tid < 64) {
+            // wave 0 looks the drafted token up in its row's entries (absent: q = 0)
+            const int xw = __builtin_amdgcn_readfirstlane(xd);
+            float qv = 0.0f;
+            if (xw >= 0 && xw < V) {
+                const size_t e0 = (size_t)(rm.d0 + i) * P.topk;
+                const int id = tid < P.topk ? P.topk_ids[e0 + tid] : -1;
+                const float pr = tid < P.topk ? P.topk_probs[e0 + tid] : 0.0f;
+                const unsigned long long hit = __ballot(id == xw);
+                if (hit != 0ull) qv = rdlane(pr, __ffsll(static_cast<long long>(hit)) - 1);
+                if (tid == 0 && __popcll(hit) > 1) flag_error(P.err, kErrTopk);
+            }
+            if (tid == 0) dt.qx = qv;
         }
         // unaligned head (piece 0) and tail (last piece): at most 7 scalars each
         float fx = -INFINITY;
@@ -733,7 +759,6 @@ __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0
 template <typename E>
 __device__ __forceinline__ void row_merge(const Params& P, int t, int npieces, const DraftTok& dt, RowShared& sh) {
     const int tid = threadIdx.x;
-    const int V = P.vocab;
     const RowMap rm = map_row(P, t, sh.red);
     if (!rm.ok) return;
     const int b = rm.b, i = rm.i, gb = rm.gb;
@@ -829,6 +854,18 @@ __device__ __forceinline__ void row_merge(const Params& P, int t, int npieces, c
     __syncthreads();
     const int k = sh.k;
     if (tid == k) { sh.mk = m_t; sh.zk = z_t; }
+    if (P.stats) {
+        uint32_t* S = P.stats;
+        if (tid == 0) {
+            count_add(&S[0], 1u);
+            count_add(&S[1], static_cast<uint32_t>(gb));
+            count_add(&S[2], static_cast<uint32_t>(k));
+            if (k == gb) count_add(&S[3], 1u);
+            count_add(&S[4 + k], 1u);
+        }
+        if (tid < gb && tid <= k) count_add(&S[5 + G + tid], 1u);
+        if (tid < k) count_add(&S[5 + 2 * G + tid], 1u);
+    }
     if (tid <= G) {
         int tok = -1;
         if (tid < k) tok = xj;
@@ -958,8 +995,15 @@ struct DrawRow {
     double mc2;          // m * c2 (both exactly 256 times their unscaled roundings)
     double z32;          // normaliser from the fp32-exponential pass
     const typename E::T* lrow;
-    const float* qrow;   // residual: q row, else nullptr
+    const float* qrow;   // residual with dense q: q row, else nullptr
     bool lalign, qalign;
+    // residual with sparse or point-mass q: the block sums are those of p, and the
+    // select takes the listed tokens' q off them; entry s of the draft row is
+    // token sid[s] with q = sq[s] (point mass: sid = the drafted token, sq null, q = 1)
+    bool qlist;
+    int nq;
+    const int32_t* sid;
+    const float* sq;
 };
 
 // e = exp((l - m) / T) of one token, in fp64 (the same expression everywhere).
@@ -1342,7 +1386,7 @@ __device__ __forceinline__ void draw_blocks_kind(const DrawRow<E>& d, int V, Blo
 template <typename E, bool kUpTo2 = false>
 __device__ __forceinline__ void draw_blocks(const DrawRow<E>& d, int V, BlockRec* recs, int jfirst, int jstride, int jend,
                             const double* tab) {
-    if (d.kind == kDrawResidual) draw_blocks_kind<E, true, kUpTo2>(d, V, recs, jfirst, jstride, jend, tab);
+    if (d.kind == kDrawResidual && !d.qlist) draw_blocks_kind<E, true, kUpTo2>(d, V, recs, jfirst, jstride, jend, tab);
     else draw_blocks_kind<E, false, kUpTo2>(d, V, recs, jfirst, jstride, jend, tab);
 }
 
@@ -1362,7 +1406,13 @@ struct SelBlock {
     double tsel;         // v * S
     double invZ64;
     bool res_w;          // token weights are residuals (else e)
+    bool with_q;         // residual weights read a dense q row (else q = 0 off the list)
     bool fallback;       // rounding left no crossing: take the block's last positive token
+    // listed q (sparse or point mass): lane s holds entry s; qmask: the entries
+    // inside the selected block (wave-uniform)
+    int qid;
+    float qq;
+    unsigned long long qmask;
 };
 
 template <typename E>
@@ -1381,7 +1431,7 @@ __device__ __forceinline__ SelBlock select_block(const DrawRow<E>& d, int V, int
         se_t[r] = in ? ld_coherent(&rc->se) : 0.0;
         ea_t[r] = qa_t[r] = 0.0;
         nm_t[r] = 0;
-        if (residual && in) {
+        if (residual && !d.qlist && in) {
             ea_t[r] = ld_coherent(&rc->ea);
             qa_t[r] = ld_coherent(&rc->qa);
             nm_t[r] = ld_coherent(&rc->nm);
@@ -1394,7 +1444,32 @@ __device__ __forceinline__ SelBlock select_block(const DrawRow<E>& d, int V, int
     const double invZ64 = 1.0 / Z64;
     int kind = d.kind;
     double wt[kSelPer];
-    if (residual) {
+    int qid = -1;
+    float qq = 0.0f;
+    bool qvalid = false;
+    if (residual && d.qlist) {
+        // q is zero except at the listed tokens: block weights are the blocks' p
+        // mass less min(p, q) of the listed tokens they hold (p - (p - q)_+)
+        if (lane < d.nq) {
+            qid = d.sid[lane];
+            qq = d.sq ? d.sq[lane] : 1.0f;
+        }
+        qvalid = qid >= 0 && qid < V;
+        if (lane < d.nq && !qvalid && qid != -1) flag_error(err, kErrTopk);
+        double cs = 0.0;
+        if (qvalid) cs = fmin(draw_e<E>(d, E::load1(d.lrow, qid), tab) * invZ64, static_cast<double>(qq));
+        const int qblk = qvalid ? qid / kBlockElems : -1;
+#pragma unroll
+        for (int r = 0; r < kSelPer; ++r) wt[r] = se_t[r] * invZ64;
+        for (int s = 0; s < d.nq; ++s) {
+            const int js = rdlane(qblk, s);
+            if (js < 0) continue;
+            const double c = rdlane(cs, s);
+#pragma unroll
+            for (int r = 0; r < kSelPer; ++r)
+                if (lane * kSelPer + r == js) wt[r] -= c;
+        }
+    } else if (residual) {
         const bool full = !(fabs(Z64 - d.z32) <= 0.5 * kSignMargin * Z64);
 #pragma unroll
         for (int r = 0; r < kSelPer; ++r) wt[r] = ea_t[r] * invZ64 - qa_t[r];
@@ -1501,7 +1576,11 @@ __device__ __forceinline__ SelBlock select_block(const DrawRow<E>& d, int V, int
     sb.tsel = tsel;
     sb.invZ64 = invZ64;
     sb.res_w = (kind == kDrawResidual);
+    sb.with_q = sb.res_w && !d.qlist;
     sb.fallback = block_fallback;
+    sb.qid = qid;
+    sb.qq = qq;
+    sb.qmask = sb.res_w ? __ballot(qvalid && qid / kBlockElems == jsel) : 0ull;
     return sb;
 }
 
@@ -1511,16 +1590,28 @@ template <typename E>
 __device__ __forceinline__ double sub_weights(const DrawRow<E>& d, const RawSub<E>& raw, long x0, int V,
                                               const SelBlock& sb, const double* tab, double* w) {
     float l[kSubTokens], q[kSubTokens];
-    decode_sub<E>(raw, sb.res_w, l, q);
-    double tsum = 0.0;
+    decode_sub<E>(raw, sb.with_q, l, q);
 #pragma unroll
     for (int k = 0; k < kSubTokens; ++k) {
         const double e = draw_e<E>(d, l[k], tab);
         w[k] = sb.res_w ? fmax(e * sb.invZ64 - static_cast<double>(q[k]), 0.0) : e;
         if (x0 + k >= V) w[k] = 0.0;
-        tsum += w[k];
         if (k & 1) __builtin_amdgcn_sched_barrier(0);
     }
+    // listed q entries among this lane's tokens (q was taken as 0 above)
+    unsigned long long m = sb.qmask;
+    while (m != 0ull) {
+        const int s = __ffsll(static_cast<long long>(m)) - 1;
+        m &= m - 1ull;
+        const int xi = rdlane(sb.qid, s);
+        const double qv = static_cast<double>(rdlane(sb.qq, s));
+#pragma unroll
+        for (int k = 0; k < kSubTokens; ++k)
+            if (x0 + k == xi) w[k] = fmax(w[k] - qv, 0.0);
+    }
+    double tsum = 0.0;
+#pragma unroll
+    for (int k = 0; k < kSubTokens; ++k) tsum += w[k];
     return tsum;
 }
 
@@ -1563,7 +1654,7 @@ __device__ __forceinline__ int draw_select_wave(const DrawRow<E>& d, int V, int 
         if (half == 1 && !sb.fallback && __ballot(ycand != 0x7fffffff) != 0ull) break;
         RawSub<E> raw[2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) issue_sub_any<E>(d, sub_first(xb, 2 * half + h), V, sb.res_w, raw[h]);
+        for (int h = 0; h < 2; ++h) issue_sub_any<E>(d, sub_first(xb, 2 * half + h), V, sb.with_q, raw[h]);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const long x0 = sub_first(xb, 2 * half + h);
@@ -1594,7 +1685,7 @@ __device__ __forceinline__ int draw_select_wg(const DrawRow<E>& d, int V, int NB
     const SelBlock sb = select_block<E>(d, V, NB, recs, tab, err);
     const long x0 = sub_first((long)sb.jsel * kBlockElems, wv);
     RawSub<E> raw;
-    issue_sub_any<E>(d, x0, V, sb.res_w, raw);
+    issue_sub_any<E>(d, x0, V, sb.with_q, raw);
     double w[kSubTokens];
     const double tsum = sub_weights<E>(d, raw, x0, V, sb, tab, w);
     const double ti = wave_inclusive_scan(tsum);
@@ -1627,9 +1718,21 @@ __device__ __forceinline__ void init_draw_row(DrawRow<E>& d, const Params& P, in
     d.mc2 = d.m * d.c2;
     d.z32 = z32;
     d.lrow = static_cast<const typename E::T*>(P.logits) + (size_t)row * P.vocab;
-    d.qrow = (kind == kDrawResidual) ? P.q + (size_t)drow * P.vocab : nullptr;
+    d.qlist = (kind == kDrawResidual) && P.qmode != kQDense;
+    d.qrow = (kind == kDrawResidual && !d.qlist) ? P.q + (size_t)drow * P.vocab : nullptr;
     d.lalign = (reinterpret_cast<uintptr_t>(d.lrow) & 15u) == 0;
     d.qalign = (reinterpret_cast<uintptr_t>(d.qrow) & 15u) == 0;
+    d.nq = 0;
+    d.sid = nullptr;
+    d.sq = nullptr;
+    if (d.qlist && P.qmode == kQSparse) {
+        d.nq = P.topk;
+        d.sid = P.topk_ids + (size_t)drow * P.topk;
+        d.sq = P.topk_probs + (size_t)drow * P.topk;
+    } else if (d.qlist) {
+        d.nq = 1;
+        d.sid = P.ids + drow;
+    }
 }
 
 static_assert(kExp2TableSize == kThreads, "one table entry per draw thread");

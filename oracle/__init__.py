@@ -10,6 +10,8 @@ from .rejection_sampler import (  # noqa: F401
     RESIDUAL_Q_FLOOR,
     OracleOutputs,
     accept_ratio,
+    acceptance_stats,
+    draft_q_rows,
     decode_logits,
     greedy_tokens,
     inverse_cdf,

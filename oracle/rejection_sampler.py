@@ -20,6 +20,11 @@ Source of the method: the spec-decoding page at dpshk.com/news/5598276
 * [page §5.3] the bonus token: when all gamma drafts are accepted, one more
   token is drawn from the (gamma+1)-th target distribution.
 * [page §8, pitfall 2] temperature 0 is greedy decoding.
+* [page §7] prompt lookup decoding: drafts taken from the prompt, with no
+  draft model.  Such a draft proposes its token with certainty, i.e. q is the
+  point mass at the drafted token.
+* [page §6.2] the serving log reports the draft acceptance rate and the
+  accepted tokens per step (acceptance_stats counts what these are made of).
 
 Readings where the page is silent (each listed with its reason in the design doc):
 temperature enters as softmax(l / T) with the max over the raw logits; T <= 0
@@ -29,6 +34,8 @@ ties); uniforms arrive as an input of shape [B, gamma+2] whose columns
 gamma+1 the bonus draw; a uniform v maps to the token min{x : C_x > v * S},
 with C the running sum of the weights in ascending token id and S their total;
 a residual with S <= 0 (impossible in exact arithmetic) falls back to p.
+A sparse q, given as (id, prob) entries per draft row, is the q that holds
+those probabilities at those ids and zero everywhere else.
 
 All floating point is fp64 from the exact fp32 / bf16 input values.
 """
@@ -121,6 +128,64 @@ def _select(C: np.ndarray, w: np.ndarray, v) -> Tuple[np.ndarray, np.ndarray, np
     return y.reshape(lead), S.reshape(lead), fb.reshape(lead)
 
 
+def draft_q_rows(inp, drows: np.ndarray) -> np.ndarray:
+    """q of draft rows ``drows`` as dense fp64 rows [len(drows), V].
+
+    Dense q is read as stored.  A sparse q (``inp.q_format == "sparse"``) holds
+    ``topk_probs[d, s]`` at token ``topk_ids[d, s]`` and zero at every token not
+    listed (id -1 marks an unused entry; the ids of a row must be distinct).  A
+    point-mass q (``"point"``, a draft proposed without a draft model,
+    [page §7]) is 1 at the drafted token and 0 elsewhere.
+    """
+    drows = np.asarray(drows, dtype=np.int64).ravel()
+    V = inp.vocab
+    fmt = getattr(inp, "q_format", "dense")
+    if fmt == "dense":
+        return np.asarray(inp.draft_probs[drows], dtype=np.float64).reshape(len(drows), V)
+    q = np.zeros((len(drows), V))
+    if fmt == "point":
+        q[np.arange(len(drows)), np.asarray(inp.draft_ids, dtype=np.int64)[drows]] = 1.0
+        return q
+    if fmt != "sparse":
+        raise ValueError(f"unknown q format {fmt!r}")
+    for j, d in enumerate(drows):
+        ids = np.asarray(inp.topk_ids[d], dtype=np.int64)
+        pr = np.asarray(inp.topk_probs[d], dtype=np.float32).astype(np.float64)
+        used = ids != -1
+        if np.any((ids[used] < 0) | (ids[used] >= V)):
+            raise ValueError(f"sparse q row {d}: id outside [-1, V)")
+        if len(np.unique(ids[used])) != int(used.sum()):
+            raise ValueError(f"sparse q row {d}: repeated id")
+        q[j, ids[used]] = pr[used]
+    return q
+
+
+def acceptance_stats(num_accepted: np.ndarray, gammas: np.ndarray, gamma: int) -> np.ndarray:
+    """Counts behind the acceptance figures of [page §6.2] for one step.
+
+    [0] requests, [1] drafts proposed (sum gamma_b), [2] drafts accepted (sum k_b),
+    [3] requests with every draft accepted, [4 + k] requests with k_b == k
+    (k = 0..gamma), [5 + gamma + i] requests whose draft i was tested
+    (i < gamma_b and i <= k_b), [5 + 2 gamma + i] requests whose draft i was
+    accepted (i < k_b).
+    """
+    k = np.asarray(num_accepted, dtype=np.int64)
+    g = np.asarray(gammas, dtype=np.int64)
+    out = np.zeros(5 + 3 * gamma, dtype=np.int64)
+    out[0] = len(k)
+    out[1] = g.sum()
+    out[2] = k.sum()
+    out[3] = int((k == g).sum())
+    for kb, gb in zip(k, g):
+        out[4 + kb] += 1
+        for i in range(gb):
+            if i <= kb:
+                out[5 + gamma + i] += 1
+            if i < kb:
+                out[5 + 2 * gamma + i] += 1
+    return out
+
+
 def _first_rejection(accepted: np.ndarray, g: int) -> np.ndarray:
     """Index of the first False along the last axis, g if none [page §5.2 cumprod]."""
     if g == 0:
@@ -198,8 +263,7 @@ def verify(inp, uniform_sets: Optional[Sequence[np.ndarray]] = None,
                 if want_greedy:
                     _greedy_chunk(outs, us, sel, trows, l, x, g)
                 else:
-                    q = np.asarray(inp.draft_probs[drows.ravel()], dtype=np.float64)
-                    q = q.reshape(len(sel), g, V)
+                    q = draft_q_rows(inp, drows).reshape(len(sel), g, V)
                     _sampled_chunk(outs, us, sel, trows, drows, l, q, x, T_all[sel], g, G)
     return outs[0] if single else outs
 
@@ -279,7 +343,7 @@ def draw_weights(inp, b: int, k: int) -> Tuple[np.ndarray, int]:
     m, e, Z, p = target_distribution(l, T)
     if k >= g:
         return e, DRAW_BONUS
-    qk = np.asarray(inp.draft_probs[int(off[b]) + k], dtype=np.float64)
+    qk = draft_q_rows(inp, [int(off[b]) + k])[0]
     w = residual_weights(p, qk)
     if not (w.sum() > 0):
         return p, DRAW_DEGENERATE

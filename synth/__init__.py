@@ -15,4 +15,8 @@ from .workloads import (  # noqa: F401
     f32_to_bf16_bits,
     make_inputs,
     make_config,
+    make_point_config,
+    make_sparse_config,
+    to_point,
+    to_sparse,
 )

@@ -48,7 +48,7 @@ class WorkloadSpec:
     draft_sigma: Union[float, Tuple[float, float]]   # fixed, or (lo, hi) per request
     temperatures: Tuple[float, ...]                  # per-request T uniform over these
     ragged: bool = False            # gamma_b ~ U{0..gamma}, packed with offsets
-    q_mode: str = "dense"           # "dense" | "half_equal_half_topk"
+    q_mode: str = "dense"           # "dense" | "half_equal_half_topk" | "topk" | "argmax"
     top_k: int = 50
     explicit_offsets: bool = False  # pass offsets even when every gamma_b == gamma
 
@@ -81,12 +81,18 @@ class VerifyInputs:
     vocab: int
     dtype: str
     logits: np.ndarray        # [R, V] float32, or uint16 bf16 bit patterns
-    draft_probs: np.ndarray   # [D, V] float32
+    draft_probs: Optional[np.ndarray]   # [D, V] float32; None for sparse / point-mass q
     draft_ids: np.ndarray     # [D] int32
     temperature: np.ndarray   # [B] float32
     uniforms: np.ndarray      # [B, gamma + 2] float32
     offsets: Optional[np.ndarray] = None   # [B + 1] int32
     name: str = ""
+    # how q is stored: "dense" (draft_probs), "sparse" (topk_ids / topk_probs
+    # [D, K], id -1 = unused entry, q = 0 off the list) or "point" (q = 1 at the
+    # drafted token, a draft proposed without a draft model)
+    q_format: str = "dense"
+    topk_ids: Optional[np.ndarray] = None
+    topk_probs: Optional[np.ndarray] = None
 
     @property
     def gammas(self) -> np.ndarray:
@@ -115,8 +121,8 @@ class VerifyInputs:
         return int(self.draft_offsets[b]) + i
 
     def nbytes(self) -> int:
-        return sum(a.nbytes for a in (self.logits, self.draft_probs, self.draft_ids,
-                                      self.temperature, self.uniforms))
+        return sum(a.nbytes for a in (self.logits, self.draft_probs, self.draft_ids, self.temperature,
+                                      self.uniforms, self.topk_ids, self.topk_probs) if a is not None)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -160,7 +166,12 @@ def _gen_request(spec: WorkloadSpec, rng: np.random.Generator, g: int, T: float,
     q32 = np.zeros((g, V), dtype=np.float32)
     ids = np.zeros(g, dtype=np.int32)
     if g > 0:
-        if T > 0:
+        if T > 0 and q_kind == "argmax":
+            # a deterministic proposal: the draft's most likely token, q one-hot
+            draft = lt[:g] + rng.normal(0.0, sigma_d, size=(g, V))
+            ids[:] = draft.argmax(axis=-1)
+            q32[np.arange(g), ids] = 1.0
+        elif T > 0:
             if q_kind == "equal_p":
                 q32[:] = _draft_distribution(lt[:g] / T)
             else:
@@ -205,7 +216,9 @@ def make_inputs(spec: WorkloadSpec, seed: int) -> VerifyInputs:
     else:
         sig = np.full(B, float(spec.draft_sigma))
     kinds = np.array(["dense"] * B, dtype=object)
-    if spec.q_mode == "half_equal_half_topk":
+    if spec.q_mode in ("topk", "argmax"):
+        kinds[:] = spec.q_mode
+    elif spec.q_mode == "half_equal_half_topk":
         perm = srng.permutation(B)
         kinds[perm[: B // 2]] = "equal_p"
         kinds[perm[B // 2:]] = "topk"
@@ -237,6 +250,51 @@ def make_inputs(spec: WorkloadSpec, seed: int) -> VerifyInputs:
         draft_ids=ids, temperature=T.astype(np.float32), uniforms=u,
         offsets=offsets.astype(np.int32) if use_offsets else None, name=spec.name,
     )
+
+
+def to_sparse(inp: VerifyInputs, k: int, seed: int = 0) -> VerifyInputs:
+    """The same q stored as k (id, prob) entries per draft row: the row's nonzero
+    entries in a seeded random slot order, unused slots id -1 / prob 0.  Every
+    row must have at most k nonzeros."""
+    D = inp.total_draft
+    ids = np.full((D, k), -1, dtype=np.int32)
+    probs = np.zeros((D, k), dtype=np.float32)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 13])))
+    for d in range(D):
+        nz = np.nonzero(inp.draft_probs[d])[0]
+        if len(nz) > k:
+            raise ValueError(f"draft row {d} has {len(nz)} nonzeros, more than {k}")
+        slots = rng.permutation(k)[:len(nz)]
+        ids[d, slots] = nz
+        probs[d, slots] = inp.draft_probs[d, nz]
+    return dataclasses.replace(inp, draft_probs=None, q_format="sparse", topk_ids=ids, topk_probs=probs,
+                               name=inp.name + f"_sparse{k}")
+
+
+def to_point(inp: VerifyInputs) -> VerifyInputs:
+    """The same drafted tokens proposed without a draft model: q is the point mass
+    at each drafted token (no q array is stored)."""
+    return dataclasses.replace(inp, draft_probs=None, q_format="point", topk_ids=None, topk_probs=None,
+                               name=inp.name + "_point")
+
+
+# Workloads of the sparse-q formats (the page's section 7 prompt lookup, and the
+# top-k draft of the ragged B=256 workload stored as (id, prob) lists).
+SPARSE_TOPK = 50
+
+
+def make_sparse_config(replicate: int = 0, **overrides) -> VerifyInputs:
+    """B=256, ragged gamma_b, V=128256, bf16, T=1, every request's q top-50
+    sparse-renormalised and stored as 50 (id, prob) entries per draft row."""
+    spec = CONFIGS[5].with_(q_mode="topk", name="B256_ragged8_V128256_bf16_top50list", **overrides)
+    return to_sparse(make_inputs(spec, seed=5100 + replicate), SPARSE_TOPK, seed=5100 + replicate)
+
+
+def make_point_config(replicate: int = 0, **overrides) -> VerifyInputs:
+    """B=64, gamma=5, V=151936, bf16, T=0.8 with point-mass drafts: each drafted
+    token is the argmax of the noisy draft logits, proposed with certainty."""
+    spec = CONFIGS[3].with_(q_mode="argmax", name="B64_g5_V151936_bf16_point", **overrides)
+    return to_point(make_inputs(spec, seed=3100 + replicate))
 
 
 def make_config(n: int, replicate: int = 0, **overrides) -> VerifyInputs:

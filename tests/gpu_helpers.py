@@ -45,11 +45,13 @@ class ParityReport:
         self.unexcused.extend(other.unexcused)
 
 
-def upload_inputs(inp, device="cuda:0", diag=True):
+def upload_inputs(inp, device="cuda:0", diag=True, stats=False):
     from lossless_rejection_sampling_sampler_amd import upload
     return upload(logits=inp.logits, logits_dtype=inp.dtype, draft_probs=inp.draft_probs,
                   draft_ids=inp.draft_ids, temperature=inp.temperature, uniforms=inp.uniforms,
-                  gamma=inp.gamma, draft_offsets=inp.offsets, device=device, diag=diag)
+                  gamma=inp.gamma, draft_offsets=inp.offsets, device=device, diag=diag,
+                  topk_ids=getattr(inp, "topk_ids", None), topk_probs=getattr(inp, "topk_probs", None),
+                  stats=stats)
 
 
 def make_verifier(inp, max_batch=None, max_gamma=None, profile=False, schedule=None):

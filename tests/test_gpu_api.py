@@ -22,7 +22,7 @@ def _args(db, **over):
     p = lambda t: 0 if t is None else t.data_ptr()
     a = SVArgs(db.batch, db.gamma, db.total_draft, db.vocab, p(db.draft_offsets), p(db.target_logits),
                p(db.draft_probs), p(db.draft_ids), p(db.temperature), p(db.uniforms), p(db.out_tokens),
-               p(db.out_num_accepted), 0, 0, 0)
+               p(db.out_num_accepted), 0, 0, 0, 0, 0, 0, 0)
     for k, v in over.items():
         setattr(a, k, v)
     return a
@@ -59,6 +59,12 @@ def test_run_argument_checks():
     assert sv.run_args(_args(db, out_tokens=None), s) == 1
     assert sv.run_args(_args(db, target_logits=db.target_logits.data_ptr() + 2), s) == 1  # misaligned fp32
     assert sv.run_args(_args(db, batch=-1), s) == 1
+    # sparse q: at most 64 entries per row, and the entry arrays when entries are used
+    assert sv.run_args(_args(db, draft_probs=None, draft_topk=65), s) == 1
+    assert sv.run_args(_args(db, draft_probs=None, draft_topk=-1), s) == 1
+    assert sv.run_args(_args(db, draft_probs=None, draft_topk=4), s) == 1
+    assert sv.run_args(_args(db, draft_probs=None, draft_topk=0), s) == 0      # point-mass drafts
+    assert sv.run_args(_args(db, stats=db.out_tokens.data_ptr() + 2), s) == 1  # misaligned counters
     torch.cuda.synchronize()
     assert sv.device_errors() == 0
 
