@@ -32,6 +32,39 @@ CSRC = os.path.join(ROOT, "lossless_rejection_sampling_sampler_amd", "csrc")
 KERNEL_SOURCES = ("sv_device.h", "spec_verify.hip")
 
 
+def _sparse_as_dense(rep):
+    """The sparse workload's q kept in dense rows (the same q; for comparison)."""
+    from synth.workloads import CONFIGS, make_inputs
+    spec = CONFIGS[5].with_(q_mode="topk", name="B256_ragged8_V128256_bf16_top50_dense")
+    return make_inputs(spec, seed=5100 + rep)
+
+
+def make_workload(name: str, rep: int):
+    from synth import make_config, make_point_config, make_sparse_config
+    if name == "config3":
+        return make_config(CONFIG_ID, replicate=rep)
+    if name == "sparse":
+        return make_sparse_config(replicate=rep)
+    if name == "sparse_as_dense":
+        return _sparse_as_dense(rep)
+    if name == "point":
+        return make_point_config(replicate=rep)
+    if name == "point_as_dense":
+        from synth.workloads import CONFIGS, make_inputs
+        return make_inputs(CONFIGS[3].with_(q_mode="argmax", name="B64_g5_V151936_bf16_argmax_dense"),
+                           seed=3100 + rep)
+    raise ValueError(name)
+
+
+WORKLOAD_TEXT = {
+    "config3": "B=64, gamma=5, V=151936, bf16 logits, fp32 q, T=0.8",
+    "sparse": "B=256, ragged gamma_b in 0..8, V=128256, bf16 logits, top-50 q as 50 (id, prob) entries per row, T=1",
+    "sparse_as_dense": "B=256, ragged gamma_b in 0..8, V=128256, bf16 logits, top-50 q in dense fp32 rows, T=1",
+    "point": "B=64, gamma=5, V=151936, bf16 logits, point-mass drafts (no q memory), T=0.8",
+    "point_as_dense": "B=64, gamma=5, V=151936, bf16 logits, point-mass drafts as one-hot dense fp32 q rows, T=0.8",
+}
+
+
 def traffic_path(kernel: str) -> str:
     """Counter-derived HBM traffic of one kernel on this workload (written from rocprofv3 runs)."""
     stem = kernel.replace("<", "_").replace(">", "")
@@ -58,20 +91,27 @@ def log(msg):
 def algorithmic_bytes(inp, num_accepted):
     """Bytes the method must move for one step (see the measurement section of the design doc).
 
-    rows kernel: every target row once, the drafted-token gathers (id, logit, q),
-    temperature, uniforms and the outputs; draw kernel: the draw row's logits
-    again for every sampled request and its q row when it is a residual.
+    rows kernel: every target row once, the drafted-token gathers (id, logit and
+    q: one value of a dense q row, the K (id, prob) entries of a sparse row, none
+    for a point mass), temperature, uniforms and the outputs; draw kernel: the
+    draw row's logits again for every sampled request and, for a residual, its
+    q (a dense q row, or the sparse entries and their tokens' logits, or the
+    drafted token and its logit for a point mass).
     """
     import numpy as np
     B, G, V, D, R = inp.batch, inp.gamma, inp.vocab, inp.total_draft, inp.total_rows
     sl = 2 if inp.dtype == "bf16" else 4
     sampled = inp.temperature > 0
     gam = inp.gammas
-    rows = R * V * sl + D * (4 + sl + 4) + 4 * B + 4 * B * (G + 2) + 4 * B * (G + 1) + 4 * B
+    fmt = getattr(inp, "q_format", "dense")
+    K = inp.topk_ids.shape[1] if fmt == "sparse" else 0
+    q_gather = {"dense": 4, "sparse": 8 * K, "point": 0}[fmt]
+    q_residual = {"dense": 4 * V, "sparse": K * (8 + sl), "point": 4 + sl}[fmt]
+    rows = R * V * sl + D * (4 + sl + q_gather) + 4 * B + 4 * B * (G + 2) + 4 * B * (G + 1) + 4 * B
     if inp.offsets is not None:
         rows += 4 * (B + 1)
     residual = sampled & (num_accepted < gam)
-    draw = int(sampled.sum()) * V * sl + int(residual.sum()) * 4 * V
+    draw = int(sampled.sum()) * V * sl + int(residual.sum()) * q_residual
     return int(rows), int(draw)
 
 
@@ -164,6 +204,9 @@ def main():
     ap.add_argument("--rotate", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed-replicate", type=int, default=0)
+    ap.add_argument("--workload", choices=list(WORKLOAD_TEXT), default="config3",
+                    help="config3 (the default line); other workloads of the draft-distribution "
+                         "formats are for comparison runs")
     ap.add_argument("--schedule", choices=["auto", "onelaunch", "twokernel"], default="auto",
                     help="one-launch step, rows + draw kernels, or the library's choice")
     ap.add_argument("--profile-steps", type=int, default=200,
@@ -189,23 +232,26 @@ def main():
 
     from lossless_rejection_sampling_sampler_amd import SpecVerify, upload
     from lossless_rejection_sampling_sampler_amd._lib import SCHEDULE_NAMES, SV_SCHEDULE_ONE_LAUNCH
-    from synth import CONFIGS, make_config
 
-    spec = CONFIGS[CONFIG_ID]
-    log(f"[bench] generating {spec.name}")
-    inp = make_config(CONFIG_ID, replicate=args.seed_replicate)
+    log(f"[bench] generating workload {args.workload}")
+    inp = make_workload(args.workload, args.seed_replicate)
+    wl_text = WORKLOAD_TEXT[args.workload]
     dev = torch.device("cuda:0")
     log("[bench] uploading, rotate=%d" % args.rotate)
     base = upload(logits=inp.logits, logits_dtype=inp.dtype, draft_probs=inp.draft_probs,
                   draft_ids=inp.draft_ids, temperature=inp.temperature, uniforms=inp.uniforms,
-                  gamma=inp.gamma, draft_offsets=inp.offsets, device=dev)
+                  gamma=inp.gamma, draft_offsets=inp.offsets, device=dev,
+                  topk_ids=inp.topk_ids, topk_probs=inp.topk_probs)
     copies = [base]
     for _ in range(args.rotate - 1):
-        c = upload(logits=inp.logits[:1], logits_dtype=inp.dtype, draft_probs=inp.draft_probs[:1],
+        c = upload(logits=inp.logits[:1], logits_dtype=inp.dtype,
+                   draft_probs=None if inp.draft_probs is None else inp.draft_probs[:1],
                    draft_ids=inp.draft_ids, temperature=inp.temperature, uniforms=inp.uniforms,
-                   gamma=inp.gamma, draft_offsets=inp.offsets, device=dev)
+                   gamma=inp.gamma, draft_offsets=inp.offsets, device=dev,
+                   topk_ids=inp.topk_ids, topk_probs=inp.topk_probs)
         c.target_logits = base.target_logits.clone()
-        c.draft_probs = base.draft_probs.clone()
+        if base.draft_probs is not None:
+            c.draft_probs = base.draft_probs.clone()
         copies.append(c)
     torch.cuda.synchronize()
 
@@ -292,8 +338,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16 in; f32 exp + f64 sums; f64 draw",
         "data": "synthetic (seeded; shapes of the pages' gamma=5, T=0.8 deployment)",
-        "config": {"workload": f"verify step {spec.name}: B=64, gamma=5, V=151936, bf16 logits, "
-                               "fp32 q, T=0.8", "batch": inp.batch, "gamma": inp.gamma,
+        "config": {"workload": f"verify step {inp.name}: {wl_text}", "batch": inp.batch, "gamma": inp.gamma,
                    "vocab": inp.vocab, "rotating_input_sets": len(copies)},
         "hbm_gbps": round(step_gbps, 1),
         "frac_of_peak": round(step_gbps / PEAK_HBM_GBPS, 4),
@@ -306,7 +351,8 @@ def main():
                        "bonus_draws": int((sampled & (num == gam)).sum())},
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbps, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(kernel_gbps / PEAK_HBM_GBPS, 4),
-                     "kernel": kname, "bytes_per_launch": kbytes, "traffic": traffic_entry(kname)},
+                     "kernel": kname, "bytes_per_launch": kbytes,
+                     "traffic": traffic_entry(kname) if args.workload == "config3" else None},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")

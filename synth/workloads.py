@@ -286,14 +286,14 @@ SPARSE_TOPK = 50
 def make_sparse_config(replicate: int = 0, **overrides) -> VerifyInputs:
     """B=256, ragged gamma_b, V=128256, bf16, T=1, every request's q top-50
     sparse-renormalised and stored as 50 (id, prob) entries per draft row."""
-    spec = CONFIGS[5].with_(q_mode="topk", name="B256_ragged8_V128256_bf16_top50list", **overrides)
+    spec = CONFIGS[5].with_(q_mode="topk", name="B256_ragged8_V128256_bf16_top50", **overrides)
     return to_sparse(make_inputs(spec, seed=5100 + replicate), SPARSE_TOPK, seed=5100 + replicate)
 
 
 def make_point_config(replicate: int = 0, **overrides) -> VerifyInputs:
     """B=64, gamma=5, V=151936, bf16, T=0.8 with point-mass drafts: each drafted
     token is the argmax of the noisy draft logits, proposed with certainty."""
-    spec = CONFIGS[3].with_(q_mode="argmax", name="B64_g5_V151936_bf16_point", **overrides)
+    spec = CONFIGS[3].with_(q_mode="argmax", name="B64_g5_V151936_bf16_argmax", **overrides)
     return to_point(make_inputs(spec, seed=3100 + replicate))
 
 
