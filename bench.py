@@ -43,6 +43,8 @@ def make_workload(name: str, rep: int):
     from synth import make_config, make_point_config, make_sparse_config
     if name == "config3":
         return make_config(CONFIG_ID, replicate=rep)
+    if name in ("config4", "config5"):
+        return make_config(int(name[-1]), replicate=rep)
     if name == "sparse":
         return make_sparse_config(replicate=rep)
     if name == "sparse_as_dense":
@@ -58,6 +60,8 @@ def make_workload(name: str, rep: int):
 
 WORKLOAD_TEXT = {
     "config3": "B=64, gamma=5, V=151936, bf16 logits, fp32 q, T=0.8",
+    "config4": "B=128, gamma=8, V=151936, bf16 logits, fp32 q, T mix {0, 0.3, 0.7, 1}",
+    "config5": "B=256, ragged gamma_b in 0..8, V=128256, bf16 logits, half q = p, half top-50 dense q, T=1",
     "sparse": "B=256, ragged gamma_b in 0..8, V=128256, bf16 logits, top-50 q as 50 (id, prob) entries per row, T=1",
     "sparse_as_dense": "B=256, ragged gamma_b in 0..8, V=128256, bf16 logits, top-50 q in dense fp32 rows, T=1",
     "point": "B=64, gamma=5, V=151936, bf16 logits, point-mass drafts (no q memory), T=0.8",

@@ -18,7 +18,7 @@ namespace {
 
 constexpr int kRowVecsPerThread = 8;    // target 16-byte vectors per thread per row split
 constexpr int kProfileRing = 2048;      // calls between forced event folds
-constexpr int kDrawBlocksPerWave = 2;   // draw kernel: blocks per wave (the kernel takes at most 2)
+constexpr int kDrawBlocksPerWave = 2;   // draw kernel: blocks per wave in straight-line code
 constexpr int kStepSlices = 1;          // one-launch step: request slices
 constexpr int kDrawPerCU = 3;           // draw kernel: workgroups per CU aimed at
 
@@ -292,13 +292,22 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
     P.vocab = a->vocab;
     P.splits = ctx->geo.splits;
     P.nblocks = ctx->geo.nblocks;
-    // draw workgroups per request: three per CU over the call where that keeps
-    // between one and kDrawBlocksPerWave (the most a draw wave takes) blocks per
-    // wave; an even count per CU balances the fp64 work across the SIMDs
+    // draw workgroups per request: three per CU over the call (one resident
+    // round) where that keeps between one and kDrawBlocksPerWave blocks per
+    // wave (an even count per CU balances the fp64 work across the SIMDs).  A
+    // call with more draw rows than that round can hold at two blocks per wave
+    // (B = 128 or 256 at V = 151936 / 128256) takes a second round of
+    // workgroups when its residual blocks stream a dense q row too; with sparse
+    // or point-mass q (every block streams logits only, so a workgroup's
+    // fixed latency outweighs its bytes) its waves take pairs of blocks in a
+    // loop instead (measured: 100 against 110 us at B = 256 with top-50 lists,
+    // 114 against 109 us with dense q)
     const int c_min = std::max(1, (ctx->geo.nblocks + sv::kWaves * kDrawBlocksPerWave - 1) /
                                       (sv::kWaves * kDrawBlocksPerWave));
     const int c_max = std::max(1, (ctx->geo.nblocks + sv::kWaves - 1) / sv::kWaves);
-    const int C = std::max(c_min, std::min(c_max, kDrawPerCU * ctx->cus / a->batch));
+    const int c_fit = kDrawPerCU * ctx->cus / a->batch;
+    const bool draw_loop = c_fit < c_min && qmode != sv::kQDense;
+    const int C = draw_loop ? std::max(1, c_fit) : std::max(c_min, std::min(c_max, c_fit));
     P.draw_wgs = C;
     P.parts = ctx->parts;
     P.rows = ctx->rows;
@@ -369,10 +378,17 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
                 hipLaunchKernelGGL(sv::rows_split_kernel<sv::F32>, dim3((unsigned)grid1), dim3(sv::kThreads), 0, stream, P);
         }
         if (prof && hipEventRecord(ev[1], stream) != hipSuccess) return SV_ERR_DEVICE;
-        if (cfg.logits_dtype == SV_BF16)
-            hipLaunchKernelGGL(sv::draw_kernel<sv::BF16>, dim3((unsigned)grid2), dim3(sv::kThreads), 0, stream, P);
-        else
-            hipLaunchKernelGGL(sv::draw_kernel<sv::F32>, dim3((unsigned)grid2), dim3(sv::kThreads), 0, stream, P);
+        if (cfg.logits_dtype == SV_BF16) {
+            if (draw_loop)
+                hipLaunchKernelGGL((sv::draw_kernel<sv::BF16, true>), dim3((unsigned)grid2), dim3(sv::kThreads), 0, stream, P);
+            else
+                hipLaunchKernelGGL((sv::draw_kernel<sv::BF16, false>), dim3((unsigned)grid2), dim3(sv::kThreads), 0, stream, P);
+        } else {
+            if (draw_loop)
+                hipLaunchKernelGGL((sv::draw_kernel<sv::F32, true>), dim3((unsigned)grid2), dim3(sv::kThreads), 0, stream, P);
+            else
+                hipLaunchKernelGGL((sv::draw_kernel<sv::F32, false>), dim3((unsigned)grid2), dim3(sv::kThreads), 0, stream, P);
+        }
     }
     if (prof) {
         if (hipEventRecord(ev[2], stream) != hipSuccess) return SV_ERR_DEVICE;

@@ -1742,7 +1742,9 @@ struct DrawShared {
     int flag;
 };
 
-template <typename E>
+// kLoop: waves may hold more than two blocks (taken two at a time in a loop);
+// otherwise the grid gives every wave at most two blocks (checked by the host).
+template <typename E, bool kLoop>
 __global__ __launch_bounds__(kThreads, 4) void draw_kernel(Params P) {
     __shared__ DrawShared sh;
 
@@ -1766,8 +1768,7 @@ __global__ __launch_bounds__(kThreads, 4) void draw_kernel(Params P) {
     init_draw_row<E>(d, P, tk.kind, tk.row, tk.drow, tk.pos, tk.v, tk.m, tk.z32, T);
     __syncthreads();
     BlockRec* recs = P.recs + (size_t)b * NB;
-    // the grid gives every wave at most two blocks (checked by the host)
-    draw_blocks<E, true>(d, P.vocab, recs, c * kWaves + (tid >> 6), C * kWaves, NB, sh.tab);
+    draw_blocks<E, !kLoop>(d, P.vocab, recs, c * kWaves + (tid >> 6), C * kWaves, NB, sh.tab);
     wait_stores();                 // every wave's record stores complete before the arrival
     __syncthreads();
     if (tid == 0) sh.flag = (arrive(&P.draw_cnt[b]) == static_cast<uint32_t>(C - 1));
