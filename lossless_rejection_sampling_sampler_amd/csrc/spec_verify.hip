@@ -54,6 +54,28 @@ int flat_workgroups(long nv, long vpr, int resident) {
     return static_cast<int>(std::max<long>(1, g));
 }
 
+// Rows kernel then draw kernel on `stream` (ev, when given, is recorded between them).
+template <typename E>
+int launch_rows_draw(bool resolve, bool loop, long grid1, long grid2, const sv::Params& P,
+                     hipStream_t stream, hipEvent_t ev) {
+    const dim3 g1((unsigned)grid1), g2((unsigned)grid2), blk(sv::kThreads);
+    if (resolve)
+        hipLaunchKernelGGL(sv::rows_flat_kernel<E>, g1, blk, 0, stream, P);
+    else
+        hipLaunchKernelGGL(sv::rows_split_kernel<E>, g1, blk, 0, stream, P);
+    if (ev && hipEventRecord(ev, stream) != hipSuccess) return SV_ERR_DEVICE;
+    if (resolve) {
+        if (loop) hipLaunchKernelGGL((sv::draw_kernel<E, true, true>), g2, blk, 0, stream, P);
+        else hipLaunchKernelGGL((sv::draw_kernel<E, false, true>), g2, blk, 0, stream, P);
+    } else {
+        if (loop) hipLaunchKernelGGL((sv::draw_kernel<E, true, false>), g2, blk, 0, stream, P);
+        else hipLaunchKernelGGL((sv::draw_kernel<E, false, false>), g2, blk, 0, stream, P);
+    }
+    return SV_OK;
+}
+
+static_assert(SV_MAX_GAMMA + 1 <= sv::kMaxReqRows, "a request's rows fit the draw kernel's resolve");
+
 }  // namespace
 
 struct sv_ctx {
@@ -320,6 +342,7 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
     P.task_tag = nullptr;
     P.epoch = 0;
     P.slices = 1;
+    P.rows_grid = 0;
 
     const long rows = (long)a->total_draft + a->batch;
     // rows start on 16-byte boundaries: stream the flattened rows in equal ranges
@@ -366,29 +389,16 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
     } else {
         const long grid1 = aligned ? flat_workgroups(P.flat_nv, P.flat_vpr, ctx->resident_flat) : rows * P.splits;
         const long grid2 = (long)a->batch * C;
-        if (aligned) {
-            if (cfg.logits_dtype == SV_BF16)
-                hipLaunchKernelGGL(sv::rows_flat_kernel<sv::BF16>, dim3((unsigned)grid1), dim3(sv::kThreads), 0, stream, P);
-            else
-                hipLaunchKernelGGL(sv::rows_flat_kernel<sv::F32>, dim3((unsigned)grid1), dim3(sv::kThreads), 0, stream, P);
-        } else {
-            if (cfg.logits_dtype == SV_BF16)
-                hipLaunchKernelGGL(sv::rows_split_kernel<sv::BF16>, dim3((unsigned)grid1), dim3(sv::kThreads), 0, stream, P);
-            else
-                hipLaunchKernelGGL(sv::rows_split_kernel<sv::F32>, dim3((unsigned)grid1), dim3(sv::kThreads), 0, stream, P);
-        }
-        if (prof && hipEventRecord(ev[1], stream) != hipSuccess) return SV_ERR_DEVICE;
-        if (cfg.logits_dtype == SV_BF16) {
-            if (draw_loop)
-                hipLaunchKernelGGL((sv::draw_kernel<sv::BF16, true>), dim3((unsigned)grid2), dim3(sv::kThreads), 0, stream, P);
-            else
-                hipLaunchKernelGGL((sv::draw_kernel<sv::BF16, false>), dim3((unsigned)grid2), dim3(sv::kThreads), 0, stream, P);
-        } else {
-            if (draw_loop)
-                hipLaunchKernelGGL((sv::draw_kernel<sv::F32, true>), dim3((unsigned)grid2), dim3(sv::kThreads), 0, stream, P);
-            else
-                hipLaunchKernelGGL((sv::draw_kernel<sv::F32, false>), dim3((unsigned)grid2), dim3(sv::kThreads), 0, stream, P);
-        }
+        P.rows_grid = static_cast<int>(grid1);
+        // aligned rows are streamed without any hand-off between workgroups and
+        // resolved by the draw kernel
+        const bool resolve = aligned;
+        const int st = (cfg.logits_dtype == SV_BF16)
+                           ? launch_rows_draw<sv::BF16>(resolve, draw_loop, grid1, grid2, P, stream,
+                                                        prof ? ev[1] : nullptr)
+                           : launch_rows_draw<sv::F32>(resolve, draw_loop, grid1, grid2, P, stream,
+                                                       prof ? ev[1] : nullptr);
+        if (st != SV_OK) return st;
     }
     if (prof) {
         if (hipEventRecord(ev[2], stream) != hipSuccess) return SV_ERR_DEVICE;

@@ -134,6 +134,7 @@ struct Params {
     long flat_nv;        // flat rows kernel: total 16-byte vectors
     long flat_vpr;       // flat rows kernel: vectors per row
     int draw_wgs;        // draw kernel: workgroups per request
+    int rows_grid;       // flat rows kernel: its grid (the piece geometry the draw kernel's resolve reads)
     int nblocks;         // draw blocks per row
     // scratch
     Piece* parts;        // [rows][kMaxPieces]
@@ -613,7 +614,10 @@ struct DraftTok {
 // The first batch of loads is issued before the request lookup, and the
 // drafted token's logit and q are read once the stream has been taken in, both
 // so that their round trips overlap other work.
-template <typename E>
+// kArrive = false (rows kernel whose merges are left to the next launch): no
+// arrival count; the piece is stored and, by the row's piece 0, the drafted
+// token's id, logit and q, for a later kernel to read.
+template <typename E, bool kArrive = true>
 __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0, long v1, int piece, int npieces,
                                                  RowShared& sh, DraftTok& dt) {
     const int tid = threadIdx.x;
@@ -644,7 +648,7 @@ __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0
     const bool greedy = !(T > 0.0f);
     const float c = greedy ? 0.0f : static_cast<float>(kLog2e / static_cast<double>(T));
     int xd = -1;
-    if (tid == 0 && !greedy && i < gb) xd = P.ids[rm.d0 + i];
+    if (tid == 0 && !greedy && i < gb && (kArrive || piece == 0)) xd = P.ids[rm.d0 + i];
 
     float mloc;          // piece max (sampled) / argmax value (greedy)
     int gloc = -1;       // argmax (greedy)
@@ -748,7 +752,15 @@ __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0
         st_coherent(&pp->m, mloc);
         st_coherent(&pp->g, gloc);
         st_coherent(&pp->z, zloc);
-        old = static_cast<int>(arrive(&P.row_cnt[t]));
+        if (kArrive) {
+            old = static_cast<int>(arrive(&P.row_cnt[t]));
+        } else if (piece == 0) {
+            RowStat* rp = &P.rows[t];
+            st_coherent(&rp->x, dt.x);
+            st_coherent(&rp->lx, dt.lx);
+            st_coherent(&rp->qx, dt.qx);
+            if (!greedy && i < gb && dt.x < 0) flag_error(P.err, kErrDraftId);
+        }
     }
     return old;
 }
@@ -969,18 +981,27 @@ __device__ __forceinline__ void rows_share(const Params& P, long r0, long r1, Pe
     }
 }
 
-// Aligned rows, all of them: one share per workgroup.
-template <typename E>
-__device__ __forceinline__ void rows_flat_range(const Params& P, RowShared& sh) {
-    PendingMerge pm;
-    rows_share<E>(P, 0, P.flat_nv / P.flat_vpr, pm, sh);
-    settle_merge<E>(P, pm, sh);
-}
-
+// Aligned rows, streamed only: every piece of this workgroup's range is stored
+// (and each row's drafted token by its piece 0); the merges, the accept tests
+// and the resolve are left to the draw kernel, which the launch boundary
+// orders after every store of this one.  No workgroup waits on another.
 template <typename E>
 __global__ __launch_bounds__(kThreads) void rows_flat_kernel(Params P) {
     __shared__ RowShared sh;
-    rows_flat_range<E>(P, sh);
+    const int w = blockIdx.x;
+    const int G = gridDim.x;
+    const long VPR = P.flat_vpr, NV = P.flat_nv;
+    const long a = (long)w * NV / G, e = (long)(w + 1) * NV / G;
+    long r = a / VPR;
+    for (long s0 = a; s0 < e; ++r) {
+        const long rs = r * VPR, re = rs + VPR;
+        const long s1 = e < re ? e : re;
+        const int wf = range_owner(rs, NV, G), wl = range_owner(re - 1, NV, G);
+        DraftTok dt;
+        row_piece_publish<E, false>(P, static_cast<int>(r), s0 - rs, s1 - rs, w - wf, wl - wf + 1, sh, dt);
+        __syncthreads();
+        s0 = s1;
+    }
 }
 
 // ----------------------------------------------------------------- draw blocks
@@ -1742,11 +1763,179 @@ struct DrawShared {
     int flag;
 };
 
+// ----------------------------------------------------------------- resolve in the draw kernel
+// After the stream-only rows kernel, every draw workgroup of request b rebuilds
+// the request's row statistics from the stored pieces, runs the accept tests
+// and finds the first rejection itself (a few hundred bytes of loads and a
+// handful of fp64 exponentials: cheaper than a hand-off between workgroups);
+// the request's workgroup 0 writes the outputs, except the drawn token, which
+// the select writes.
+constexpr int kMaxReqRows = 129;          // gamma_b + 1 rows of one request at most
+constexpr int kResolveChunk = 8;          // pieces a thread loads in one round
+
+struct ResolveShared {
+    float rm[kMaxReqRows];       // row max (sampled) / argmax value (greedy)
+    double rz[kMaxReqRows];      // row normaliser
+    int rej[kMaxReqRows];        // draft i rejected
+};
+
+// Uniform call.  Returns request b's draw task (kDrawNone: greedy, nothing to
+// draw, or an inconsistent layout, which is flagged); `writer` workgroups store
+// the outputs, counters and diagnostics.  Thread i owns row i of the request:
+// it loads the row's pieces and its draft's id, logit, q and uniform in one
+// round, merges the pieces and runs the accept test, so that a single barrier
+// publishes the rows' results.
+template <typename E>
+__device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool writer, float T, ResolveShared& rs) {
+    const int tid = threadIdx.x;
+    const int G = P.gamma;
+    DrawTask tk;
+    tk.kind = kDrawNone;
+    tk.row = tk.drow = tk.pos = 0;
+    tk.v = tk.m = 0.0f;
+    tk.z32 = 0.0;
+    int o0, o1;
+    if (P.offsets) {
+        o0 = P.offsets[b];
+        o1 = P.offsets[b + 1];
+    } else {
+        o0 = b * G;
+        o1 = o0 + G;
+    }
+    const int gb = o1 - o0;
+    if (!(o0 >= 0 && o1 <= P.total_draft && gb >= 0 && gb <= G && gb < kMaxReqRows)) {
+        if (writer && tid == 0) flag_error(P.err, kErrOffsets);
+        return tk;
+    }
+    const int t0 = o0 + b;
+    const bool greedy = !(T > 0.0f);
+    const double c = greedy ? 0.0 : static_cast<double>(static_cast<float>(kLog2e / static_cast<double>(T)));
+    const float v_res = P.uniforms[(size_t)b * (G + 2) + G];
+    const float v_bonus = P.uniforms[(size_t)b * (G + 2) + G + 1];
+    const bool owner = tid <= gb;
+    float M = -INFINITY;          // row max, or the argmax value
+    int g = 0x7fffffff;           // argmax
+    double Z = 0.0;
+    int xid = -1;
+    bool rej = false;
+    double r = 0.0;
+    if (owner) {
+        const int t = t0 + tid;
+        const long rsv = (long)t * P.flat_vpr;
+        const int np = range_owner(rsv + P.flat_vpr - 1, P.flat_nv, P.rows_grid) - range_owner(rsv, P.flat_nv, P.rows_grid) + 1;
+        int xs = -1;
+        float lx = 0.0f, qx = 0.0f, u = 0.0f;
+        if (tid < gb) {
+            xid = P.ids[o0 + tid];
+            if (!greedy) {
+                const RowStat* rp = &P.rows[t];
+                xs = ld_coherent(&rp->x);
+                lx = ld_coherent(&rp->lx);
+                qx = ld_coherent(&rp->qx);
+                u = P.uniforms[(size_t)b * (G + 2) + tid];
+            }
+        }
+        const Piece* pp = &P.parts[(size_t)t * kMaxPieces];
+        for (int p0 = 0; p0 < np; p0 += kResolveChunk) {
+            float mm[kResolveChunk];
+            int gg[kResolveChunk];
+            double zz[kResolveChunk];
+#pragma unroll
+            for (int q = 0; q < kResolveChunk; ++q) {
+                const bool in = p0 + q < np;
+                mm[q] = in ? ld_coherent(&pp[p0 + q].m) : -INFINITY;
+                gg[q] = in ? ld_coherent(&pp[p0 + q].g) : 0x7fffffff;
+                zz[q] = in ? ld_coherent(&pp[p0 + q].z) : 0.0;
+            }
+            if (!greedy) {
+                // the pieces' sums rescaled to the row max, in piece order
+                float Mc = M;
+#pragma unroll
+                for (int q = 0; q < kResolveChunk; ++q) Mc = fmaxf(Mc, mm[q]);
+                if (Mc > M && M > -INFINITY) Z *= exp2((static_cast<double>(M) - static_cast<double>(Mc)) * c);
+                M = Mc;
+#pragma unroll
+                for (int q = 0; q < kResolveChunk; ++q)
+                    if (mm[q] > -INFINITY) Z += zz[q] * exp2((static_cast<double>(mm[q]) - static_cast<double>(M)) * c);
+            } else {
+#pragma unroll
+                for (int q = 0; q < kResolveChunk; ++q) argmax_merge(M, g, mm[q], gg[q]);
+            }
+        }
+        // accept test (page section 5.2: q floored at 1e-10, strict "<")
+        if (tid < gb) {
+            bool acc;
+            if (greedy) {
+                acc = (xid == g);
+            } else {
+                const double invT = 1.0 / static_cast<double>(T);
+                const double px = exp((static_cast<double>(lx) - static_cast<double>(M)) * invT) / Z;
+                r = px / fmax(static_cast<double>(qx), kQFloor);
+                acc = (xs >= 0) && (static_cast<double>(u) < fmin(1.0, r));
+            }
+            rej = !acc;
+        }
+        rs.rm[tid] = M;
+        rs.rz[tid] = Z;
+        rs.rej[tid] = rej ? 1 : 0;
+    }
+    __syncthreads();
+    // k = the first rejected draft (every wave finds the same)
+    const int lane = tid & 63;
+    int k = gb;
+    for (int base = 0; base < gb; base += 64) {
+        const unsigned long long m = __ballot(base + lane < gb && rs.rej[base + lane] != 0);
+        if (m != 0ull) {
+            k = base + __ffsll(static_cast<long long>(m)) - 1;
+            break;
+        }
+    }
+    if (writer) {
+        if (owner) {
+            if (P.diag_m) P.diag_m[t0 + tid] = M;
+            if (P.diag_z) P.diag_z[t0 + tid] = greedy ? 0.0 : Z;
+            if (tid < gb && P.diag_r) P.diag_r[o0 + tid] = greedy ? __uint_as_float(0x7fc00000u) : static_cast<float>(r);
+        }
+        if (tid <= G) {
+            int tok = -1;
+            if (tid < k) tok = xid;
+            else if (tid == k && greedy) tok = g;
+            // the drawn token's slot is the select's (another workgroup of this launch)
+            if (!(tid == k && !greedy)) P.out_tokens[(size_t)b * (G + 1) + tid] = tok;
+        }
+        if (tid == 0) P.out_num[b] = k;
+        if (P.stats) {
+            uint32_t* S = P.stats;
+            if (tid == 0) {
+                count_add(&S[0], 1u);
+                count_add(&S[1], static_cast<uint32_t>(gb));
+                count_add(&S[2], static_cast<uint32_t>(k));
+                if (k == gb) count_add(&S[3], 1u);
+                count_add(&S[4 + k], 1u);
+            }
+            if (tid < gb && tid <= k) count_add(&S[5 + G + tid], 1u);
+            if (tid < k) count_add(&S[5 + 2 * G + tid], 1u);
+        }
+    }
+    if (greedy) return tk;
+    tk.kind = k < gb ? kDrawResidual : kDrawBonus;
+    tk.row = t0 + k;
+    tk.drow = o0 + k;
+    tk.pos = k;
+    tk.v = k < gb ? v_res : v_bonus;
+    tk.m = rs.rm[k];
+    tk.z32 = rs.rz[k];
+    return tk;
+}
+
 // kLoop: waves may hold more than two blocks (taken two at a time in a loop);
 // otherwise the grid gives every wave at most two blocks (checked by the host).
-template <typename E, bool kLoop>
+// kResolve: the rows kernel only streamed (rows_flat_kernel): the request is
+// resolved here; otherwise the draw task left by the rows kernel's resolve is read.
+template <typename E, bool kLoop, bool kResolve>
 __global__ __launch_bounds__(kThreads, 4) void draw_kernel(Params P) {
     __shared__ DrawShared sh;
+    __shared__ ResolveShared rsh;
 
     const int tid = threadIdx.x;
     const int C = P.draw_wgs;
@@ -1754,11 +1943,18 @@ __global__ __launch_bounds__(kThreads, 4) void draw_kernel(Params P) {
     const int c = blockIdx.x - b * C;
     const int NB = P.nblocks;
 
-    // the task, the temperature and the exponential table in one round of loads
+    // the task (or the request's inputs), the temperature and the exponential
+    // table in one round of loads
     const double tv = kExp2Table[tid];
-    const DrawTask tk = P.tasks[b];
     const float T = P.temperature[b];
-    sh.tab[tid] = tv;
+    DrawTask tk;
+    if (kResolve) {
+        sh.tab[tid] = tv;
+        tk = resolve_request<E>(P, b, c == 0, T, rsh);
+    } else {
+        tk = P.tasks[b];
+        sh.tab[tid] = tv;
+    }
     if (tk.kind == kDrawNone) return;
     const bool residual = (tk.kind == kDrawResidual);
     if (tk.row < 0 || tk.row >= P.total_draft + P.batch || tk.pos < 0 || tk.pos > P.gamma ||
@@ -1778,7 +1974,7 @@ __global__ __launch_bounds__(kThreads, 4) void draw_kernel(Params P) {
     const int y = draw_select_wg<E>(d, P.vocab, NB, recs, sh.tab, P.err, sh.sel);
     if (tid == 0) {
         P.out_tokens[(size_t)b * (P.gamma + 1) + tk.pos] = y;
-        P.tasks[b].kind = kDrawNone;               // consumed: a stale task is never replayed
+        if (!kResolve) P.tasks[b].kind = kDrawNone;   // consumed: a stale task is never replayed
     }
 }
 
