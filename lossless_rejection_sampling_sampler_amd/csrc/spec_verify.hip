@@ -86,6 +86,7 @@ struct sv_ctx {
     int resident_flat = 0;     // rows-flat workgroups resident at once on the device
     int cus = 0;               // compute units of the device
     int resident_step = 0;     // one-launch workgroups resident at once
+    int resident_draw = 0;     // draw workgroups resident at once
     uint32_t epoch = 0;        // tag of the one-launch step's draw tasks
     int last_schedule = SV_SCHEDULE_NONE;
     uint32_t* task_tag = nullptr;
@@ -196,6 +197,10 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
         ctx->resident_flat = std::max(1, cus * std::min(3, std::max(1, per_cu)));
         ctx->cus = std::max(1, cus);
 
+        int per_draw = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_draw, sv::draw_kernel<sv::BF16, false, true>,
+                                                         sv::kThreads, 0) == hipSuccess)
+            ctx->resident_draw = cus * per_draw;
         int per_bf16 = 0, per_f32 = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_bf16, sv::step_kernel<sv::BF16>, sv::kThreads, 0) ==
                 hipSuccess &&
@@ -343,6 +348,7 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
     P.epoch = 0;
     P.slices = 1;
     P.rows_grid = 0;
+    P.draw_cmajor = 0;
 
     const long rows = (long)a->total_draft + a->batch;
     // rows start on 16-byte boundaries: stream the flattened rows in equal ranges
@@ -390,6 +396,7 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
         const long grid1 = aligned ? flat_workgroups(P.flat_nv, P.flat_vpr, ctx->resident_flat) : rows * P.splits;
         const long grid2 = (long)a->batch * C;
         P.rows_grid = static_cast<int>(grid1);
+        P.draw_cmajor = grid2 <= ctx->resident_draw ? 1 : 0;
         // aligned rows are streamed without any hand-off between workgroups and
         // resolved by the draw kernel
         const bool resolve = aligned;

@@ -134,6 +134,7 @@ struct Params {
     long flat_nv;        // flat rows kernel: total 16-byte vectors
     long flat_vpr;       // flat rows kernel: vectors per row
     int draw_wgs;        // draw kernel: workgroups per request
+    int draw_cmajor;     // draw kernel: workgroup w serves request w % batch (else w / draw_wgs)
     int rows_grid;       // flat rows kernel: its grid (the piece geometry the draw kernel's resolve reads)
     int nblocks;         // draw blocks per row
     // scratch
@@ -1939,8 +1940,12 @@ __global__ __launch_bounds__(kThreads, 4) void draw_kernel(Params P) {
 
     const int tid = threadIdx.x;
     const int C = P.draw_wgs;
-    const int b = blockIdx.x / C;
-    const int c = blockIdx.x - b * C;
+    // a grid that is resident in one round is dispatched piece-index-major, so
+    // that the workgroups holding the most blocks (low c) start first and the
+    // lightest last (a CU serves its older workgroups first); a larger grid is
+    // request-major, so that early requests finish while later ones wait for slots
+    const int b = P.draw_cmajor ? static_cast<int>(blockIdx.x % P.batch) : static_cast<int>(blockIdx.x / C);
+    const int c = P.draw_cmajor ? static_cast<int>(blockIdx.x / P.batch) : static_cast<int>(blockIdx.x - b * C);
     const int NB = P.nblocks;
 
     // the task (or the request's inputs), the temperature and the exponential
