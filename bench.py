@@ -320,12 +320,20 @@ def main():
     rows_avg_ms, draw_avg_ms = rows_ms / n_prof, draw_ms / n_prof
     svp.close()
 
+    def roofline(kname, kbytes, kms):
+        gbps = kbytes / (kms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(gbps / PEAK_HBM_GBPS, 4), "kernel": kname, "bytes_per_launch": kbytes,
+                "avg_launch_ms": round(kms, 6),
+                "traffic": traffic_entry(kname) if args.workload == "config3" else None}
+
     if svp_schedule == SV_SCHEDULE_ONE_LAUNCH:
         # one kernel does the whole step: its bytes are the step's
-        kname, kbytes = f"step_kernel<{KDT}>", step_bytes
+        lines = [roofline(f"step_kernel<{KDT}>", step_bytes, rows_avg_ms)]
     else:
-        kname, kbytes = f"rows_flat_kernel<{KDT}>", rows_b
-    kernel_gbps = kbytes / (rows_avg_ms * 1e-3) / 1e9
+        lines = [roofline(f"rows_flat_kernel<{KDT}>", rows_b, rows_avg_ms),
+                 roofline(f"draw_kernel<{KDT}>", draw_b, draw_avg_ms)]
+    dominant = max(lines, key=lambda r: r["avg_launch_ms"])
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     sampled = inp.temperature > 0
     gam = inp.gammas
@@ -353,10 +361,8 @@ def main():
         "acceptance": {"mean_accepted": float(num.mean()),
                        "residual_draws": int((sampled & (num < gam)).sum()),
                        "bonus_draws": int((sampled & (num == gam)).sum())},
-        "roofline": {"bound": "hbm", "achieved": round(kernel_gbps, 1), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(kernel_gbps / PEAK_HBM_GBPS, 4),
-                     "kernel": kname, "bytes_per_launch": kbytes,
-                     "traffic": traffic_entry(kname) if args.workload == "config3" else None},
+        "roofline": dominant,
+        "roofline_per_kernel": lines,
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
