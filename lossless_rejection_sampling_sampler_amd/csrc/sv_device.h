@@ -1829,10 +1829,12 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
         if (tid < gb) {
             xid = P.ids[o0 + tid];
             if (!greedy) {
+                // stored by the rows kernel: the launch boundary orders those
+                // stores before these plain loads
                 const RowStat* rp = &P.rows[t];
-                xs = ld_coherent(&rp->x);
-                lx = ld_coherent(&rp->lx);
-                qx = ld_coherent(&rp->qx);
+                xs = rp->x;
+                lx = rp->lx;
+                qx = rp->qx;
                 u = P.uniforms[(size_t)b * (G + 2) + tid];
             }
         }
@@ -1844,9 +1846,9 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
 #pragma unroll
             for (int q = 0; q < kResolveChunk; ++q) {
                 const bool in = p0 + q < np;
-                mm[q] = in ? ld_coherent(&pp[p0 + q].m) : -INFINITY;
-                gg[q] = in ? ld_coherent(&pp[p0 + q].g) : 0x7fffffff;
-                zz[q] = in ? ld_coherent(&pp[p0 + q].z) : 0.0;
+                mm[q] = in ? pp[p0 + q].m : -INFINITY;
+                gg[q] = in ? pp[p0 + q].g : 0x7fffffff;
+                zz[q] = in ? pp[p0 + q].z : 0.0;
             }
             if (!greedy) {
                 // the pieces' sums rescaled to the row max, in piece order
