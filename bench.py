@@ -51,6 +51,9 @@ def make_workload(name: str, rep: int):
         return _sparse_as_dense(rep)
     if name == "point":
         return make_point_config(replicate=rep)
+    if name == "sample":
+        from synth import make_sample_config
+        return make_sample_config(replicate=rep)
     if name == "point_as_dense":
         from synth.workloads import CONFIGS, make_inputs
         return make_inputs(CONFIGS[3].with_(q_mode="argmax", name="B64_g5_V151936_bf16_argmax_dense"),
@@ -66,6 +69,7 @@ WORKLOAD_TEXT = {
     "sparse_as_dense": "B=256, ragged gamma_b in 0..8, V=128256, bf16 logits, top-50 q in dense fp32 rows, T=1",
     "point": "B=64, gamma=5, V=151936, bf16 logits, point-mass drafts (no q memory), T=0.8",
     "point_as_dense": "B=64, gamma=5, V=151936, bf16 logits, point-mass drafts as one-hot dense fp32 q rows, T=0.8",
+    "sample": "draft-side sampling: B=64 rows, gamma=0, V=151936, bf16 logits, T=0.8",
 }
 
 

@@ -16,6 +16,7 @@ from .workloads import (  # noqa: F401
     make_inputs,
     make_config,
     make_point_config,
+    make_sample_config,
     make_sparse_config,
     to_point,
     to_sparse,

@@ -297,6 +297,17 @@ def make_point_config(replicate: int = 0, **overrides) -> VerifyInputs:
     return to_point(make_inputs(spec, seed=3100 + replicate))
 
 
+def make_sample_config(replicate: int = 0, batch: int = 64, vocab: int = 151936, dtype: str = "bf16",
+                       temperature: float = 0.8) -> VerifyInputs:
+    """Draft-side sampling x ~ softmax(l / T): one row of draft logits per request
+    and no drafts to verify (gamma = 0), so the verify step's bonus draw is the
+    categorical sample.  Logits ~ N(0, 3^2) with 8 peaks of +8 (the recipe of
+    the B=64 workload); the sample's uniform is column 1 of [B, 2]."""
+    spec = CONFIGS[3].with_(batch=batch, gamma=0, vocab=vocab, dtype=dtype, temperatures=(temperature,),
+                            name=f"B{batch}_V{vocab}_{dtype}_sample")
+    return make_inputs(spec, seed=3200 + replicate)
+
+
 def make_config(n: int, replicate: int = 0, **overrides) -> VerifyInputs:
     """Inputs for workload configuration ``n`` (1..5); seed = 1000 * n + replicate."""
     spec = CONFIGS[n]

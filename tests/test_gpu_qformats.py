@@ -110,3 +110,24 @@ def test_bad_sparse_entries_set_error_word(schedule):
     assert sv.device_errors(clear=True) & SV_DEVERR_TOPK
     tok, num = res[0]
     assert np.all((tok >= -1) & (tok < 3000)) and np.all((num >= 0) & (num <= inp.gamma))
+
+
+# ---------------------------------------------------------------- draft-side sampling
+@pytest.mark.parametrize("schedule", SCHEDULES)
+@pytest.mark.parametrize("kw", [dict(batch=16, vocab=9001, dtype="f32"), dict(batch=40, vocab=16384),
+                                dict(batch=8, vocab=1001)], ids=["f32_ragged", "bf16_aligned", "bf16_oddV"])
+def test_small_sample_parity(kw, schedule):
+    from synth import make_sample_config
+    inp = make_sample_config(replicate=5, **kw)
+    sets = [inp.uniforms] + [uniforms_from_seed(inp.uniforms.shape, 80 + s) for s in range(15)]
+    rep, errs, _ = parity_check(inp, sets, label=f"sample {kw}", schedule=schedule)
+    _assert_ok(rep, errs)
+
+
+def test_full_sample_parity():
+    from synth import make_sample_config
+    inp = make_sample_config()
+    log(f"[full-sample] {inp.name} B={inp.batch} V={inp.vocab} sets=313")
+    sets = [inp.uniforms] + [uniforms_from_seed(inp.uniforms.shape, 900 + s) for s in range(312)]
+    rep, errs, _ = parity_check(inp, sets, label="sample-full")
+    _assert_ok(rep, errs, min_requests=20000)

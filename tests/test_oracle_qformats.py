@@ -135,3 +135,24 @@ def test_acceptance_stats_invariants():
     # a tested draft is accepted or is the request's first rejection
     rejected_at = np.bincount(k[k < gam], minlength=G)[:G]
     assert np.array_equal(tested - accepted, rejected_at)
+
+
+def test_draft_side_sampling_is_categorical():
+    """With gamma = 0 the step is a batched categorical draw from softmax(l / T)
+    (the draft-side sampler x ~ q of the spec-decoding page's section 3.1): on a
+    dyadic p and an exact 64-point stratified grid the sampled law is p."""
+    p = np.array([0.5, 0.25, 0.125, 0.0625, 0.0625])
+    V, N = 5, 64
+    grid = (np.arange(N) + 0.5) / N
+    logits = np.broadcast_to(np.log(p), (N, 1, V)).astype(np.float32)
+    u = np.stack([np.zeros(N), grid], axis=1)
+    o = oracle.verify(explicit_inputs(logits, np.zeros((N, 0, V)), np.zeros((N, 0), int), np.ones(N), u))
+    assert np.all(o.num_accepted == 0) and np.all(o.draw_kind == 2)
+    assert np.array_equal(np.bincount(o.tokens[:, 0], minlength=V) / N, p)
+
+
+def test_sample_workload_builds():
+    from synth import make_sample_config
+    s = make_sample_config(batch=3, vocab=777)
+    assert s.gamma == 0 and s.total_draft == 0 and s.uniforms.shape == (3, 2)
+    assert np.all(oracle.verify(s).tokens[:, 0] >= 0)
