@@ -554,7 +554,10 @@ __device__ __forceinline__ void accumulate_batch(const float* f, float c, float&
 }
 
 // Argmax over one loaded batch (vectors jb .. jb + kRowUnroll - 1 of this
-// thread's n), element indices counted from the row start.
+// thread's n), element indices counted from the row start.  A thread visits its
+// elements in increasing index order, so a strictly greater value is the only
+// one that replaces the running argmax (the lowest index wins a tie); the
+// reductions across lanes and pieces break ties by index.
 template <typename E>
 __device__ __forceinline__ void argmax_batch(const v4u* buf, int jb, int n, long first, int head, float& bv, int& bi) {
 #pragma unroll
@@ -564,7 +567,11 @@ __device__ __forceinline__ void argmax_batch(const v4u* buf, int jb, int n, long
         const int x0 = head + static_cast<int>((first + (long)(jb + u) * kThreads) * E::kPerVec);
         if (jb + u < n) {
 #pragma unroll
-            for (int k = 0; k < E::kPerVec; ++k) argmax_merge(bv, bi, f[k], x0 + k);
+            for (int k = 0; k < E::kPerVec; ++k) {
+                const bool gt = f[k] > bv;
+                bv = gt ? f[k] : bv;
+                bi = gt ? x0 + k : bi;
+            }
         }
     }
 }
@@ -710,8 +717,10 @@ __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0
             zs = st * exp2(static_cast<double>(kref) - static_cast<double>(mloc) * static_cast<double>(c));
         zloc = wg_sum(zs, sh.red);
     } else {
+        // a thread with elements starts at its first one, so that a piece of
+        // -inf logits still reports its lowest index (as a tie-breaking merge would)
         float bv = -INFINITY;
-        int bi = 0x7fffffff;
+        int bi = n > 0 ? head + static_cast<int>(first * E::kPerVec) : 0x7fffffff;
         dt.x = -1;
         // two batches at a time, as in the sampled stream
         v4u Bf[kRowUnroll];

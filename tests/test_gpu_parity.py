@@ -121,3 +121,29 @@ def test_full_workload_each_schedule(n, schedule):
     sets = [inp.uniforms] + [uniforms_from_seed(inp.uniforms.shape, 500 + s) for s in range(19)]
     rep, errs, _ = parity_check(inp, sets, label=f"config{n}-{schedule}", schedule=schedule)
     _assert_ok(rep, errs)
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES)
+@pytest.mark.parametrize("dtype,V", [("f32", 50000), ("bf16", 60000), ("bf16", 1001)])
+def test_greedy_ties_and_all_neg_inf_rows(dtype, V, schedule):
+    """Greedy rows: a row of -inf logits gives index 0, and a maximum repeated far
+    apart (other threads and pieces) gives its lowest index."""
+    from synth.workloads import f32_to_bf16_bits
+    from tests.helpers import explicit_inputs
+    rng = np.random.default_rng(11)
+    B, g = 4, 2
+    l = rng.normal(0.0, 1.0, size=(B, g + 1, V)).astype(np.float32)
+    l[0, 0, :] = -np.inf                          # request 0: draft 0 = argmax 0 is accepted
+    l[1, :, [3, V // 2, V - 2]] = 9.0             # three-way tie on every row of request 1
+    l[2, 1, :] = -np.inf
+    l[3, 0, [V - 1, 0]] = 9.0
+    ids = np.array([[0, 5], [3, V // 2], [int(l[2, 0].argmax()), 0], [0, 1]])
+    u = np.zeros((B, g + 2), dtype=np.float32)
+    inp = explicit_inputs(l, np.zeros((B, g, V)), ids, np.zeros(B), u)
+    if dtype == "bf16":
+        inp.logits = f32_to_bf16_bits(inp.logits)
+        inp.dtype = "bf16"
+    log(f"[greedy-ties] dtype={dtype} V={V} schedule={schedule}")
+    rep, errs, _ = parity_check(inp, label="greedy-ties", schedule=schedule)
+    _assert_ok(rep, errs)
+    assert rep.mismatched == 0
