@@ -1796,7 +1796,8 @@ struct ResolveShared {
 // round, merges the pieces and runs the accept test, so that a single barrier
 // publishes the rows' results.
 template <typename E>
-__device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool writer, float T, ResolveShared& rs) {
+__device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool writer, float T, ResolveShared& rs,
+                                                   const double* tab) {
     const int tid = threadIdx.x;
     const int G = P.gamma;
     DrawTask tk;
@@ -1819,7 +1820,11 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
     }
     const int t0 = o0 + b;
     const bool greedy = !(T > 0.0f);
-    const double c = greedy ? 0.0 : static_cast<double>(static_cast<float>(kLog2e / static_cast<double>(T)));
+    // 256 times the pieces' scale log2(e) / T as the rows kernel rounded it
+    // (exact), and 256 log2(e) / T for the accept ratio: exponentials by the
+    // same table-based exp2 as the draw weights
+    const double c256 = greedy ? 0.0 : 256.0 * static_cast<double>(static_cast<float>(kLog2e / static_cast<double>(T)));
+    const double c2 = greedy ? 0.0 : 256.0 * (kLog2e / static_cast<double>(T));
     const float v_res = P.uniforms[(size_t)b * (G + 2) + G];
     const float v_bonus = P.uniforms[(size_t)b * (G + 2) + G + 1];
     const bool owner = tid <= gb;
@@ -1829,12 +1834,16 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
     int xid = -1;
     bool rej = false;
     double r = 0.0;
+    int xs = -1, np = 0;
+    float lx = 0.0f, qx = 0.0f, u = 0.0f;
+    const Piece* pp = nullptr;
+    float mm[kResolveChunk];
+    int gg[kResolveChunk];
+    double zz[kResolveChunk];
     if (owner) {
         const int t = t0 + tid;
         const long rsv = (long)t * P.flat_vpr;
-        const int np = range_owner(rsv + P.flat_vpr - 1, P.flat_nv, P.rows_grid) - range_owner(rsv, P.flat_nv, P.rows_grid) + 1;
-        int xs = -1;
-        float lx = 0.0f, qx = 0.0f, u = 0.0f;
+        np = range_owner(rsv + P.flat_vpr - 1, P.flat_nv, P.rows_grid) - range_owner(rsv, P.flat_nv, P.rows_grid) + 1;
         if (tid < gb) {
             xid = P.ids[o0 + tid];
             if (!greedy) {
@@ -1847,41 +1856,54 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
                 u = P.uniforms[(size_t)b * (G + 2) + tid];
             }
         }
-        const Piece* pp = &P.parts[(size_t)t * kMaxPieces];
-        for (int p0 = 0; p0 < np; p0 += kResolveChunk) {
-            float mm[kResolveChunk];
-            int gg[kResolveChunk];
-            double zz[kResolveChunk];
+        pp = &P.parts[(size_t)t * kMaxPieces];
 #pragma unroll
-            for (int q = 0; q < kResolveChunk; ++q) {
-                const bool in = p0 + q < np;
-                mm[q] = in ? pp[p0 + q].m : -INFINITY;
-                gg[q] = in ? pp[p0 + q].g : 0x7fffffff;
-                zz[q] = in ? pp[p0 + q].z : 0.0;
+        for (int q = 0; q < kResolveChunk; ++q) {
+            const bool in = q < np;
+            mm[q] = in ? pp[q].m : -INFINITY;
+            gg[q] = in ? pp[q].g : 0x7fffffff;
+            zz[q] = in ? pp[q].z : 0.0;
+        }
+    }
+    // publishes the exponential table (stored to LDS by the caller); the loads
+    // above are complete after it
+    __syncthreads();
+    if (owner) {
+        for (int p0 = 0; p0 < np; p0 += kResolveChunk) {
+            if (p0 > 0) {
+#pragma unroll
+                for (int q = 0; q < kResolveChunk; ++q) {
+                    const bool in = p0 + q < np;
+                    mm[q] = in ? pp[p0 + q].m : -INFINITY;
+                    gg[q] = in ? pp[p0 + q].g : 0x7fffffff;
+                    zz[q] = in ? pp[p0 + q].z : 0.0;
+                }
             }
             if (!greedy) {
                 // the pieces' sums rescaled to the row max, in piece order
                 float Mc = M;
 #pragma unroll
                 for (int q = 0; q < kResolveChunk; ++q) Mc = fmaxf(Mc, mm[q]);
-                if (Mc > M && M > -INFINITY) Z *= exp2((static_cast<double>(M) - static_cast<double>(Mc)) * c);
+                if (Mc > M && M > -INFINITY)
+                    Z *= exp2_256((static_cast<double>(M) - static_cast<double>(Mc)) * c256, tab);
                 M = Mc;
 #pragma unroll
                 for (int q = 0; q < kResolveChunk; ++q)
-                    if (mm[q] > -INFINITY) Z += zz[q] * exp2((static_cast<double>(mm[q]) - static_cast<double>(M)) * c);
+                    if (mm[q] > -INFINITY)
+                        Z += zz[q] * exp2_256((static_cast<double>(mm[q]) - static_cast<double>(M)) * c256, tab);
             } else {
 #pragma unroll
                 for (int q = 0; q < kResolveChunk; ++q) argmax_merge(M, g, mm[q], gg[q]);
             }
         }
-        // accept test (page section 5.2: q floored at 1e-10, strict "<")
+        // accept test (page section 5.2: q floored at 1e-10, strict "<"); p(x)
+        // by the draw weights' own expression
         if (tid < gb) {
             bool acc;
             if (greedy) {
                 acc = (xid == g);
             } else {
-                const double invT = 1.0 / static_cast<double>(T);
-                const double px = exp((static_cast<double>(lx) - static_cast<double>(M)) * invT) / Z;
+                const double px = exp2_256(fma(static_cast<double>(lx), c2, -(static_cast<double>(M) * c2)), tab) / Z;
                 r = px / fmax(static_cast<double>(qx), kQFloor);
                 acc = (xs >= 0) && (static_cast<double>(u) < fmin(1.0, r));
             }
@@ -1966,7 +1988,7 @@ __global__ __launch_bounds__(kThreads, 4) void draw_kernel(Params P) {
     DrawTask tk;
     if (kResolve) {
         sh.tab[tid] = tv;
-        tk = resolve_request<E>(P, b, c == 0, T, rsh);
+        tk = resolve_request<E>(P, b, c == 0, T, rsh, sh.tab);
     } else {
         tk = P.tasks[b];
         sh.tab[tid] = tv;
