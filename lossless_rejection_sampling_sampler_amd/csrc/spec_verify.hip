@@ -56,21 +56,16 @@ int flat_workgroups(long nv, long vpr, int resident) {
 
 // Rows kernel then draw kernel on `stream` (ev, when given, is recorded between them).
 template <typename E>
-int launch_rows_draw(bool resolve, bool loop, long grid1, long grid2, const sv::Params& P,
-                     hipStream_t stream, hipEvent_t ev) {
+int launch_rows_draw(bool aligned, bool loop, long grid1, long grid2, const sv::Params& P, hipStream_t stream,
+                     hipEvent_t ev) {
     const dim3 g1((unsigned)grid1), g2((unsigned)grid2), blk(sv::kThreads);
-    if (resolve)
+    if (aligned)
         hipLaunchKernelGGL(sv::rows_flat_kernel<E>, g1, blk, 0, stream, P);
     else
         hipLaunchKernelGGL(sv::rows_split_kernel<E>, g1, blk, 0, stream, P);
     if (ev && hipEventRecord(ev, stream) != hipSuccess) return SV_ERR_DEVICE;
-    if (resolve) {
-        if (loop) hipLaunchKernelGGL((sv::draw_kernel<E, true, true>), g2, blk, 0, stream, P);
-        else hipLaunchKernelGGL((sv::draw_kernel<E, false, true>), g2, blk, 0, stream, P);
-    } else {
-        if (loop) hipLaunchKernelGGL((sv::draw_kernel<E, true, false>), g2, blk, 0, stream, P);
-        else hipLaunchKernelGGL((sv::draw_kernel<E, false, false>), g2, blk, 0, stream, P);
-    }
+    if (loop) hipLaunchKernelGGL((sv::draw_kernel<E, true>), g2, blk, 0, stream, P);
+    else hipLaunchKernelGGL((sv::draw_kernel<E, false>), g2, blk, 0, stream, P);
     return SV_OK;
 }
 
@@ -198,7 +193,7 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
         ctx->cus = std::max(1, cus);
 
         int per_draw = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_draw, sv::draw_kernel<sv::BF16, false, true>,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_draw, sv::draw_kernel<sv::BF16, false>,
                                                          sv::kThreads, 0) == hipSuccess)
             ctx->resident_draw = cus * per_draw;
         int per_bf16 = 0, per_f32 = 0;
@@ -348,6 +343,7 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
     P.epoch = 0;
     P.slices = 1;
     P.rows_grid = 0;
+    P.split_pieces = 0;
     P.draw_cmajor = 0;
 
     const long rows = (long)a->total_draft + a->batch;
@@ -397,13 +393,14 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
         const long grid2 = (long)a->batch * C;
         P.rows_grid = static_cast<int>(grid1);
         P.draw_cmajor = grid2 <= ctx->resident_draw ? 1 : 0;
-        // aligned rows are streamed without any hand-off between workgroups and
-        // resolved by the draw kernel
-        const bool resolve = aligned;
+        // rows are streamed without any hand-off between workgroups (flattened
+        // ranges for 16-byte aligned rows, per-row splits otherwise) and every
+        // request is resolved by its draw workgroups
+        P.split_pieces = aligned ? 0 : P.splits;
         const int st = (cfg.logits_dtype == SV_BF16)
-                           ? launch_rows_draw<sv::BF16>(resolve, draw_loop, grid1, grid2, P, stream,
+                           ? launch_rows_draw<sv::BF16>(aligned, draw_loop, grid1, grid2, P, stream,
                                                         prof ? ev[1] : nullptr)
-                           : launch_rows_draw<sv::F32>(resolve, draw_loop, grid1, grid2, P, stream,
+                           : launch_rows_draw<sv::F32>(aligned, draw_loop, grid1, grid2, P, stream,
                                                        prof ? ev[1] : nullptr);
         if (st != SV_OK) return st;
     }

@@ -13,25 +13,28 @@
 //                and sum of exp2((l - m) * log2(e) / T) (fp32 exponentials summed
 //                into fp64), or a running argmax for greedy rows; reduces across
 //                the 64-wide waves with DPP lane moves and across the four waves
-//                through LDS, and writes one partial per (row, piece).  When
-//                rows are 16-byte aligned the flattened [rows x vocab] stream is
-//                cut into equal contiguous ranges, one per workgroup (a range
-//                covers pieces of one or two rows); otherwise each row is cut
-//                into equal splits with scalar head/tail handling.  The last
-//                piece of a row to finish merges the pieces; the last row of a
-//                request to finish runs that request's accept tests, finds the
-//                first rejection, writes the outputs and leaves a draw task.
-//   draw kernel  streams the one draw row of every sampled request (residual
-//                (p - q)_+ or bonus p) in fp64, one 2048-token block per wave,
-//                and records per-block sums; the first wave of the last
-//                workgroup of the request rebuilds the exact fp64 normaliser,
-//                picks the block holding v * S with a block scan, rescans that
-//                block token by token and writes the token.
+//                through LDS, and stores one partial per (row, piece), plus the
+//                row's drafted token (id, logit, q) from its piece 0.  When rows
+//                are 16-byte aligned the flattened [rows x vocab] stream is cut
+//                into equal contiguous ranges, one per workgroup (a range covers
+//                pieces of one or two rows); otherwise each row is cut into equal
+//                splits with scalar head/tail handling.  No workgroup waits on
+//                another: the launch boundary orders these stores before the
+//                draw kernel.
+//   draw kernel  every workgroup of a request first resolves it: thread i merges
+//                row i's pieces, runs its accept test, and the first rejection k
+//                is found with a ballot; workgroup 0 writes the outputs.  Then the
+//                draw row of a sampled request (residual (p - q)_+ at k, or bonus
+//                p) is streamed in fp64, one or two 2048-token blocks per wave,
+//                with per-block sums; the last workgroup of the request rebuilds
+//                the exact fp64 normaliser, picks the block holding v * S by a
+//                block scan, rescans that block token by token and writes the
+//                token.
 //
-// Cross-workgroup hand-off uses per-row / per-request arrival counters; see
-// the note at wait_stores().  Counters are reset by their last arrival (rows,
-// draws) or by the draw kernel (requests), so every call leaves the scratch
-// ready for the next.
+// An opt-in one-launch schedule (step_kernel) merges and resolves rows inside
+// the same launch through per-row / per-request arrival counters; see the note
+// at wait_stores().  Its counters are reset by their last arrival, so every call
+// leaves the scratch ready for the next.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -136,6 +139,7 @@ struct Params {
     int draw_wgs;        // draw kernel: workgroups per request
     int draw_cmajor;     // draw kernel: workgroup w serves request w % batch (else w / draw_wgs)
     int rows_grid;       // flat rows kernel: its grid (the piece geometry the draw kernel's resolve reads)
+    int split_pieces;    // split rows kernel: pieces per row (0: the flat geometry)
     int nblocks;         // draw blocks per row
     // scratch
     Piece* parts;        // [rows][kMaxPieces]
@@ -931,10 +935,8 @@ __global__ __launch_bounds__(kThreads) void rows_split_kernel(Params P) {
     if (head > V) head = V;
     const long nvec = (V - head) / E::kPerVec;
     DraftTok dt;
-    const int old = row_piece_publish<E>(P, t, (long)s * nvec / S, (long)(s + 1) * nvec / S, s, S, sh, dt);
-    if (threadIdx.x == 0) sh.flag = (old == S - 1);
-    __syncthreads();
-    if (sh.flag) row_merge<E>(P, t, S, dt, sh);
+    // pieces only: the draw kernel merges and resolves (P.split_pieces = S)
+    row_piece_publish<E, false>(P, t, (long)s * nvec / S, (long)(s + 1) * nvec / S, s, S, sh, dt);
 }
 
 // Workgroup owning vector v when nv vectors are cut into g equal ranges
@@ -991,7 +993,7 @@ __device__ __forceinline__ void rows_share(const Params& P, long r0, long r1, Pe
     }
 }
 
-// Aligned rows, streamed only: every piece of this workgroup's range is stored
+// Rows streamed only: every piece of this workgroup's range is stored
 // (and each row's drafted token by its piece 0); the merges, the accept tests
 // and the resolve are left to the draw kernel, which the launch boundary
 // orders after every store of this one.  No workgroup waits on another.
@@ -1842,8 +1844,12 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
     double zz[kResolveChunk];
     if (owner) {
         const int t = t0 + tid;
-        const long rsv = (long)t * P.flat_vpr;
-        np = range_owner(rsv + P.flat_vpr - 1, P.flat_nv, P.rows_grid) - range_owner(rsv, P.flat_nv, P.rows_grid) + 1;
+        if (P.split_pieces > 0) {
+            np = P.split_pieces;
+        } else {
+            const long rsv = (long)t * P.flat_vpr;
+            np = range_owner(rsv + P.flat_vpr - 1, P.flat_nv, P.rows_grid) - range_owner(rsv, P.flat_nv, P.rows_grid) + 1;
+        }
         if (tid < gb) {
             xid = P.ids[o0 + tid];
             if (!greedy) {
@@ -1964,9 +1970,8 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
 
 // kLoop: waves may hold more than two blocks (taken two at a time in a loop);
 // otherwise the grid gives every wave at most two blocks (checked by the host).
-// kResolve: the rows kernel only streamed (rows_flat_kernel): the request is
-// resolved here; otherwise the draw task left by the rows kernel's resolve is read.
-template <typename E, bool kLoop, bool kResolve>
+// The rows kernel only streamed: every workgroup first resolves its request.
+template <typename E, bool kLoop>
 __global__ __launch_bounds__(kThreads, 4) void draw_kernel(Params P) {
     __shared__ DrawShared sh;
     __shared__ ResolveShared rsh;
@@ -1985,14 +1990,8 @@ __global__ __launch_bounds__(kThreads, 4) void draw_kernel(Params P) {
     // table in one round of loads
     const double tv = kExp2Table[tid];
     const float T = P.temperature[b];
-    DrawTask tk;
-    if (kResolve) {
-        sh.tab[tid] = tv;
-        tk = resolve_request<E>(P, b, c == 0, T, rsh, sh.tab);
-    } else {
-        tk = P.tasks[b];
-        sh.tab[tid] = tv;
-    }
+    sh.tab[tid] = tv;
+    const DrawTask tk = resolve_request<E>(P, b, c == 0, T, rsh, sh.tab);
     if (tk.kind == kDrawNone) return;
     const bool residual = (tk.kind == kDrawResidual);
     if (tk.row < 0 || tk.row >= P.total_draft + P.batch || tk.pos < 0 || tk.pos > P.gamma ||
@@ -2012,7 +2011,6 @@ __global__ __launch_bounds__(kThreads, 4) void draw_kernel(Params P) {
     const int y = draw_select_wg<E>(d, P.vocab, NB, recs, sh.tab, P.err, sh.sel);
     if (tid == 0) {
         P.out_tokens[(size_t)b * (P.gamma + 1) + tk.pos] = y;
-        if (!kResolve) P.tasks[b].kind = kDrawNone;   // consumed: a stale task is never replayed
     }
 }
 
