@@ -147,3 +147,25 @@ def test_greedy_ties_and_all_neg_inf_rows(dtype, V, schedule):
     rep, errs, _ = parity_check(inp, label="greedy-ties", schedule=schedule)
     _assert_ok(rep, errs)
     assert rep.mismatched == 0
+
+
+# Few rows over a large vocabulary: rows are cut into more pieces than the draw
+# kernel's resolve loads in one round (8), on the flat path (aligned rows) and
+# on the split path (odd V, 19 pieces per row).
+MANY_PIECES = [
+    ("B1_g4_V151936_bf16", dict(n=3, batch=1, gamma=4)),          # ~20 pieces per row
+    ("B2_g8_V65536_f32", dict(n=2, batch=2, gamma=8, vocab=65536)),  # ~16 pieces per row
+    ("B3_g2_V300001_bf16_split", dict(n=3, batch=3, gamma=2, vocab=300001)),
+    ("B2_T_mix_V151936", dict(n=4, batch=2, gamma=3)),            # greedy rows with many pieces
+]
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES)
+@pytest.mark.parametrize("name,kw", MANY_PIECES, ids=[m[0] for m in MANY_PIECES])
+def test_rows_with_many_pieces(name, kw, schedule):
+    kw = dict(kw)
+    n = kw.pop("n")
+    inp = make_config(n, replicate=9, **kw)
+    sets = [inp.uniforms] + [uniforms_from_seed(inp.uniforms.shape, 300 + s) for s in range(31)]
+    rep, errs, _ = parity_check(inp, sets, label=name, schedule=schedule)
+    _assert_ok(rep, errs)
