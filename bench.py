@@ -43,7 +43,7 @@ def make_workload(name: str, rep: int):
     from synth import make_config, make_point_config, make_sparse_config
     if name == "config3":
         return make_config(CONFIG_ID, replicate=rep)
-    if name in ("config4", "config5"):
+    if name in ("config1", "config2", "config4", "config5"):
         return make_config(int(name[-1]), replicate=rep)
     if name == "sparse":
         return make_sparse_config(replicate=rep)
@@ -63,6 +63,8 @@ def make_workload(name: str, rep: int):
 
 WORKLOAD_TEXT = {
     "config3": "B=64, gamma=5, V=151936, bf16 logits, fp32 q, T=0.8",
+    "config1": "B=1, gamma=4, V=1000, fp32 logits, fp32 q, T=1",
+    "config2": "B=8, gamma=5, V=32000, fp32 logits, fp32 q, T=1",
     "config4": "B=128, gamma=8, V=151936, bf16 logits, fp32 q, T mix {0, 0.3, 0.7, 1}",
     "config5": "B=256, ragged gamma_b in 0..8, V=128256, bf16 logits, half q = p, half top-50 dense q, T=1",
     "sparse": "B=256, ragged gamma_b in 0..8, V=128256, bf16 logits, top-50 q as 50 (id, prob) entries per row, T=1",
