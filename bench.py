@@ -219,6 +219,9 @@ def main():
                          "formats are for comparison runs")
     ap.add_argument("--schedule", choices=["auto", "onelaunch", "twokernel"], default="auto",
                     help="one-launch step, rows + draw kernels, or the library's choice")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from a captured HIP graph (one call per replay, "
+                         "input sets rotating) and report it as graph_steps_per_s")
     ap.add_argument("--profile-steps", type=int, default=200,
                     help="steps of the per-kernel HIP-event timing pass")
     ap.add_argument("--pmc-workload", action="store_true",
@@ -300,6 +303,31 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
 
+    graph_rate = None
+    if args.graph:
+        # one captured call per input set; replays cycle through them
+        graphs = []
+        for i in range(len(packed)):
+            gph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gph):
+                # launched on the capture stream torch has made current
+                st = sv.run_args(packed[i], torch.cuda.current_stream().cuda_stream)
+                if st:
+                    raise RuntimeError(f"spec_verify_run failed with status {st} under capture")
+            graphs.append(gph)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for i in range(args.steps):
+            graphs[i % len(graphs)].replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_rate = 1000.0 * args.steps / g0.elapsed_time(g1)
+
     sv_schedule = sv.last_schedule()
     if args.pmc_workload:
         log(f"[bench] counter workload done: {args.warmup + args.steps} steps")
@@ -367,6 +395,7 @@ def main():
         "acceptance": {"mean_accepted": float(num.mean()),
                        "residual_draws": int((sampled & (num < gam)).sum()),
                        "bonus_draws": int((sampled & (num == gam)).sum())},
+        "graph_steps_per_s": None if graph_rate is None else round(graph_rate, 2),
         "roofline": dominant,
         "roofline_per_kernel": lines,
     }

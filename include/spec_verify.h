@@ -193,7 +193,12 @@ int spec_verify_create(const sv_config *cfg, int device, sv_ctx **out);
  * and returns without waiting.  Host-visible arguments are checked first; on a
  * non-SV_OK status nothing is enqueued.  Outputs are valid once the stream has
  * reached this point.  The call allocates nothing.  One context must not be
- * used by two streams at the same time (its scratch is per call). */
+ * used by two streams at the same time (its scratch is per call).  Without
+ * SV_FLAG_ONE_LAUNCH or SV_FLAG_PROFILE the call only launches kernels whose
+ * arrival counters reset themselves, so it may be captured in a HIP graph and
+ * replayed (the buffers' contents may change between replays; their addresses
+ * and the sizes may not).  The one-launch schedule tags each call's draw tasks
+ * with a host-side epoch, which a replay would repeat: do not capture it. */
 int spec_verify_run(sv_ctx *ctx, const sv_args *args, void *stream);
 
 /* Frees the context and its scratch after synchronising its device.  NULL is a
