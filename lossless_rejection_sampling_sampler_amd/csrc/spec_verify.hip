@@ -38,10 +38,10 @@ Geometry geometry_for(int vocab, int dtype) {
     return g;
 }
 
-// Workgroups for the flat rows kernel: all resident at once, at least one batch
-// of loads per thread or else one workgroup per row (a small call is
-// latency-bound: its rows' merge chains then run side by side), and no row cut
-// into more than kMaxPieces pieces.
+// Workgroups for the flat rows stream (and the one-launch step): all resident at
+// once, at least one batch of loads per thread or else one workgroup per row (a
+// small call is latency-bound: its rows then stream side by side), and no row
+// cut into more than kMaxPieces pieces.
 int flat_workgroups(long nv, long vpr, int resident) {
     const long rows = vpr > 0 ? nv / vpr : 1;
     long g = std::min<long>(resident, std::max<long>(rows, nv / ((long)sv::kThreads * sv::kRowUnroll)));

@@ -2022,9 +2022,9 @@ __global__ __launch_bounds__(kThreads, 4) void draw_kernel(Params P) {
 // 0's rows, then of slice 1's, then takes its share of slice 0's draw blocks,
 // then slice 2's rows, slice 1's draw blocks, and so on: the fp64 draw work of
 // early requests runs beside the memory-bound stream of later ones, and only the
-// last slice's draws are left once the stream ends.  Merges and resolves work
-// as in the rows kernel; a resolve publishes its request's draw task with this
-// call's epoch, and a wave waits only for the task of the request whose blocks
+// last slice's draws are left once the stream ends.  The last piece of a row
+// to arrive merges the row (row_merge) and the last row of a request resolves
+// it; a resolve publishes its request's draw task with this call's epoch, and a wave waits only for the task of the request whose blocks
 // it holds.  The wave that lands a request's last block record runs that
 // request's select.
 constexpr int kPhaseSpinLimit = 1 << 20;   // bounded wait for a draw task (seconds)
