@@ -2004,10 +2004,12 @@ __global__ __launch_bounds__(kThreads, 4) void draw_kernel(Params P) {
     draw_blocks<E, !kLoop>(d, P.vocab, recs, c * kWaves + (tid >> 6), C * kWaves, NB, sh.tab);
     wait_stores();                 // every wave's record stores complete before the arrival
     __syncthreads();
-    if (tid == 0) sh.flag = (arrive(&P.draw_cnt[b]) == static_cast<uint32_t>(C - 1));
-    __syncthreads();
-    if (!sh.flag) return;
-    if (tid == 0) reset_counter(&P.draw_cnt[b]);
+    if (C > 1) {                   // (a request's only workgroup selects without arriving)
+        if (tid == 0) sh.flag = (arrive(&P.draw_cnt[b]) == static_cast<uint32_t>(C - 1));
+        __syncthreads();
+        if (!sh.flag) return;
+        if (tid == 0) reset_counter(&P.draw_cnt[b]);
+    }
     const int y = draw_select_wg<E>(d, P.vocab, NB, recs, sh.tab, P.err, sh.sel);
     if (tid == 0) {
         P.out_tokens[(size_t)b * (P.gamma + 1) + tk.pos] = y;
