@@ -99,7 +99,7 @@ def log(msg):
 
 
 def algorithmic_bytes(inp, num_accepted):
-    """Bytes the method must move for one step (see the measurement section of the design doc).
+    """Bytes the method must move for one step (bytes it avoids are not counted).
 
     rows kernel: every target row once, the drafted-token gathers (id, logit and
     q: one value of a dense q row, the K (id, prob) entries of a sparse row, none

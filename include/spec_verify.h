@@ -60,7 +60,7 @@ enum sv_status {
     SV_ERR_INVALID_ARG = 1,    /* a host-visible argument violates the contract */
     SV_ERR_OUT_OF_MEMORY = 2,  /* device allocation failed in spec_verify_create */
     SV_ERR_DEVICE = 3,         /* a HIP call failed (launch, event, copy) */
-    SV_ERR_UNSUPPORTED = 4,    /* dtype / size outside what this build handles */
+    SV_ERR_UNSUPPORTED = 4,    /* dtype / size outside what the library handles */
     SV_ERR_CAPACITY = 5        /* batch, gamma or vocab exceed the context's limits */
 };
 

@@ -26,7 +26,7 @@ Source of the method: the spec-decoding page at dpshk.com/news/5598276
 * [page §6.2] the serving log reports the draft acceptance rate and the
   accepted tokens per step (acceptance_stats counts what these are made of).
 
-Readings where the page is silent (each listed with its reason in the design doc):
+Readings where the page is silent:
 temperature enters as softmax(l / T) with the max over the raw logits; T <= 0
 or NaN selects the greedy variant (argmax of the raw logits, lowest index on
 ties); uniforms arrive as an input of shape [B, gamma+2] whose columns

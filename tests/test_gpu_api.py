@@ -1,4 +1,4 @@
-"""Host-side contract of the C ABI, exercised on the GPU machine: argument checks,
+"""Host-side contract of the C ABI, exercised on a GPU: argument checks,
 status codes, no-op batches, the sticky device-error word, profiling."""
 
 import ctypes
