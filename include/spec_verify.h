@@ -185,8 +185,10 @@ typedef struct sv_ctx sv_ctx;    /* opaque; owns the device scratch of one strea
 /* Creates a context on HIP device `device` and allocates its scratch (row
  * statistics, counters, draw records) for cfg's limits.  On success *out
  * holds the context (free it with spec_verify_destroy).  Returns
- * SV_ERR_INVALID_ARG for bad limits, SV_ERR_OUT_OF_MEMORY / SV_ERR_DEVICE on
- * HIP failure (then *out is NULL). */
+ * SV_ERR_INVALID_ARG for bad limits, SV_ERR_UNSUPPORTED for a dtype, vocab or
+ * row count (max_batch * (max_gamma + 1) above 2^31 - 1) the library does not
+ * handle, SV_ERR_OUT_OF_MEMORY / SV_ERR_DEVICE on HIP failure (then *out is
+ * NULL). */
 int spec_verify_create(const sv_config *cfg, int device, sv_ctx **out);
 
 /* Enqueues one verify step on `stream` (a hipStream_t; NULL = default stream)

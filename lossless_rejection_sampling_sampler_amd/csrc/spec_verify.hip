@@ -170,6 +170,8 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
         return SV_ERR_INVALID_ARG;
     if (cfg->logits_dtype != SV_F32 && cfg->logits_dtype != SV_BF16) return SV_ERR_UNSUPPORTED;
     if ((long)cfg->vocab > (long)sv::kMaxDrawBlocks * sv::kBlockElems) return SV_ERR_UNSUPPORTED;
+    // row indices are 32-bit: max_batch * (max_gamma + 1) target rows must fit
+    if ((long)cfg->max_batch * ((long)cfg->max_gamma + 1) > (long)INT32_MAX) return SV_ERR_UNSUPPORTED;
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev) return SV_ERR_DEVICE;
 

@@ -38,6 +38,11 @@ def test_create_argument_checks():
         assert lib.spec_verify_create(ctypes.byref(cfg), 0, ctypes.byref(h)) == 1
         assert not h.value
     assert lib.spec_verify_create(ctypes.byref(SVConfig(4, 4, 100, 7, 0)), 0, ctypes.byref(h)) == 4
+    # row counts beyond 32-bit indices are refused; scratch beyond the device's memory fails cleanly
+    assert lib.spec_verify_create(ctypes.byref(SVConfig(1 << 24, 128, 100, 1, 0)), 0, ctypes.byref(h)) == 4
+    assert not h.value
+    assert lib.spec_verify_create(ctypes.byref(SVConfig(1 << 22, 128, 100, 1, 0)), 0, ctypes.byref(h)) == 2
+    assert not h.value
     assert lib.spec_verify_create(ctypes.byref(SVConfig(4, 4, 100, 1, 0)), 99, ctypes.byref(h)) == 3
     assert lib.spec_verify_destroy(None) == 0
 
