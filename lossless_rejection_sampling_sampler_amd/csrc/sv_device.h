@@ -1968,11 +1968,13 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
     return tk;
 }
 
-// kLoop: waves may hold more than two blocks (taken two at a time in a loop);
-// otherwise the grid gives every wave at most two blocks (checked by the host).
-// The rows kernel only streamed: every workgroup first resolves its request.
+// kLoop: waves may hold more than two blocks (taken two at a time in a loop;
+// such grids hold at most three workgroups per CU, so the register budget is
+// that of three); otherwise the grid gives every wave at most two blocks
+// (checked by the host).  The rows kernel only streamed: every workgroup first
+// resolves its request.
 template <typename E, bool kLoop>
-__global__ __launch_bounds__(kThreads, 4) void draw_kernel(Params P) {
+__global__ __launch_bounds__(kThreads, kLoop ? 3 : 4) void draw_kernel(Params P) {
     __shared__ DrawShared sh;
     __shared__ ResolveShared rsh;
 
