@@ -51,6 +51,8 @@ def make_workload(name: str, rep: int):
         return _sparse_as_dense(rep)
     if name == "point":
         return make_point_config(replicate=rep)
+    if name == "shard4":
+        return make_config(CONFIG_ID, replicate=rep, vocab=151936 // 4, name="B64_g5_V37984_bf16_shard")
     if name == "sample":
         from synth import make_sample_config
         return make_sample_config(replicate=rep)
@@ -72,6 +74,7 @@ WORKLOAD_TEXT = {
     "point": "B=64, gamma=5, V=151936, bf16 logits, point-mass drafts (no q memory), T=0.8",
     "point_as_dense": "B=64, gamma=5, V=151936, bf16 logits, point-mass drafts as one-hot dense fp32 q rows, T=0.8",
     "sample": "draft-side sampling: B=64 rows, gamma=0, V=151936, bf16 logits, T=0.8",
+    "shard4": "one vocabulary shard of four: B=64, gamma=5, V=37984, bf16 logits, fp32 q, T=0.8",
 }
 
 
