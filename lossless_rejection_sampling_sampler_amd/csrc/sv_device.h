@@ -400,6 +400,8 @@ struct RedScratch {
     float f[kWaves];
     double d[kWaves];
     int i[kWaves];
+    int o0, o1;          // map_row: the found request's offsets and temperature,
+    float T;             // passed on by the thread that loaded them
 };
 
 __device__ __forceinline__ float wg_max(float v, RedScratch& s) {
@@ -491,6 +493,7 @@ __device__ __forceinline__ double wg_inclusive_scan(double v, double& total, Red
 struct RowMap {
     int b, i, gb, d0;
     bool ok;
+    float T;             // the request's temperature
 };
 
 __device__ __forceinline__ RowMap map_row(const Params& P, int t, RedScratch& red) {
@@ -501,22 +504,56 @@ __device__ __forceinline__ RowMap map_row(const Params& P, int t, RedScratch& re
         r.gb = P.gamma;
         r.d0 = r.b * P.gamma;
         r.ok = true;
+        r.T = P.temperature[r.b];
         return r;
     }
-    // request b starts at target row offsets[b] + b: count the starts <= t
-    int cnt = 0;
-    for (int j = threadIdx.x; j < P.batch; j += kThreads) cnt += (P.offsets[j] + j <= t);
-    const int b = wg_sum_int(cnt, red) - 1;
+    // Request b starts at target row offsets[b] + b: count the starts <= t.  In
+    // the same round of loads each thread keeps the offsets and temperature of
+    // the last request whose start it counted; the thread that counted b's start
+    // passes them on through LDS between the sum's two barriers, so no second
+    // round trip follows.  With inconsistent offsets no thread may own b: the
+    // sentinel then fails the checks below.
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (threadIdx.x == 0) red.o0 = -1;
+    int cnt = 0, jmax = -1, oj0 = 0, oj1 = 0;
+    float tj = 0.0f;
+    for (int j = threadIdx.x; j < P.batch; j += kThreads) {
+        const int o = P.offsets[j];
+        const int on = P.offsets[j + 1];
+        const float tt = P.temperature[j];
+        if (o + j <= t) {
+            ++cnt;
+            jmax = j;
+            oj0 = o;
+            oj1 = on;
+            tj = tt;
+        }
+    }
+    cnt = wave_sum_int(cnt);
+    if (lane == 0) red.i[w] = cnt;
+    __syncthreads();
+    int total = 0;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) total += red.i[k];
+    const int b = total - 1;
+    if (jmax >= 0 && jmax == b) {
+        red.o0 = oj0;
+        red.o1 = oj1;
+        red.T = tj;
+    }
+    __syncthreads();
+    const int o0 = red.o0, o1 = red.o1;
     r.b = b;
-    r.ok = false;
-    r.i = r.gb = r.d0 = 0;
-    if (b < 0 || b >= P.batch) return r;
-    const int o0 = P.offsets[b], o1 = P.offsets[b + 1];
+    r.T = red.T;
     r.gb = o1 - o0;
     r.d0 = o0;
     r.i = t - (o0 + b);
-    r.ok = (o0 >= 0) && (o1 <= P.total_draft) && (r.gb >= 0) && (r.gb <= P.gamma) &&
-           (r.i >= 0) && (r.i <= r.gb);
+    r.ok = (b >= 0) && (b < P.batch) && (o0 >= 0) && (o1 <= P.total_draft) && (r.gb >= 0) &&
+           (r.gb <= P.gamma) && (r.i >= 0) && (r.i <= r.gb);
+    // uniform: a failing caller returns at once, and this barrier keeps the
+    // fields above from being overwritten by its next lookup before every
+    // thread has read them (a passing caller reduces over the workgroup first)
+    if (!r.ok) __syncthreads();
     return r;
 }
 
@@ -656,7 +693,7 @@ __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0
         return -1;
     }
     const int b = rm.b, i = rm.i, gb = rm.gb;
-    const float T = P.temperature[b];
+    const float T = rm.T;
     const bool greedy = !(T > 0.0f);
     const float c = greedy ? 0.0f : static_cast<float>(kLog2e / static_cast<double>(T));
     int xd = -1;
@@ -788,7 +825,7 @@ __device__ __forceinline__ void row_merge(const Params& P, int t, int npieces, c
     const RowMap rm = map_row(P, t, sh.red);
     if (!rm.ok) return;
     const int b = rm.b, i = rm.i, gb = rm.gb;
-    const float T = P.temperature[b];
+    const float T = rm.T;
     const bool greedy = !(T > 0.0f);
     const float c = greedy ? 0.0f : static_cast<float>(kLog2e / static_cast<double>(T));
     if (tid == 0) reset_counter(&P.row_cnt[t]);
