@@ -105,16 +105,17 @@ def test_out_of_range_draft_id_sets_error_word(schedule):
 
 
 @pytest.mark.parametrize("schedule", SCHEDULES)
-def test_bad_offsets_set_error_word_without_faulting(schedule):
+@pytest.mark.parametrize("batch,bad", [(8, 3), (300, 270)])   # 300: a thread counts two starts
+def test_bad_offsets_set_error_word_without_faulting(schedule, batch, bad):
     from lossless_rejection_sampling_sampler_amd._lib import SV_DEVERR_OFFSETS
-    inp = make_config(5, replicate=1, vocab=600, batch=8)
-    inp.offsets[3] = inp.offsets[4] + 3      # gamma_3 negative, gamma_4 too large
-    log(f"[api] inconsistent offsets, schedule={schedule}")
+    inp = make_config(5, replicate=1, vocab=600, batch=batch)
+    inp.offsets[bad] = inp.offsets[bad + 1] + 3    # gamma_bad negative
+    log(f"[api] inconsistent offsets B={batch} at {bad}, schedule={schedule}")
     res, _, sv = run_gpu(inp, diag=False, schedule=schedule)
     assert sv.device_errors(clear=True) & SV_DEVERR_OFFSETS
     assert sv.device_errors() == 0
     # a following valid call on the same context is exact again
-    good = make_config(5, replicate=1, vocab=600, batch=8)
+    good = make_config(5, replicate=1, vocab=600, batch=batch)
     res2, _, _ = run_gpu(good, sv=sv)
     res3, _, _ = run_gpu(good, schedule=schedule)
     assert np.array_equal(res2[0][0], res3[0][0]) and np.array_equal(res2[0][1], res3[0][1])

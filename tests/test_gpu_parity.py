@@ -37,6 +37,10 @@ SMALL = [
     ("c1_tinyV_aligned", dict(n=1, vocab=8, batch=33)),             # one 32-byte row: one piece
     ("c3_aligned", dict(n=3, vocab=16384, batch=32)),
     ("c5_aligned", dict(n=5, vocab=4096, batch=64)),                # ragged, gamma_b = 0, q = p
+    # more requests than a workgroup has threads: a thread counts several request
+    # starts in the row-to-request lookup
+    ("c5_wide", dict(n=5, vocab=520, batch=600)),
+    ("c5_wide_oddV", dict(n=5, vocab=517, batch=300)),
 ]
 
 

@@ -33,6 +33,7 @@ SMALL = [
     ("sparse", make_sparse_config, dict(vocab=9001, batch=40)),          # ragged tail block
     ("sparse_oddV", make_sparse_config, dict(vocab=4099, batch=24)),     # rows not 16-byte aligned
     ("sparse_aligned", make_sparse_config, dict(vocab=16384, batch=32)),
+    ("sparse_wide", make_sparse_config, dict(vocab=1024, batch=520)),   # > 256 ragged requests
     ("point", make_point_config, dict(vocab=9001, batch=24)),
     ("point_oddV", make_point_config, dict(vocab=1001, batch=16)),
     ("point_aligned", make_point_config, dict(vocab=16384, batch=16)),
