@@ -257,32 +257,34 @@ __device__ __forceinline__ DrawTask load_task(const DrawTask* p) {
 }
 
 // ----------------------------------------------------------------- fp64 exp2
-// kExp2Table[j] = 2^(j/256), j = 0..255 (generated by gen_exp2_table.py).
+// kExp2Table[j] = 2^(j/1024), j = 0..1023 (generated by gen_exp2_table.py).
 #include "sv_exp2_table.h"
-constexpr int kExp2TableSize = 256;
+constexpr int kExp2TableSize = 1024;
+constexpr int kExp2Shift = 10;               // log2 of the table size
+constexpr double kExp2Scale = 1024.0;        // exp2_tab takes its argument times this
 // Adding 1.5 * 2^52 to a double of magnitude below 2^51 rounds it to an integer
 // (to nearest, ties to even) that then sits in the low bits of the mantissa.
 constexpr double kRoundMagic = 6755399441055744.0;
 
-// 2^(s/256) for s <= 0 (s = -inf allowed), relative error about 2e-16: s = k + r
+// 2^(s/1024) for s <= 0 (s = -inf allowed), relative error below 1e-15: s = k + r
 // with |r| <= 1/2 exactly (k rounded by the magic addition, whose low word is k
-// itself), 2^(r/256) by its Taylor series in r*ln2/256 to degree 4 (truncation
-// below 4e-17; the coefficients are (ln2)^i / i! scaled by 2^(-8i), exactly),
-// 2^((k mod 256)/256) from the table (kept in LDS by the caller) and 2^(k div 256)
-// by ldexp.  s is clamped at -276480 = 256 * -1080 first, whose power of two is
-// below the smallest double, so such results (and NaN inputs) are 0.  Taking s
-// already scaled by 256 (folded into the caller's coefficients, exactly) keeps
-// the rounding to one add.
-__device__ __forceinline__ double exp2_256(double s, const double* tab) {
-    s = fmax(s, -276480.0);
+// itself), 2^(r/1024) by its Taylor series in r*ln2/1024 to degree 3 (truncation
+// below 5.5e-16; the coefficients are (ln2)^i / i! scaled by 2^(-10i), exactly),
+// 2^((k mod 1024)/1024) from the table (kept in LDS by the caller) and
+// 2^(k div 1024) by ldexp.  s is clamped at -1105920 = 1024 * -1080 first, whose
+// power of two is below the smallest double, so such results (and NaN inputs)
+// are 0.  Taking s already scaled by 1024 (folded into the caller's
+// coefficients, exactly) keeps the rounding to one add; the 1024-entry table
+// keeps the polynomial one fma shorter than a 256-entry one would.
+__device__ __forceinline__ double exp2_tab(double s, const double* tab) {
+    s = fmax(s, -1105920.0);
     const double t = s + kRoundMagic;
     const int k = __double2loint(t);
     const double r = s - (t - kRoundMagic);
-    double p = fma(r, 2.239395190875157e-12, 3.3083026805413713e-09);
-    p = fma(r, p, 3.665565596910106e-06);
-    p = fma(r, p, 0.0027076061740622863);
+    double p = fma(r, 5.1692229383458926e-11, 2.2909784980688164e-07);
+    p = fma(r, p, 0.0006769015435155716);
     p = fma(r, p, 1.0);
-    return ldexp(tab[k & (kExp2TableSize - 1)] * p, k >> 8);
+    return ldexp(tab[k & (kExp2TableSize - 1)] * p, k >> kExp2Shift);
 }
 
 // ----------------------------------------------------------------- reductions
@@ -1061,8 +1063,8 @@ struct DrawRow {
     int pos;             // output column
     float v;             // uniform of the draw
     double m;            // row max (raw logits)
-    double c2;           // 256 log2(e) / T
-    double mc2;          // m * c2 (both exactly 256 times their unscaled roundings)
+    double c2;           // 1024 log2(e) / T
+    double mc2;          // m * c2 (both exactly 1024 times their unscaled roundings)
     double z32;          // normaliser from the fp32-exponential pass
     const typename E::T* lrow;
     const float* qrow;   // residual with dense q: q row, else nullptr
@@ -1079,7 +1081,7 @@ struct DrawRow {
 // e = exp((l - m) / T) of one token, in fp64 (the same expression everywhere).
 template <typename E>
 __device__ __forceinline__ double draw_e(const DrawRow<E>& d, float l, const double* tab) {
-    return exp2_256(fma(static_cast<double>(l), d.c2, -d.mc2), tab);
+    return exp2_tab(fma(static_cast<double>(l), d.c2, -d.mc2), tab);
 }
 
 // One lane's 8 tokens of one sub-block as loaded (raw element bits), and its
@@ -1195,7 +1197,7 @@ __device__ __noinline__ void record_marginal(const typename E::T* lrow, const fl
                     st_coherent(&rec->mx[slot], static_cast<int>(x));
                     st_coherent(&rec->mq[slot], qrow[x]);
                     st_coherent(&rec->me[slot],
-                                exp2_256(fma(static_cast<double>(E::load1(lrow, x)), c2, -mc2), tab));
+                                exp2_tab(fma(static_cast<double>(E::load1(lrow, x)), c2, -mc2), tab));
                 }
                 ++slot;
             }
@@ -1784,7 +1786,7 @@ __device__ __forceinline__ void init_draw_row(DrawRow<E>& d, const Params& P, in
     d.pos = pos;
     d.v = v;
     d.m = static_cast<double>(m);
-    d.c2 = 256.0 * (kLog2e / static_cast<double>(T));
+    d.c2 = kExp2Scale * (kLog2e / static_cast<double>(T));
     d.mc2 = d.m * d.c2;
     d.z32 = z32;
     d.lrow = static_cast<const typename E::T*>(P.logits) + (size_t)row * P.vocab;
@@ -1805,7 +1807,8 @@ __device__ __forceinline__ void init_draw_row(DrawRow<E>& d, const Params& P, in
     }
 }
 
-static_assert(kExp2TableSize == kThreads, "one table entry per draw thread");
+static_assert(kExp2TableSize % kThreads == 0, "whole table entries per draw thread");
+constexpr int kTabPerThread = kExp2TableSize / kThreads;
 struct DrawShared {
     double tab[kExp2TableSize];
     SelShared sel;
@@ -1859,11 +1862,11 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
     }
     const int t0 = o0 + b;
     const bool greedy = !(T > 0.0f);
-    // 256 times the pieces' scale log2(e) / T as the rows kernel rounded it
-    // (exact), and 256 log2(e) / T for the accept ratio: exponentials by the
+    // 1024 times the pieces' scale log2(e) / T as the rows kernel rounded it
+    // (exact), and 1024 log2(e) / T for the accept ratio: exponentials by the
     // same table-based exp2 as the draw weights
-    const double c256 = greedy ? 0.0 : 256.0 * static_cast<double>(static_cast<float>(kLog2e / static_cast<double>(T)));
-    const double c2 = greedy ? 0.0 : 256.0 * (kLog2e / static_cast<double>(T));
+    const double cpz = greedy ? 0.0 : kExp2Scale * static_cast<double>(static_cast<float>(kLog2e / static_cast<double>(T)));
+    const double c2 = greedy ? 0.0 : kExp2Scale * (kLog2e / static_cast<double>(T));
     const float v_res = P.uniforms[(size_t)b * (G + 2) + G];
     const float v_bonus = P.uniforms[(size_t)b * (G + 2) + G + 1];
     const bool owner = tid <= gb;
@@ -1928,12 +1931,12 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
 #pragma unroll
                 for (int q = 0; q < kResolveChunk; ++q) Mc = fmaxf(Mc, mm[q]);
                 if (Mc > M && M > -INFINITY)
-                    Z *= exp2_256((static_cast<double>(M) - static_cast<double>(Mc)) * c256, tab);
+                    Z *= exp2_tab((static_cast<double>(M) - static_cast<double>(Mc)) * cpz, tab);
                 M = Mc;
 #pragma unroll
                 for (int q = 0; q < kResolveChunk; ++q)
                     if (mm[q] > -INFINITY)
-                        Z += zz[q] * exp2_256((static_cast<double>(mm[q]) - static_cast<double>(M)) * c256, tab);
+                        Z += zz[q] * exp2_tab((static_cast<double>(mm[q]) - static_cast<double>(M)) * cpz, tab);
             } else {
 #pragma unroll
                 for (int q = 0; q < kResolveChunk; ++q) argmax_merge(M, g, mm[q], gg[q]);
@@ -1946,7 +1949,7 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
             if (greedy) {
                 acc = (xid == g);
             } else {
-                const double px = exp2_256(fma(static_cast<double>(lx), c2, -(static_cast<double>(M) * c2)), tab) / Z;
+                const double px = exp2_tab(fma(static_cast<double>(lx), c2, -(static_cast<double>(M) * c2)), tab) / Z;
                 r = px / fmax(static_cast<double>(qx), kQFloor);
                 acc = (xs >= 0) && (static_cast<double>(u) < fmin(1.0, r));
             }
@@ -2027,9 +2030,12 @@ __global__ __launch_bounds__(kThreads, kLoop ? 3 : 4) void draw_kernel(Params P)
 
     // the task (or the request's inputs), the temperature and the exponential
     // table in one round of loads
-    const double tv = kExp2Table[tid];
+    double tv[kTabPerThread];
+#pragma unroll
+    for (int j = 0; j < kTabPerThread; ++j) tv[j] = kExp2Table[tid + j * kThreads];
     const float T = P.temperature[b];
-    sh.tab[tid] = tv;
+#pragma unroll
+    for (int j = 0; j < kTabPerThread; ++j) sh.tab[tid + j * kThreads] = tv[j];
     const DrawTask tk = resolve_request<E>(P, b, c == 0, T, rsh, sh.tab);
     if (tk.kind == kDrawNone) return;
     const bool residual = (tk.kind == kDrawResidual);
