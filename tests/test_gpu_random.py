@@ -15,11 +15,14 @@ pytestmark = pytest.mark.gpu
 N_CASES = 64
 
 
-def _case(k):
-    rng = np.random.default_rng(9000 + k)
-    V = int(rng.choice([777, 1000, 4096, 6001, 16384, 20000]))
+N_WIDE = 16       # batches of 200-600 requests: more than a workgroup's threads
+
+
+def _case(k, wide=False):
+    rng = np.random.default_rng((19000 if wide else 9000) + k)
+    V = int(rng.choice([515, 777, 1000, 4096, 6001]) if wide else rng.choice([777, 1000, 4096, 6001, 16384, 20000]))
     spec = CONFIGS[4].with_(
-        batch=int(rng.integers(1, 41)),
+        batch=int(rng.integers(200, 601) if wide else rng.integers(1, 41)),
         gamma=int(rng.integers(0, 9)),
         vocab=V,
         dtype=str(rng.choice(["f32", "bf16"])),
@@ -29,9 +32,9 @@ def _case(k):
         ragged=bool(rng.integers(0, 2)),
         q_mode=str(rng.choice(["dense", "topk", "argmax"])),
         top_k=int(rng.integers(1, 65)),
-        name=f"random{k}",
+        name=f"random{'_wide' if wide else ''}{k}",
     )
-    inp = make_inputs(spec, seed=9100 + k)
+    inp = make_inputs(spec, seed=(19100 if wide else 9100) + k)
     fmt = "dense"
     if spec.q_mode == "topk" and inp.total_draft and rng.integers(0, 2):
         K = int(max(1, (inp.draft_probs != 0).sum(axis=1).max()))
@@ -51,6 +54,20 @@ def test_random_case(k, schedule):
         f"ragged={spec.ragged} q={spec.q_mode}/{fmt} schedule={schedule}")
     sets = [inp.uniforms] + [uniforms_from_seed(inp.uniforms.shape, 9500 + k * 10 + s) for s in range(5)]
     rep, errs, sv = parity_check(inp, sets, label=f"random{k}", schedule=schedule)
+    assert not rep.unexcused, "\n".join(rep.unexcused[:10])
+    assert not errs, errs
+    assert rep.excused <= 1e-4 * rep.requests + 1e-9 or rep.excused == 0
+    assert sv.device_errors() == 0
+
+
+@pytest.mark.parametrize("schedule", ["twokernel", "onelaunch"])
+@pytest.mark.parametrize("k", range(N_WIDE))
+def test_random_wide_case(k, schedule):
+    spec, inp, fmt = _case(k, wide=True)
+    log(f"[random wide {k}] B={inp.batch} gamma={inp.gamma} V={inp.vocab} {inp.dtype} T={spec.temperatures} "
+        f"ragged={spec.ragged} q={spec.q_mode}/{fmt} schedule={schedule}")
+    sets = [inp.uniforms] + [uniforms_from_seed(inp.uniforms.shape, 29500 + k * 10 + s) for s in range(3)]
+    rep, errs, sv = parity_check(inp, sets, label=f"random_wide{k}", schedule=schedule)
     assert not rep.unexcused, "\n".join(rep.unexcused[:10])
     assert not errs, errs
     assert rep.excused <= 1e-4 * rep.requests + 1e-9 or rep.excused == 0
