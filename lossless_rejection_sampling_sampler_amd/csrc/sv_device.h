@@ -1254,15 +1254,35 @@ __device__ __forceinline__ void accumulate_sub(const DrawRow<E>& d, const float*
 template <typename E, bool kResidual>
 __device__ __forceinline__ void accumulate_raw(const DrawRow<E>& d, const RawSub<E>& r, int u, double apos,
                                                double aneg, const double* tab, BlockSums& b) {
+    if constexpr (sizeof(typename E::T) == 2) {
+        // bf16: four tokens at a time (more independent fp64 chains per wave;
+        // the fp32 form would spill at this width)
 #pragma unroll
-    for (int k = 0; k < kSubTokens; k += 2) {
-        float la = sub_logit<E>(r, k), lb = sub_logit<E>(r, k + 1);
-        if (k > 0) asm volatile("" : "+v"(la), "+v"(lb) : "v"(b.se));
-        accumulate_token<E, kResidual>(d, la, kResidual ? sub_q<E>(r, k) : 0.0f, u * kSubTokens + k, apos, aneg,
-                                       tab, b);
-        accumulate_token<E, kResidual>(d, lb, kResidual ? sub_q<E>(r, k + 1) : 0.0f, u * kSubTokens + k + 1, apos,
-                                       aneg, tab, b);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int k = 0; k < kSubTokens; k += 4) {
+            float la = sub_logit<E>(r, k), lb = sub_logit<E>(r, k + 1);
+            float lc = sub_logit<E>(r, k + 2), ld = sub_logit<E>(r, k + 3);
+            if (k > 0) asm volatile("" : "+v"(la), "+v"(lb), "+v"(lc), "+v"(ld) : "v"(b.se));
+            accumulate_token<E, kResidual>(d, la, kResidual ? sub_q<E>(r, k) : 0.0f, u * kSubTokens + k, apos,
+                                           aneg, tab, b);
+            accumulate_token<E, kResidual>(d, lb, kResidual ? sub_q<E>(r, k + 1) : 0.0f, u * kSubTokens + k + 1,
+                                           apos, aneg, tab, b);
+            accumulate_token<E, kResidual>(d, lc, kResidual ? sub_q<E>(r, k + 2) : 0.0f, u * kSubTokens + k + 2,
+                                           apos, aneg, tab, b);
+            accumulate_token<E, kResidual>(d, ld, kResidual ? sub_q<E>(r, k + 3) : 0.0f, u * kSubTokens + k + 3,
+                                           apos, aneg, tab, b);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < kSubTokens; k += 2) {
+            float la = sub_logit<E>(r, k), lb = sub_logit<E>(r, k + 1);
+            if (k > 0) asm volatile("" : "+v"(la), "+v"(lb) : "v"(b.se));
+            accumulate_token<E, kResidual>(d, la, kResidual ? sub_q<E>(r, k) : 0.0f, u * kSubTokens + k, apos,
+                                           aneg, tab, b);
+            accumulate_token<E, kResidual>(d, lb, kResidual ? sub_q<E>(r, k + 1) : 0.0f, u * kSubTokens + k + 1,
+                                           apos, aneg, tab, b);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 }
 
