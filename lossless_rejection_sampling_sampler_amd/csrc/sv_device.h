@@ -1249,7 +1249,7 @@ __device__ __forceinline__ void accumulate_sub(const DrawRow<E>& d, const float*
     }
 }
 
-// The same sums taken straight from a loaded sub-block, two tokens at a time,
+// The same sums taken straight from a loaded sub-block, four (bf16) or two (fp32) tokens at a time,
 // with no decoded copy of the sub-block held in registers.
 template <typename E, bool kResidual>
 __device__ __forceinline__ void accumulate_raw(const DrawRow<E>& d, const RawSub<E>& r, int u, double apos,
