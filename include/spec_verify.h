@@ -14,7 +14,7 @@
  *                (p - q)_+ / sum (p - q)_+, which makes the emitted tokens
  *                distributed exactly as p;
  *   section 5.2  q is floored at 1e-10 before dividing, the test is the strict
- *                comparison "uniform < accept probability", and acceptance is a
+ *                comparison of the uniform with the accept probability, and acceptance is a
  *                prefix property (a cumulative product of the accept bits);
  *   section 5.3  when all gamma_b drafts are accepted a bonus token is drawn
  *                from the (gamma_b + 1)-th target distribution;

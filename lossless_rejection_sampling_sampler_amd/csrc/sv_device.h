@@ -3,7 +3,7 @@
 // Method: the spec-decoding page at dpshk.com/news/5598276 ("企业官网建设流程全解析"),
 // sections 3.1-3.2 (accept with probability min(1, p/q), stop at the first
 // rejection, redraw from (p - q)_+), 5.2 (q floored at 1e-10, strict
-// "uniform < accept probability", prefix acceptance), 5.3 (bonus token from the
+// comparison of the uniform with the accept probability, prefix acceptance), 5.3 (bonus token from the
 // last target row) and 8 (T = 0 is greedy).
 //
 // Two kernels per verify step, both bandwidth-bound streams over the vocabulary:
@@ -60,7 +60,7 @@ constexpr int kMaxDrawBlocks = 256;                  // vocab up to 2^19 tokens
 constexpr int kSelPer = kMaxDrawBlocks / 64;         // blocks per lane in the select
 constexpr int kMarginSlots = 2;          // marginal tokens kept inline per block record (code assumes 2)
 constexpr double kLog2e = 1.4426950408889634;
-constexpr double kQFloor = 1e-10;        // page section 5.2: q.clamp(min=1e-10)
+constexpr double kQFloor = 1e-10;        // page section 5.2: q is floored at 1e-10 before dividing
 // Relative margin within which a residual weight's sign could depend on the
 // last bits of the normaliser; such tokens are kept aside and re-evaluated with
 // the exact fp64 normaliser.

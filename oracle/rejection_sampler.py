@@ -15,7 +15,8 @@ Source of the method: the spec-decoding page at dpshk.com/news/5598276
   that the combined procedure emits tokens distributed exactly as p.
 * [page §4] the worked example figure (ratios 0.92, 0.75, 0.31; three tokens).
 * [page §5.2] the vectorised sampler: softmax of the target logits, q clamped
-  below at 1e-10, "uniform < accept_prob", a cumulative product as the prefix
+  below at 1e-10, a strict comparison of the uniform with the accept
+  probability, a cumulative product as the prefix
   mask, and the residual clamp / normalise / categorical draw.
 * [page §5.3] the bonus token: when all gamma drafts are accepted, one more
   token is drawn from the (gamma+1)-th target distribution.
@@ -187,7 +188,8 @@ def acceptance_stats(num_accepted: np.ndarray, gammas: np.ndarray, gamma: int) -
 
 
 def _first_rejection(accepted: np.ndarray, g: int) -> np.ndarray:
-    """Index of the first False along the last axis, g if none [page §5.2 cumprod]."""
+    """Index of the first False along the last axis, g if none (the prefix of
+    accepted drafts, [page §5.2])."""
     if g == 0:
         return np.zeros(accepted.shape[0], dtype=np.int64)
     return np.where(accepted.all(axis=-1), g, accepted.argmin(axis=-1))

@@ -56,7 +56,7 @@ def test_worked_example_from_figure():
 # ---------------------------------------------------------------- exact tie
 @pytest.mark.parametrize("u0, accepted", [(0.25, False), (0.25 - U_STEP, True)])
 def test_exact_tie_rejects(u0, accepted):
-    """[page §5.2] 'uniform < accept_prob' is strict: a die equal to the ratio rejects.
+    """[page §5.2] the accept comparison is strict: a die equal to the ratio rejects.
 
     Equal logits at T = 1 give p = 1/8 exactly; q(x) = 1/2 gives ratio 1/4 exactly.
     """
