@@ -2,13 +2,20 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-A step is one spec_verify_run (one cooperative launch, or rows kernel + draw
-kernel, as the library or --schedule picks) over the workload
+A step is one spec_verify_run (rows kernel + draw kernel) over the workload
 B=64, gamma=5, V=151936, bf16 target logits, fp32 draft probabilities,
 T=0.8 on every request.  Inputs are synthetic (seeded, see synth/), already
 resident in HBM; R rotating copies of the inputs (more than the 256 MB
-Infinity Cache can hold) are cycled so every step streams from HBM.  Prints
-one JSON line.
+Infinity Cache can hold) are cycled so every step streams from HBM.
+
+Before any GPU call the CPU oracle is timed on the same workload, in one
+process and in a pool of forked workers over request chunks (the host's cores,
+at most 16).  Then: the timed region (exactly K steps between two
+synchronisations), a pass with an event between consecutive steps for the
+median / p10 / p90 step time, a pass whose kernels are stamped by their own
+dispatches (kernel durations without the gap between dispatches, as rocprofv3
+reports them), and a plain streaming read of 1 GiB and of one step's bytes for
+the device's practical read ceiling.  Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -174,7 +181,7 @@ def write_traffic(fetch_csv, write_csv):
     sha = kernel_source_sha()
     for name in fetch:
         short = None
-        for kn in ("rows_flat_kernel", "rows_split_kernel", "draw_kernel", "step_kernel"):
+        for kn in ("rows_flat_kernel", "rows_split_kernel", "draw_kernel"):
             if kn in name:
                 short = f"{kn}<{'BF16' if 'BF16' in name else 'F32'}>"
         if short is None or name not in write:
@@ -195,18 +202,144 @@ def write_traffic(fetch_csv, write_csv):
         print(f"{short}: {rec['bytes_per_launch'] / 1e6:.1f} MB per launch -> {traffic_path(short)}")
 
 
-def cpu_baseline(inp, budget_s=12.0):
+def sub_batch(inp, b0: int, b1: int):
+    """Requests [b0, b1) of ``inp`` as a batch of their own (same layout rules)."""
+    import dataclasses
+    import numpy as np
+    off = inp.draft_offsets
+    d0, d1 = int(off[b0]), int(off[b1])
+    t0, t1 = d0 + b0, d1 + b1
+    cut = lambda a, lo, hi: None if a is None else a[lo:hi]
+    return dataclasses.replace(
+        inp, batch=b1 - b0, logits=inp.logits[t0:t1], draft_probs=cut(inp.draft_probs, d0, d1),
+        draft_ids=inp.draft_ids[d0:d1], temperature=inp.temperature[b0:b1], uniforms=inp.uniforms[b0:b1],
+        offsets=None if inp.offsets is None else (np.asarray(off[b0:b1 + 1]) - d0).astype(np.int32),
+        topk_ids=cut(inp.topk_ids, d0, d1), topk_probs=cut(inp.topk_probs, d0, d1))
+
+
+_POOL_INP = None
+
+
+def _pool_verify(rng):
     import oracle
+    b0, b1 = rng
+    oracle.verify(sub_batch(_POOL_INP, b0, b1))
+    return b1 - b0
+
+
+def cpu_baseline(inp, budget_s=10.0, max_workers=16):
+    """The oracle timed on the host: one process, then forked workers over request
+    chunks.  Runs before any GPU call (forking a process that has initialised the
+    GPU is not allowed)."""
+    import multiprocessing as mp
+    import oracle
+    global _POOL_INP
     t0 = time.perf_counter()
-    n = 0
+    n1 = 0
     while True:
         oracle.verify(inp)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= 50:
+        n1 += 1
+        el1 = time.perf_counter() - t0
+        if el1 >= budget_s or n1 >= 50:
             break
-    return {"value": n / el, "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} full B={inp.batch} steps of the same workload (fp64 NumPy, one process)"}
+    host_cpus = os.cpu_count() or 1
+    workers = max(1, min(host_cpus, max_workers, inp.batch))
+    bounds = [round(k * inp.batch / workers) for k in range(workers + 1)]
+    chunks = [(bounds[k], bounds[k + 1]) for k in range(workers) if bounds[k + 1] > bounds[k]]
+    _POOL_INP = inp
+    with mp.get_context("fork").Pool(len(chunks)) as pool:
+        pool.map(_pool_verify, chunks)             # start-up outside the timing
+        t0 = time.perf_counter()
+        nw = 0
+        while True:
+            done = sum(pool.map(_pool_verify, chunks))
+            assert done == inp.batch
+            nw += 1
+            elw = time.perf_counter() - t0
+            if elw >= budget_s or nw >= 200:
+                break
+    _POOL_INP = None
+    return {"value": round(nw / elw, 4), "unit": "steps/s", "cores": len(chunks), "kind": "oracle",
+            "sample": f"{nw} full B={inp.batch} steps of the same workload, each split into {len(chunks)} "
+                      f"request chunks over {len(chunks)} forked worker processes (fp64 NumPy)",
+            "host_cpu_count": host_cpus,
+            "one_core": {"value": round(n1 / el1, 4), "unit": "steps/s", "cores": 1,
+                         "sample": f"{n1} full steps in one process"}}
+
+
+def durations_path():
+    return os.path.join(ROOT, "profiles", "kernel_durations_B64_g5_V151936.json")
+
+
+def write_durations(stats_csv):
+    """Per-kernel average durations of one rocprofv3 --stats run (kernel_stats.csv),
+    stamped with the kernel sources' hash, for the bench line's roofline."""
+    import csv
+    out = {"workload": "B=64, gamma=5, V=151936, bf16 logits, fp32 q, T=0.8",
+           "kernel_source_sha256": kernel_source_sha(), "source": os.path.relpath(stats_csv, ROOT), "kernels": {}}
+    with open(stats_csv, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row["Name"]
+            for kn in ("rows_flat_kernel", "rows_split_kernel", "draw_kernel"):
+                if f"sv::{kn}<" in name:
+                    short = f"{kn}<{'BF16' if 'BF16' in name else 'F32'}>"
+                    out["kernels"][short] = {"calls": int(row["Calls"]),
+                                             "avg_ms": float(row["AverageNs"]) / 1e6,
+                                             "min_ms": float(row["MinNs"]) / 1e6,
+                                             "max_ms": float(row["MaxNs"]) / 1e6}
+    with open(durations_path(), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out["kernels"], indent=1))
+
+
+def profiled_avg_ms(kernel: str):
+    """rocprofv3's average duration of ``kernel`` on this workload, if recorded for
+    the current kernel sources."""
+    try:
+        rec = json.load(open(durations_path()))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    k = rec["kernels"].get(kernel)
+    return None if k is None else k["avg_ms"]
+
+
+def read_ceiling(torch, nbytes_list, reps=5):
+    """GB/s of the plain streaming-read probe over buffers of the given sizes."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "lossless_rejection_sampling_sampler_amd", "libhbmprobe.so"))
+    lib.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.hbm_read_probe.restype = ctypes.c_int
+    props = torch.cuda.get_device_properties(0)
+    grid = 4 * props.multi_processor_count
+    out = torch.empty(grid, dtype=torch.int32, device="cuda:0")
+    sh = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for nb in nbytes_list:
+        nb = nb // 16 * 16
+        # several buffers, so the Infinity Cache cannot serve a repeat
+        bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda:0") for _ in range(max(1, (1 << 30) // nb + 1))]
+        for b in bufs:
+            b.fill_(1)
+        times = []
+        for r in range(reps + 1):
+            b = bufs[r % len(bufs)]
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            st = lib.hbm_read_probe(ctypes.c_void_p(b.data_ptr()), nb, ctypes.c_void_p(out.data_ptr()), grid,
+                                    ctypes.c_void_p(sh))
+            e1.record()
+            if st:
+                raise RuntimeError(f"hbm_read_probe status {st}")
+            torch.cuda.synchronize()
+            if r:
+                times.append(e0.elapsed_time(e1))
+        times.sort()
+        res[nb] = nb / (times[len(times) // 2] * 1e-3) / 1e9
+        del bufs
+        torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -216,26 +349,35 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--rotate", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds per CPU baseline leg")
     ap.add_argument("--seed-replicate", type=int, default=0)
     ap.add_argument("--workload", choices=list(WORKLOAD_TEXT), default="config3",
-                    help="config3 (the default line); other workloads of the draft-distribution "
-                         "formats are for comparison runs")
-    ap.add_argument("--schedule", choices=["auto", "onelaunch", "twokernel"], default="auto",
-                    help="one-launch step, rows + draw kernels, or the library's choice")
+                    help="config3 (the default line); other workloads are for comparison runs")
+    ap.add_argument("--schedule", choices=["auto", "twokernel"], default="auto",
+                    help="rows + draw kernels, or the library's choice")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed from a captured HIP graph (one call per replay, "
                          "input sets rotating) and report it as graph_steps_per_s")
-    ap.add_argument("--profile-steps", type=int, default=200,
-                    help="steps of the per-kernel HIP-event timing pass")
+    ap.add_argument("--profile-steps", type=int, default=500,
+                    help="steps of the dispatch-stamped per-kernel timing pass")
+    ap.add_argument("--dist-steps", type=int, default=500,
+                    help="steps of the per-step timing pass (median / p10 / p90)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
     ap.add_argument("--pmc-workload", action="store_true",
                     help="for rocprofv3 counter passes: a plain copy of known size (the scale "
                          "reference), then --warmup + --steps verify steps; prints no JSON")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="(CPU only) turn two counter_collection.csv files of --pmc-workload runs "
                          "into per-kernel HBM traffic records under profiles/")
+    ap.add_argument("--durations-from", metavar="KERNEL_STATS_CSV",
+                    help="(CPU only) record rocprofv3's per-kernel averages of a default-workload run "
+                         "under profiles/ for the bench line")
     args = ap.parse_args()
     if args.traffic_from:
         write_traffic(*args.traffic_from)
+        return
+    if args.durations_from:
+        write_durations(args.durations_from)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the verify step shards by "
@@ -244,14 +386,21 @@ def main():
         sys.exit(2)
 
     import numpy as np
-    import torch
-
-    from lossless_rejection_sampling_sampler_amd import SpecVerify, upload
-    from lossless_rejection_sampling_sampler_amd._lib import SCHEDULE_NAMES, SV_SCHEDULE_ONE_LAUNCH
 
     log(f"[bench] generating workload {args.workload}")
     inp = make_workload(args.workload, args.seed_replicate)
     wl_text = WORKLOAD_TEXT[args.workload]
+    cpu = None
+    if not args.no_cpu_baseline and not args.pmc_workload:
+        log("[bench] timing the CPU oracle (before any GPU call)")
+        cpu = cpu_baseline(inp, args.cpu_budget)
+        log(f"[bench] oracle: {cpu['one_core']['value']} steps/s on one core, {cpu['value']} on {cpu['cores']}")
+
+    import torch
+
+    from lossless_rejection_sampling_sampler_amd import SpecVerify, upload
+    from lossless_rejection_sampling_sampler_amd._lib import SCHEDULE_NAMES
+
     dev = torch.device("cuda:0")
     log("[bench] uploading, rotate=%d" % args.rotate)
     base = upload(logits=inp.logits, logits_dtype=inp.dtype, draft_probs=inp.draft_probs,
@@ -279,6 +428,7 @@ def main():
         for _ in range(COPY_REPS):
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
+        del src, dst
     sv = SpecVerify(inp.batch, inp.gamma, inp.vocab, inp.dtype, device=0, schedule=schedule)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
@@ -293,6 +443,7 @@ def main():
     for i in range(args.warmup):
         step(sv, i)
     torch.cuda.synchronize()
+    log(f"[bench] warm-up done ({args.warmup} steps); timing {args.steps} steps")
 
     # ---- timed region: exactly K steps, synchronised on both sides
     t_start = torch.cuda.Event(enable_timing=True)
@@ -305,6 +456,26 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
+    log(f"[bench] {ms_per_step * 1e3:.2f} us per step")
+
+    if args.pmc_workload:
+        log(f"[bench] counter workload done: {args.warmup + args.steps} steps")
+        sv.close()
+        return
+
+    # ---- per-step times: one event between consecutive steps
+    nd = max(2, args.dist_steps)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nd + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(nd):
+        step(sv, i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(nd)])
+    dist = {"steps": nd, "median_ms": round(float(np.median(per)), 6),
+            "p10_ms": round(float(np.percentile(per, 10)), 6), "p90_ms": round(float(np.percentile(per, 90)), 6),
+            "mean_ms": round(float(per.mean()), 6)}
 
     graph_rate = None
     if args.graph:
@@ -332,10 +503,6 @@ def main():
         graph_rate = 1000.0 * args.steps / g0.elapsed_time(g1)
 
     sv_schedule = sv.last_schedule()
-    if args.pmc_workload:
-        log(f"[bench] counter workload done: {args.warmup + args.steps} steps")
-        sv.close()
-        return
     tok, num = base.results()
     for c in copies[1:]:
         t2, n2 = c.results()
@@ -343,7 +510,7 @@ def main():
     rows_b, draw_b = algorithmic_bytes(inp, num)
     step_bytes = rows_b + draw_b
 
-    # ---- per-kernel durations: HIP events recorded by the library on this stream
+    # ---- per-kernel durations, stamped by the kernels' own dispatches
     svp = SpecVerify(inp.batch, inp.gamma, inp.vocab, inp.dtype, device=0, profile=True, schedule=schedule)
     for i in range(args.warmup):
         step(svp, i)
@@ -353,23 +520,38 @@ def main():
     for i in range(kp):
         step(svp, i)
     rows_ms, draw_ms, n_prof = svp.profile_read()
-    svp_schedule = svp.last_schedule()
     rows_avg_ms, draw_avg_ms = rows_ms / n_prof, draw_ms / n_prof
     svp.close()
+    log(f"[bench] kernels: rows {rows_avg_ms * 1e3:.2f} us, draw {draw_avg_ms * 1e3:.2f} us")
+
+    ceiling = None
+    if not args.no_ceiling:
+        for c in copies[1:]:
+            c.target_logits = c.draft_probs = None
+        copies = copies[:1]
+        packed = packed[:1]
+        torch.cuda.empty_cache()
+        cz = read_ceiling(torch, [1 << 30, step_bytes])
+        ceiling = {"read_1GiB_gbps": round(cz[(1 << 30) // 16 * 16], 1),
+                   "read_step_bytes_gbps": round(cz[step_bytes // 16 * 16], 1),
+                   "kernel": "16-byte non-temporal loads, 4 workgroups of 256 per CU, one launch per buffer"}
+        log(f"[bench] read ceiling {ceiling}")
 
     def roofline(kname, kbytes, kms):
         gbps = kbytes / (kms * 1e-3) / 1e9
-        return {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(gbps / PEAK_HBM_GBPS, 4), "kernel": kname, "bytes_per_launch": kbytes,
-                "avg_launch_ms": round(kms, 6),
-                "traffic": traffic_entry(kname) if args.workload == "config3" else None}
+        prof = profiled_avg_ms(kname) if args.workload == "config3" else None
+        r = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+             "frac": round(gbps / PEAK_HBM_GBPS, 4), "kernel": kname, "bytes_per_launch": kbytes,
+             "avg_launch_ms": round(kms, 6), "timing": "dispatch-stamped HIP events over the profiling pass",
+             "traffic": traffic_entry(kname) if args.workload == "config3" else None,
+             "rocprof_avg_ms": prof,
+             "rocprof_frac": None if prof is None else round(kbytes / (prof * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+        return r
 
-    if svp_schedule == SV_SCHEDULE_ONE_LAUNCH:
-        # one kernel does the whole step: its bytes are the step's
-        lines = [roofline(f"step_kernel<{KDT}>", step_bytes, rows_avg_ms)]
-    else:
-        lines = [roofline(f"rows_flat_kernel<{KDT}>", rows_b, rows_avg_ms),
-                 roofline(f"draw_kernel<{KDT}>", draw_b, draw_avg_ms)]
+    split = sv_schedule == 1
+    lines = [roofline(f"{'rows_split_kernel' if split else 'rows_flat_kernel'}<{KDT if inp.dtype == 'bf16' else 'F32'}>",
+                      rows_b, rows_avg_ms),
+             roofline(f"draw_kernel<{KDT if inp.dtype == 'bf16' else 'F32'}>", draw_b, draw_avg_ms)]
     dominant = max(lines, key=lambda r: r["avg_launch_ms"])
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     sampled = inp.temperature > 0
@@ -388,23 +570,24 @@ def main():
         "dtype": "bf16 in; f32 exp + f64 sums; f64 draw",
         "data": "synthetic (seeded; shapes of the pages' gamma=5, T=0.8 deployment)",
         "config": {"workload": f"verify step {inp.name}: {wl_text}", "batch": inp.batch, "gamma": inp.gamma,
-                   "vocab": inp.vocab, "rotating_input_sets": len(copies)},
+                   "vocab": inp.vocab, "rotating_input_sets": args.rotate},
         "hbm_gbps": round(step_gbps, 1),
         "frac_of_peak": round(step_gbps / PEAK_HBM_GBPS, 4),
         "algorithmic_bytes_per_step": step_bytes,
+        "step_time_distribution": dist,
         "schedule": SCHEDULE_NAMES.get(sv_schedule, "none"),
         "kernels": {"rows_ms": round(rows_avg_ms, 6), "draw_ms": round(draw_avg_ms, 6),
-                    "rows_bytes": rows_b, "draw_bytes": draw_b, "events_over_steps": n_prof},
+                    "rows_bytes": rows_b, "draw_bytes": draw_b, "profiled_steps": n_prof},
         "acceptance": {"mean_accepted": float(num.mean()),
                        "residual_draws": int((sampled & (num < gam)).sum()),
                        "bonus_draws": int((sampled & (num == gam)).sum())},
         "graph_steps_per_s": None if graph_rate is None else round(graph_rate, 2),
+        "read_ceiling": ceiling,
         "roofline": dominant,
         "roofline_per_kernel": lines,
     }
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle")
-        result["cpu_baseline"] = cpu_baseline(inp)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
     sv.close()
 

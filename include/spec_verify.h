@@ -61,7 +61,10 @@ enum sv_status {
     SV_ERR_OUT_OF_MEMORY = 2,  /* device allocation failed in spec_verify_create */
     SV_ERR_DEVICE = 3,         /* a HIP call failed (launch, event, copy) */
     SV_ERR_UNSUPPORTED = 4,    /* dtype / size outside what the library handles */
-    SV_ERR_CAPACITY = 5        /* batch, gamma or vocab exceed the context's limits */
+    SV_ERR_CAPACITY = 5,       /* batch, gamma or vocab exceed the context's limits */
+    SV_ERR_DEVICE_CONTRACT = 6 /* an earlier call on this context broke the device-side
+                                  contract (see sv_device_error); nothing was enqueued.
+                                  Read and clear the bits with spec_verify_device_errors */
 };
 
 /* Logits element type. */
@@ -70,29 +73,26 @@ enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 };
 /* Context flags. */
 enum sv_flags {
     SV_FLAG_PROFILE = 1u,      /* record per-kernel HIP events (see spec_verify_profile_read) */
-    SV_FLAG_TWO_KERNEL = 2u,   /* schedule: rows kernel, then draw kernel */
-    SV_FLAG_ONE_LAUNCH = 4u    /* schedule: one launch whose workgroups stream their rows, then
-                                  turn to draw blocks (rows must be 16-byte aligned, else the
-                                  two-kernel schedule is used).  The grid is sized to what the
-                                  device holds at once, so its workgroups wait on each other: it
-                                  needs the device to itself (see SV_DEVERR_STALLED).  With no
-                                  schedule flag the library picks the faster schedule */
+    SV_FLAG_TWO_KERNEL = 2u    /* schedule: rows kernel, then draw kernel (also the default) */
 };
 
-/* Device-side contract violations, OR-ed into a sticky per-context word. */
+/* Device-side contract violations, OR-ed into a sticky per-context word.  A
+ * request that breaks the contract gets -1 in every token column and in
+ * num_accepted, is not counted in the acceptance counters, and no access
+ * leaves the buffers' bounds.  Once the device has run such a call, every
+ * later spec_verify_run on the context returns SV_ERR_DEVICE_CONTRACT until
+ * spec_verify_device_errors clears the word. */
 enum sv_device_error {
-    SV_DEVERR_DRAFT_ID = 1u,   /* a draft id outside [0, vocab); that draft counts as rejected */
+    SV_DEVERR_DRAFT_ID = 1u,   /* a draft id outside [0, vocab) (the page's section 8, pitfall 1:
+                                  draft and target share one vocabulary) */
     SV_DEVERR_OFFSETS = 2u,    /* draft_offsets not prefix sums with 0 <= gamma_b <= gamma and
-                                  offsets[batch] <= total_draft; the affected requests' outputs
-                                  are unspecified (no access leaves the buffers' bounds) */
-    SV_DEVERR_NONFINITE = 4u,  /* a draw row without positive finite mass (a target row with no
-                                  finite logit, or NaN logits); that token is unspecified */
-    SV_DEVERR_STALLED = 8u,    /* one-launch schedule: a bounded wait (seconds) for a draw task
-                                  expired, e.g. because other work kept part of the grid from
-                                  becoming resident; that call's outputs are unspecified */
+                                  offsets[batch] <= total_draft: requests whose own offsets are
+                                  inconsistent get -1; other requests whose rows those offsets
+                                  misplace are unspecified */
+    SV_DEVERR_NONFINITE = 4u,  /* a sampled target row without a positive finite normaliser (no
+                                  finite logit, NaN or +inf logits) */
     SV_DEVERR_TOPK = 16u       /* sparse q: an entry id outside [-1, vocab), or the drafted token
-                                  listed twice in its row; such entries are ignored (the
-                                  request's outputs are unspecified, no access leaves the buffers) */
+                                  listed twice in its row */
 };
 
 /* Largest number of (id, prob) entries per draft row of a sparse q. */
@@ -149,8 +149,10 @@ typedef struct sv_config {
  *   uniforms       [batch, gamma + 2] fp32 in [0, 1) (see the column map above).
  * Outputs (written for every request):
  *   out_tokens       [batch, gamma + 1] int32: drafts 0..k-1, then the drawn (or
- *                    greedy) token at k, then -1.
- *   out_num_accepted [batch] int32: k, the number of accepted drafts.
+ *                    greedy) token at k, then -1 (all -1 for a request that
+ *                    breaks the device-side contract, see sv_device_error).
+ *   out_num_accepted [batch] int32: k, the number of accepted drafts (-1 for
+ *                    a request that breaks the contract).
  * Optional diagnostics (NULL to skip):
  *   diag_row_max   [total_draft + batch] fp32: max raw logit of every target row.
  *   diag_row_norm  [total_draft + batch] fp64: Z = sum exp((l - max) / T) of every
@@ -182,49 +184,56 @@ typedef struct sv_args {
 
 typedef struct sv_ctx sv_ctx;    /* opaque; owns the device scratch of one stream */
 
-/* Creates a context on HIP device `device` and allocates its scratch (row
- * statistics, counters, draw records) for cfg's limits.  On success *out
- * holds the context (free it with spec_verify_destroy).  Returns
- * SV_ERR_INVALID_ARG for bad limits, SV_ERR_UNSUPPORTED for a dtype, vocab or
- * row count (max_batch * (max_gamma + 1) above 2^31 - 1) the library does not
- * handle, SV_ERR_OUT_OF_MEMORY / SV_ERR_DEVICE on HIP failure (then *out is
- * NULL). */
+/* Creates a context for the verify step of the spec-decoding page (section 3.1:
+ * B requests, gamma_b drafts each, gamma_b + 1 target distributions over one
+ * vocabulary shared by draft and target, section 8 pitfall 1) on HIP device
+ * `device`, and allocates what every call reuses: device scratch for the row
+ * statistics, draw records and arrival counters sized for cfg's limits, a
+ * pinned host word for contract violations, an internal non-blocking stream
+ * and an event.  On success *out holds the context (free it with
+ * spec_verify_destroy).  Returns SV_ERR_INVALID_ARG for bad limits,
+ * SV_ERR_UNSUPPORTED for a dtype, vocab or row count (max_batch *
+ * (max_gamma + 1) above 2^31 - 1) the library does not handle,
+ * SV_ERR_OUT_OF_MEMORY / SV_ERR_DEVICE on HIP failure (then *out is NULL). */
 int spec_verify_create(const sv_config *cfg, int device, sv_ctx **out);
 
 /* Enqueues one verify step on `stream` (a hipStream_t; NULL = default stream)
- * and returns without waiting.  Host-visible arguments are checked first; on a
- * non-SV_OK status nothing is enqueued.  Outputs are valid once the stream has
- * reached this point.  The call allocates nothing.  One context must not be
- * used by two streams at the same time (its scratch is per call).  Without
- * SV_FLAG_ONE_LAUNCH or SV_FLAG_PROFILE the call only launches kernels whose
- * arrival counters reset themselves, so it may be captured in a HIP graph and
- * replayed (the buffers' contents may change between replays; their addresses
- * and the sizes may not).  The one-launch schedule tags each call's draw tasks
- * with a host-side epoch, which a replay would repeat: do not capture it. */
+ * and returns without waiting.  First, if the device has reported a contract
+ * violation of an earlier call, returns SV_ERR_DEVICE_CONTRACT; then the
+ * host-visible arguments are checked; on a non-SV_OK status nothing is
+ * enqueued.  Outputs are valid once the stream has reached this point.  The
+ * call allocates nothing.  One context must not be used by two streams at the
+ * same time (its scratch is per call).  Without SV_FLAG_PROFILE the call only
+ * launches kernels whose arrival counters reset themselves, so it may be
+ * captured in a HIP graph and replayed (the buffers' contents may change
+ * between replays; their addresses and the sizes may not). */
 int spec_verify_run(sv_ctx *ctx, const sv_args *args, void *stream);
 
-/* Frees the context and its scratch after synchronising its device.  NULL is a
- * no-op. */
+/* Releases what spec_verify_create allocated (lifecycle only; the page defines
+ * no such step).  Waits for the context's last eagerly launched call and its
+ * internal stream first, not for other work on the device (freeing device
+ * memory may itself synchronise the device).  NULL is a no-op. */
 int spec_verify_destroy(sv_ctx *ctx);
 
-/* Reads (and, if clear != 0, resets) the sticky SV_DEVERR_* word.  Synchronises
- * the context's device first.  Clearing also resets the context's arrival
- * counters, which a call with inconsistent draft_offsets can leave behind: after
- * a non-zero word, clear it before the next run. */
+/* Reads (and, if clear != 0, resets) the sticky SV_DEVERR_* word.  Waits for the
+ * context's last eagerly launched call (the point of its stream where that call
+ * ended; synchronise a replayed graph yourself) and uses the context's internal
+ * stream for the read and the reset, so other streams are not waited for.  Do
+ * not call it while a call on this context may still be enqueued elsewhere. */
 int spec_verify_device_errors(sv_ctx *ctx, uint32_t *bits, int clear);
 
 /* With SV_FLAG_PROFILE: waits for the recorded events and returns the summed
  * durations (milliseconds) over `*count` calls since the last read, then resets
- * the sums.  rows_ms is the row-statistics kernel and draw_ms the draw kernel; for
- * a one-launch step rows_ms is the whole step and draw_ms is ~0. */
+ * the sums.  rows_ms is the row-statistics kernel and draw_ms the draw kernel,
+ * each stamped by its own dispatch (start to end of the kernel's execution, the
+ * gap between dispatches excluded). */
 int spec_verify_profile_read(sv_ctx *ctx, double *rows_ms, double *draw_ms, int32_t *count);
 
 /* Schedule the last successful spec_verify_run on this context launched. */
 enum sv_schedule {
     SV_SCHEDULE_NONE = 0,       /* no call yet, or the last call had batch == 0 */
     SV_SCHEDULE_SPLIT = 1,      /* rows kernel with per-row pieces (unaligned rows), draw kernel */
-    SV_SCHEDULE_FLAT = 2,       /* rows kernel over the flattened rows, draw kernel */
-    SV_SCHEDULE_ONE_LAUNCH = 3  /* one launch: rows, then draws, per workgroup */
+    SV_SCHEDULE_FLAT = 2        /* rows kernel over the flattened rows, draw kernel */
 };
 
 /* Writes the sv_schedule of the last successful run to *schedule.  Host-only

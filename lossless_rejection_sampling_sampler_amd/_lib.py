@@ -21,15 +21,14 @@ SV_ERR_OUT_OF_MEMORY = 2
 SV_ERR_DEVICE = 3
 SV_ERR_UNSUPPORTED = 4
 SV_ERR_CAPACITY = 5
+SV_ERR_DEVICE_CONTRACT = 6
 SV_F32 = 0
 SV_BF16 = 1
 SV_FLAG_PROFILE = 1
 SV_FLAG_TWO_KERNEL = 2
-SV_FLAG_ONE_LAUNCH = 4
 SV_DEVERR_DRAFT_ID = 1
 SV_DEVERR_OFFSETS = 2
 SV_DEVERR_NONFINITE = 4
-SV_DEVERR_STALLED = 8
 SV_DEVERR_TOPK = 16
 SV_MAX_GAMMA = 128
 SV_MAX_TOPK = 64
@@ -41,11 +40,9 @@ def stats_len(gamma: int) -> int:
 SV_SCHEDULE_NONE = 0
 SV_SCHEDULE_SPLIT = 1
 SV_SCHEDULE_FLAT = 2
-SV_SCHEDULE_ONE_LAUNCH = 3
 
-SCHEDULE_FLAGS = {None: 0, "auto": 0, "twokernel": SV_FLAG_TWO_KERNEL, "onelaunch": SV_FLAG_ONE_LAUNCH}
-SCHEDULE_NAMES = {SV_SCHEDULE_NONE: "none", SV_SCHEDULE_SPLIT: "rows-split+draw", SV_SCHEDULE_FLAT: "rows+draw",
-                  SV_SCHEDULE_ONE_LAUNCH: "one-launch"}
+SCHEDULE_FLAGS = {None: 0, "auto": 0, "twokernel": SV_FLAG_TWO_KERNEL}
+SCHEDULE_NAMES = {SV_SCHEDULE_NONE: "none", SV_SCHEDULE_SPLIT: "rows-split+draw", SV_SCHEDULE_FLAT: "rows+draw"}
 
 EXPORTS = (
     "spec_verify_create",

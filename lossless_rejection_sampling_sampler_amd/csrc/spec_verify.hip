@@ -4,6 +4,7 @@
 // Method: the spec-decoding page at dpshk.com/news/5598276, sections 3.1-3.2,
 // 5.2-5.4 and 8 (see the header for the operation and the readings).
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <algorithm>
 #include <cstdint>
@@ -19,7 +20,6 @@ namespace {
 constexpr int kRowVecsPerThread = 8;    // target 16-byte vectors per thread per row split
 constexpr int kProfileRing = 2048;      // calls between forced event folds
 constexpr int kDrawBlocksPerWave = 2;   // draw kernel: blocks per wave in straight-line code
-constexpr int kStepSlices = 1;          // one-launch step: request slices
 constexpr int kDrawPerCU = 3;           // draw kernel: workgroups per CU aimed at
 
 struct Geometry {
@@ -38,7 +38,7 @@ Geometry geometry_for(int vocab, int dtype) {
     return g;
 }
 
-// Workgroups for the flat rows stream (and the one-launch step): all resident at
+// Workgroups for the flat rows stream: all resident at
 // once, at least one batch of loads per thread or else one workgroup per row (a
 // small call is latency-bound: its rows then stream side by side), and no row
 // cut into more than kMaxPieces pieces.
@@ -54,22 +54,143 @@ int flat_workgroups(long nv, long vpr, int resident) {
     return static_cast<int>(std::max<long>(1, g));
 }
 
-// Rows kernel then draw kernel on `stream` (ev, when given, is recorded between them).
+// Rows kernel then draw kernel on `stream`.  ev, when given, holds four events
+// that the dispatches themselves stamp: rows start / end, draw start / end (the
+// kernels' own execution, without the gap between dispatches).
 template <typename E>
 int launch_rows_draw(bool aligned, bool loop, long grid1, long grid2, const sv::Params& P, hipStream_t stream,
-                     hipEvent_t ev) {
+                     const hipEvent_t* ev) {
     const dim3 g1((unsigned)grid1), g2((unsigned)grid2), blk(sv::kThreads);
+    hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
+    hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
     if (aligned)
-        hipLaunchKernelGGL(sv::rows_flat_kernel<E>, g1, blk, 0, stream, P);
+        hipExtLaunchKernelGGL(sv::rows_flat_kernel<E>, g1, blk, 0, stream, e0, e1, 0, P);
     else
-        hipLaunchKernelGGL(sv::rows_split_kernel<E>, g1, blk, 0, stream, P);
-    if (ev && hipEventRecord(ev, stream) != hipSuccess) return SV_ERR_DEVICE;
-    if (loop) hipLaunchKernelGGL((sv::draw_kernel<E, true>), g2, blk, 0, stream, P);
-    else hipLaunchKernelGGL((sv::draw_kernel<E, false>), g2, blk, 0, stream, P);
+        hipExtLaunchKernelGGL(sv::rows_split_kernel<E>, g1, blk, 0, stream, e0, e1, 0, P);
+    if (loop) hipExtLaunchKernelGGL((sv::draw_kernel<E, true>), g2, blk, 0, stream, e2, e3, 0, P);
+    else hipExtLaunchKernelGGL((sv::draw_kernel<E, false>), g2, blk, 0, stream, e2, e3, 0, P);
     return SV_OK;
 }
 
 static_assert(SV_MAX_GAMMA + 1 <= sv::kMaxReqRows, "a request's rows fit the draw kernel's resolve");
+
+// Scratch the kernels of one call use (device memory) and the host-mapped
+// contract word (may be null).
+struct Scratch {
+    sv::Piece* parts;
+    sv::RowStat* rows;
+    sv::DrawTask* tasks;
+    sv::BlockRec* recs;
+    uint32_t* draw_cnt;
+    uint32_t* err;
+    uint32_t* err_host;
+};
+
+// Host-visible argument checks (nothing is enqueued unless SV_OK); *qmode
+// receives how q is given.
+int check_args(int max_batch, int max_gamma, int vocab, int dtype, const sv_args* a, int* qmode) {
+    if (a->batch < 0 || a->gamma < 0 || a->total_draft < 0) return SV_ERR_INVALID_ARG;
+    *qmode = sv::kQDense;
+    if (a->batch == 0) return SV_OK;
+    if (a->batch > max_batch || a->gamma > max_gamma) return SV_ERR_CAPACITY;
+    if (a->vocab != vocab) return SV_ERR_INVALID_ARG;   // one vocabulary for draft and target
+    if ((long)a->total_draft > (long)a->batch * a->gamma) return SV_ERR_INVALID_ARG;
+    if (!a->draft_offsets && a->total_draft != a->batch * a->gamma) return SV_ERR_INVALID_ARG;
+    if (!a->target_logits || !a->temperature || !a->uniforms || !a->out_tokens || !a->out_num_accepted)
+        return SV_ERR_INVALID_ARG;
+    if (a->total_draft > 0 && !a->draft_ids) return SV_ERR_INVALID_ARG;
+    // q: dense rows, sparse (id, prob) entries, or point masses at the drafted tokens
+    if (!a->draft_probs) {
+        if (a->draft_topk < 0 || a->draft_topk > SV_MAX_TOPK) return SV_ERR_INVALID_ARG;
+        *qmode = a->draft_topk > 0 ? sv::kQSparse : sv::kQPoint;
+        if (*qmode == sv::kQSparse && a->total_draft > 0 && (!a->draft_topk_ids || !a->draft_topk_probs))
+            return SV_ERR_INVALID_ARG;
+        if (reinterpret_cast<uintptr_t>(a->draft_topk_ids) % 4 || reinterpret_cast<uintptr_t>(a->draft_topk_probs) % 4)
+            return SV_ERR_INVALID_ARG;
+    }
+    if (reinterpret_cast<uintptr_t>(a->stats) % 4) return SV_ERR_INVALID_ARG;
+    const size_t esize = (dtype == SV_BF16) ? 2 : 4;
+    if (reinterpret_cast<uintptr_t>(a->target_logits) % esize) return SV_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(a->draft_probs) % 4 || reinterpret_cast<uintptr_t>(a->draft_ids) % 4)
+        return SV_ERR_INVALID_ARG;
+    return SV_OK;
+}
+
+// Enqueues the rows kernel and the draw kernel of one checked call (batch > 0)
+// on `stream`; `ev` (null, or four events) times the two dispatches.  *schedule
+// receives the SV_SCHEDULE_* launched.
+int enqueue(const Geometry& geo, int resident_flat, int cus, int resident_draw, int dtype, const Scratch& sc,
+            const sv_args* a, int qmode, hipStream_t stream, const hipEvent_t* ev, int* schedule) {
+    const size_t esize = (dtype == SV_BF16) ? 2 : 4;
+    sv::Params P;
+    P.logits = a->target_logits;
+    P.q = a->draft_probs;
+    P.ids = a->draft_ids;
+    P.temperature = a->temperature;
+    P.uniforms = a->uniforms;
+    P.offsets = a->draft_offsets;
+    P.out_tokens = a->out_tokens;
+    P.out_num = a->out_num_accepted;
+    P.diag_m = a->diag_row_max;
+    P.diag_z = a->diag_row_norm;
+    P.diag_r = a->diag_ratio;
+    P.qmode = qmode;
+    P.topk = qmode == sv::kQSparse ? a->draft_topk : 0;
+    P.topk_ids = qmode == sv::kQSparse ? a->draft_topk_ids : nullptr;
+    P.topk_probs = qmode == sv::kQSparse ? a->draft_topk_probs : nullptr;
+    P.stats = a->stats;
+    P.batch = a->batch;
+    P.gamma = a->gamma;
+    P.total_draft = a->total_draft;
+    P.vocab = a->vocab;
+    P.splits = geo.splits;
+    P.nblocks = geo.nblocks;
+    // draw workgroups per request: three per CU over the call (one resident
+    // round) where that keeps between one and kDrawBlocksPerWave blocks per
+    // wave (an even count per CU balances the fp64 work across the SIMDs).  A
+    // call with more draw rows than that round can hold at two blocks per wave
+    // (B = 128 or 256 at V = 151936 / 128256) takes a second round of
+    // workgroups when its residual blocks stream a dense q row too; with sparse
+    // or point-mass q (every block streams logits only, so a workgroup's
+    // fixed latency outweighs its bytes) its waves take pairs of blocks in a
+    // loop instead (measured: 100 against 110 us at B = 256 with top-50 lists,
+    // 114 against 109 us with dense q)
+    const int c_min = std::max(1, (geo.nblocks + sv::kWaves * kDrawBlocksPerWave - 1) /
+                                      (sv::kWaves * kDrawBlocksPerWave));
+    const int c_max = std::max(1, (geo.nblocks + sv::kWaves - 1) / sv::kWaves);
+    const int c_fit = kDrawPerCU * cus / a->batch;
+    const bool draw_loop = c_fit < c_min && qmode != sv::kQDense;
+    const int C = draw_loop ? std::max(1, c_fit) : std::max(c_min, std::min(c_max, c_fit));
+    P.draw_wgs = C;
+    P.parts = sc.parts;
+    P.rows = sc.rows;
+    P.tasks = sc.tasks;
+    P.recs = sc.recs;
+    P.draw_cnt = sc.draw_cnt;
+    P.err = sc.err;
+    P.err_host = sc.err_host;
+
+    const long rows = (long)a->total_draft + a->batch;
+    // rows start on 16-byte boundaries: stream the flattened rows in equal ranges
+    const bool aligned = (reinterpret_cast<uintptr_t>(a->target_logits) % 16 == 0) &&
+                         (((long)a->vocab * (long)esize) % 16 == 0);
+    P.flat_vpr = (long)a->vocab * (long)esize / 16;
+    P.flat_nv = rows * P.flat_vpr;
+    const long grid1 = aligned ? flat_workgroups(P.flat_nv, P.flat_vpr, resident_flat) : rows * P.splits;
+    const long grid2 = (long)a->batch * C;
+    P.rows_grid = static_cast<int>(grid1);
+    P.draw_cmajor = grid2 <= resident_draw ? 1 : 0;
+    // rows are streamed without any hand-off between workgroups (flattened
+    // ranges for 16-byte aligned rows, per-row splits otherwise) and every
+    // request is resolved by its draw workgroups
+    P.split_pieces = aligned ? 0 : P.splits;
+    const int st = (dtype == SV_BF16)
+                       ? launch_rows_draw<sv::BF16>(aligned, draw_loop, grid1, grid2, P, stream, ev)
+                       : launch_rows_draw<sv::F32>(aligned, draw_loop, grid1, grid2, P, stream, ev);
+    if (st != SV_OK) return st;
+    *schedule = aligned ? SV_SCHEDULE_FLAT : SV_SCHEDULE_SPLIT;
+    return SV_OK;
+}
 
 }  // namespace
 
@@ -80,23 +201,25 @@ struct sv_ctx {
     int max_rows = 0;
     int resident_flat = 0;     // rows-flat workgroups resident at once on the device
     int cus = 0;               // compute units of the device
-    int resident_step = 0;     // one-launch workgroups resident at once
     int resident_draw = 0;     // draw workgroups resident at once
-    uint32_t epoch = 0;        // tag of the one-launch step's draw tasks
     int last_schedule = SV_SCHEDULE_NONE;
-    uint32_t* task_tag = nullptr;
     // device scratch (one allocation)
     void* scratch = nullptr;
     sv::Piece* parts = nullptr;
     sv::RowStat* rows = nullptr;
     sv::DrawTask* tasks = nullptr;
     sv::BlockRec* recs = nullptr;
-    uint32_t* row_cnt = nullptr;
-    uint32_t* req_cnt = nullptr;
     uint32_t* draw_cnt = nullptr;
     uint32_t* err = nullptr;
+    // host-mapped pinned word the kernels set on a contract violation (checked by run)
+    uint32_t* err_host = nullptr;
+    uint32_t* err_host_dev = nullptr;   // its device-side address
+    uint32_t* err_read = nullptr;       // pinned staging word for spec_verify_device_errors
+    hipStream_t aux = nullptr;          // internal non-blocking stream: clears and reads of the error word
+    hipEvent_t done = nullptr;          // recorded after every eager run on the caller's stream
+    bool done_recorded = false;
     // profiling
-    std::vector<hipEvent_t> events;    // 3 per call
+    std::vector<hipEvent_t> events;    // 4 per call: rows start / end, draw start / end
     int prof_n = 0;
     double prof_rows_ms = 0.0, prof_draw_ms = 0.0;
     int prof_calls = 0;
@@ -108,11 +231,11 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int fold_profile(sv_ctx* ctx) {
     if (ctx->prof_n == 0) return SV_OK;
-    if (hipEventSynchronize(ctx->events[3 * (ctx->prof_n - 1) + 2]) != hipSuccess) return SV_ERR_DEVICE;
+    if (hipEventSynchronize(ctx->events[4 * (ctx->prof_n - 1) + 3]) != hipSuccess) return SV_ERR_DEVICE;
     for (int i = 0; i < ctx->prof_n; ++i) {
         float a = 0.f, b = 0.f;
-        if (hipEventElapsedTime(&a, ctx->events[3 * i], ctx->events[3 * i + 1]) != hipSuccess ||
-            hipEventElapsedTime(&b, ctx->events[3 * i + 1], ctx->events[3 * i + 2]) != hipSuccess)
+        if (hipEventElapsedTime(&a, ctx->events[4 * i], ctx->events[4 * i + 1]) != hipSuccess ||
+            hipEventElapsedTime(&b, ctx->events[4 * i + 2], ctx->events[4 * i + 3]) != hipSuccess)
             return SV_ERR_DEVICE;
         ctx->prof_rows_ms += a;
         ctx->prof_draw_ms += b;
@@ -128,9 +251,21 @@ void free_ctx(sv_ctx* ctx) {
     (void)hipGetDevice(&prev);
     (void)hipSetDevice(ctx->device);
     for (hipEvent_t e : ctx->events) (void)hipEventDestroy(e);
+    if (ctx->done) (void)hipEventDestroy(ctx->done);
+    if (ctx->aux) (void)hipStreamDestroy(ctx->aux);
+    if (ctx->err_host) (void)hipHostFree(ctx->err_host);
+    if (ctx->err_read) (void)hipHostFree(ctx->err_read);
     if (ctx->scratch) (void)hipFree(ctx->scratch);
     (void)hipSetDevice(prev);
     delete ctx;
+}
+
+// Waits for the last eagerly launched call of this context (its stream up to that
+// call) and for the context's internal stream; no other stream is waited for.
+int wait_context(sv_ctx* ctx) {
+    if (ctx->done_recorded && hipEventSynchronize(ctx->done) != hipSuccess) return SV_ERR_DEVICE;
+    if (ctx->aux && hipStreamSynchronize(ctx->aux) != hipSuccess) return SV_ERR_DEVICE;
+    return SV_OK;
 }
 
 struct DeviceGuard {
@@ -158,6 +293,7 @@ const char* spec_verify_status_string(int status) {
         case SV_ERR_DEVICE: return "HIP device error";
         case SV_ERR_UNSUPPORTED: return "unsupported configuration";
         case SV_ERR_CAPACITY: return "exceeds the context's limits";
+        case SV_ERR_DEVICE_CONTRACT: return "an earlier call broke the device-side contract";
         default: return "unknown status";
     }
 }
@@ -198,12 +334,6 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_draw, sv::draw_kernel<sv::BF16, false>,
                                                          sv::kThreads, 0) == hipSuccess)
             ctx->resident_draw = cus * per_draw;
-        int per_bf16 = 0, per_f32 = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_bf16, sv::step_kernel<sv::BF16>, sv::kThreads, 0) ==
-                hipSuccess &&
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_f32, sv::step_kernel<sv::F32>, sv::kThreads, 0) ==
-                hipSuccess)
-            ctx->resident_step = cus * std::min(per_bf16, per_f32);
         (void)hipGetLastError();
     }
     const size_t n_rows = (size_t)ctx->max_rows;
@@ -213,8 +343,7 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
     const size_t o_rows = off;  off = align_up(off + n_rows * sizeof(sv::RowStat), 256);
     const size_t o_tasks = off; off = align_up(off + n_b * sizeof(sv::DrawTask), 256);
     const size_t o_recs = off;  off = align_up(off + n_b * ctx->geo.nblocks * sizeof(sv::BlockRec), 256);
-    const size_t o_cnt = off;   off = align_up(off + (n_rows + 2 * n_b + 1) * sizeof(uint32_t), 256);
-    const size_t o_tag = off;   off = align_up(off + n_b * sizeof(uint32_t), 256);
+    const size_t o_cnt = off;   off = align_up(off + (n_b + 1) * sizeof(uint32_t), 256);
     const size_t total = off;
     if (hipMalloc(&ctx->scratch, total) != hipSuccess) {
         (void)hipGetLastError();
@@ -226,17 +355,28 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
     ctx->rows = reinterpret_cast<sv::RowStat*>(base + o_rows);
     ctx->tasks = reinterpret_cast<sv::DrawTask*>(base + o_tasks);
     ctx->recs = reinterpret_cast<sv::BlockRec*>(base + o_recs);
-    ctx->row_cnt = reinterpret_cast<uint32_t*>(base + o_cnt);
-    ctx->req_cnt = ctx->row_cnt + n_rows;
-    ctx->draw_cnt = ctx->req_cnt + n_b;
+    ctx->draw_cnt = reinterpret_cast<uint32_t*>(base + o_cnt);
     ctx->err = ctx->draw_cnt + n_b;
-    ctx->task_tag = reinterpret_cast<uint32_t*>(base + o_tag);
-    if (hipMemset(ctx->scratch, 0, total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    if (hipHostMalloc(reinterpret_cast<void**>(&ctx->err_host), sizeof(uint32_t),
+                      hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess ||
+        hipHostMalloc(reinterpret_cast<void**>(&ctx->err_read), sizeof(uint32_t), hipHostMallocDefault) != hipSuccess) {
+        (void)hipGetLastError();
+        free_ctx(ctx);
+        return SV_ERR_OUT_OF_MEMORY;
+    }
+    *reinterpret_cast<volatile uint32_t*>(ctx->err_host) = 0u;
+    if (hipHostGetDevicePointer(reinterpret_cast<void**>(&ctx->err_host_dev), ctx->err_host, 0) != hipSuccess ||
+        hipStreamCreateWithFlags(&ctx->aux, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ctx->done, hipEventDisableTiming) != hipSuccess) {
+        free_ctx(ctx);
+        return SV_ERR_DEVICE;
+    }
+    if (hipMemsetAsync(ctx->scratch, 0, total, ctx->aux) != hipSuccess || hipStreamSynchronize(ctx->aux) != hipSuccess) {
         free_ctx(ctx);
         return SV_ERR_DEVICE;
     }
     if (cfg->flags & SV_FLAG_PROFILE) {
-        ctx->events.resize(3 * kProfileRing, nullptr);
+        ctx->events.resize(4 * kProfileRing, nullptr);
         for (auto& e : ctx->events) {
             if (hipEventCreate(&e) != hipSuccess) {
                 e = nullptr;
@@ -253,7 +393,7 @@ int spec_verify_destroy(sv_ctx* ctx) {
     if (!ctx) return SV_OK;
     {
         DeviceGuard guard(ctx->device);
-        (void)hipDeviceSynchronize();
+        (void)wait_context(ctx);
     }
     free_ctx(ctx);
     return SV_OK;
@@ -261,157 +401,53 @@ int spec_verify_destroy(sv_ctx* ctx) {
 
 int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
     if (!ctx || !a) return SV_ERR_INVALID_ARG;
+    // a violation the device has reported (host-mapped word) blocks further calls
+    // until spec_verify_device_errors clears it
+    if (*reinterpret_cast<volatile uint32_t*>(ctx->err_host) != 0u) return SV_ERR_DEVICE_CONTRACT;
     const sv_config& cfg = ctx->cfg;
-    if (a->batch < 0 || a->gamma < 0 || a->total_draft < 0) return SV_ERR_INVALID_ARG;
+    int qmode = 0;
+    const int st0 = check_args(cfg.max_batch, cfg.max_gamma, cfg.vocab, cfg.logits_dtype, a, &qmode);
+    if (st0 != SV_OK) return st0;
     if (a->batch == 0) {
         ctx->last_schedule = SV_SCHEDULE_NONE;
         return SV_OK;
     }
-    if (a->batch > cfg.max_batch || a->gamma > cfg.max_gamma) return SV_ERR_CAPACITY;
-    if (a->vocab != cfg.vocab) return SV_ERR_INVALID_ARG;   // one vocabulary for draft and target
-    if ((long)a->total_draft > (long)a->batch * a->gamma) return SV_ERR_INVALID_ARG;
-    if (!a->draft_offsets && a->total_draft != a->batch * a->gamma) return SV_ERR_INVALID_ARG;
-    if (!a->target_logits || !a->temperature || !a->uniforms || !a->out_tokens || !a->out_num_accepted)
-        return SV_ERR_INVALID_ARG;
-    if (a->total_draft > 0 && !a->draft_ids) return SV_ERR_INVALID_ARG;
-    // q: dense rows, sparse (id, prob) entries, or point masses at the drafted tokens
-    int qmode = sv::kQDense;
-    if (!a->draft_probs) {
-        if (a->draft_topk < 0 || a->draft_topk > SV_MAX_TOPK) return SV_ERR_INVALID_ARG;
-        qmode = a->draft_topk > 0 ? sv::kQSparse : sv::kQPoint;
-        if (qmode == sv::kQSparse && a->total_draft > 0 && (!a->draft_topk_ids || !a->draft_topk_probs))
-            return SV_ERR_INVALID_ARG;
-        if (reinterpret_cast<uintptr_t>(a->draft_topk_ids) % 4 || reinterpret_cast<uintptr_t>(a->draft_topk_probs) % 4)
-            return SV_ERR_INVALID_ARG;
-    }
-    if (reinterpret_cast<uintptr_t>(a->stats) % 4) return SV_ERR_INVALID_ARG;
-    const size_t esize = (cfg.logits_dtype == SV_BF16) ? 2 : 4;
-    if (reinterpret_cast<uintptr_t>(a->target_logits) % esize) return SV_ERR_INVALID_ARG;
-    if (reinterpret_cast<uintptr_t>(a->draft_probs) % 4 || reinterpret_cast<uintptr_t>(a->draft_ids) % 4)
-        return SV_ERR_INVALID_ARG;
-
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
     DeviceGuard guard(ctx->device);
 
-    sv::Params P;
-    P.logits = a->target_logits;
-    P.q = a->draft_probs;
-    P.ids = a->draft_ids;
-    P.temperature = a->temperature;
-    P.uniforms = a->uniforms;
-    P.offsets = a->draft_offsets;
-    P.out_tokens = a->out_tokens;
-    P.out_num = a->out_num_accepted;
-    P.diag_m = a->diag_row_max;
-    P.diag_z = a->diag_row_norm;
-    P.diag_r = a->diag_ratio;
-    P.qmode = qmode;
-    P.topk = qmode == sv::kQSparse ? a->draft_topk : 0;
-    P.topk_ids = qmode == sv::kQSparse ? a->draft_topk_ids : nullptr;
-    P.topk_probs = qmode == sv::kQSparse ? a->draft_topk_probs : nullptr;
-    P.stats = a->stats;
-    P.batch = a->batch;
-    P.gamma = a->gamma;
-    P.total_draft = a->total_draft;
-    P.vocab = a->vocab;
-    P.splits = ctx->geo.splits;
-    P.nblocks = ctx->geo.nblocks;
-    // draw workgroups per request: three per CU over the call (one resident
-    // round) where that keeps between one and kDrawBlocksPerWave blocks per
-    // wave (an even count per CU balances the fp64 work across the SIMDs).  A
-    // call with more draw rows than that round can hold at two blocks per wave
-    // (B = 128 or 256 at V = 151936 / 128256) takes a second round of
-    // workgroups when its residual blocks stream a dense q row too; with sparse
-    // or point-mass q (every block streams logits only, so a workgroup's
-    // fixed latency outweighs its bytes) its waves take pairs of blocks in a
-    // loop instead (measured: 100 against 110 us at B = 256 with top-50 lists,
-    // 114 against 109 us with dense q)
-    const int c_min = std::max(1, (ctx->geo.nblocks + sv::kWaves * kDrawBlocksPerWave - 1) /
-                                      (sv::kWaves * kDrawBlocksPerWave));
-    const int c_max = std::max(1, (ctx->geo.nblocks + sv::kWaves - 1) / sv::kWaves);
-    const int c_fit = kDrawPerCU * ctx->cus / a->batch;
-    const bool draw_loop = c_fit < c_min && qmode != sv::kQDense;
-    const int C = draw_loop ? std::max(1, c_fit) : std::max(c_min, std::min(c_max, c_fit));
-    P.draw_wgs = C;
-    P.parts = ctx->parts;
-    P.rows = ctx->rows;
-    P.tasks = ctx->tasks;
-    P.recs = ctx->recs;
-    P.row_cnt = ctx->row_cnt;
-    P.req_cnt = ctx->req_cnt;
-    P.draw_cnt = ctx->draw_cnt;
-    P.err = ctx->err;
-    P.task_tag = nullptr;
-    P.epoch = 0;
-    P.slices = 1;
-    P.rows_grid = 0;
-    P.split_pieces = 0;
-    P.draw_cmajor = 0;
-
-    const long rows = (long)a->total_draft + a->batch;
-    // rows start on 16-byte boundaries: stream the flattened rows in equal ranges
-    const bool aligned = (reinterpret_cast<uintptr_t>(a->target_logits) % 16 == 0) &&
-                         (((long)a->vocab * (long)esize) % 16 == 0);
-    P.flat_vpr = (long)a->vocab * (long)esize / 16;
-    P.flat_nv = rows * P.flat_vpr;
-
-    // the one-launch step is opt-in until it beats the two-kernel schedule
-    const bool one_launch = aligned && (cfg.flags & SV_FLAG_ONE_LAUNCH) && !(cfg.flags & SV_FLAG_TWO_KERNEL) &&
-                            ctx->resident_step > 0;
+    Scratch sc;
+    sc.parts = ctx->parts;
+    sc.rows = ctx->rows;
+    sc.tasks = ctx->tasks;
+    sc.recs = ctx->recs;
+    sc.draw_cnt = ctx->draw_cnt;
+    sc.err = ctx->err;
+    sc.err_host = ctx->err_host_dev;
 
     const bool prof = (cfg.flags & SV_FLAG_PROFILE) != 0;
     if (prof && ctx->prof_n == kProfileRing) {
         const int st = fold_profile(ctx);
         if (st != SV_OK) return st;
     }
-    hipEvent_t* ev = prof ? &ctx->events[3 * ctx->prof_n] : nullptr;
-    if (prof && hipEventRecord(ev[0], stream) != hipSuccess) return SV_ERR_DEVICE;
-    if (one_launch) {
-        if (++ctx->epoch == 0) ctx->epoch = 1;
-        P.task_tag = ctx->task_tag;
-        P.epoch = ctx->epoch;
-        P.slices = std::max(1, std::min(kStepSlices, a->batch));
-        // every slice is split over the whole grid: about one batch of loads per
-        // thread per slice, and no row cut into more than kMaxPieces pieces even
-        // in the smallest slice the offsets allow (a request has at least one row)
-        const long rows_per_req_min = a->draft_offsets ? 1 : (long)a->gamma + 1;
-        const long slice_min_nv = (long)(a->batch / P.slices) * rows_per_req_min * P.flat_vpr;
-        long grid = std::min<long>(ctx->resident_step,
-                                   std::max<long>(1, P.flat_nv / ((long)P.slices * sv::kThreads * sv::kRowUnroll)));
-        while (grid > 1) {
-            const long lmin = slice_min_nv / grid;
-            if (lmin > 0 && (P.flat_vpr + lmin - 1) / lmin + 1 <= sv::kMaxPieces) break;
-            --grid;
-        }
-        // an ordinary launch: the grid never exceeds what the device holds at once
-        // (a cooperative launch would guarantee it, at a cost of microseconds per call)
-        if (cfg.logits_dtype == SV_BF16)
-            hipLaunchKernelGGL(sv::step_kernel<sv::BF16>, dim3((unsigned)grid), dim3(sv::kThreads), 0, stream, P);
-        else
-            hipLaunchKernelGGL(sv::step_kernel<sv::F32>, dim3((unsigned)grid), dim3(sv::kThreads), 0, stream, P);
-        if (prof && hipEventRecord(ev[1], stream) != hipSuccess) return SV_ERR_DEVICE;
-    } else {
-        const long grid1 = aligned ? flat_workgroups(P.flat_nv, P.flat_vpr, ctx->resident_flat) : rows * P.splits;
-        const long grid2 = (long)a->batch * C;
-        P.rows_grid = static_cast<int>(grid1);
-        P.draw_cmajor = grid2 <= ctx->resident_draw ? 1 : 0;
-        // rows are streamed without any hand-off between workgroups (flattened
-        // ranges for 16-byte aligned rows, per-row splits otherwise) and every
-        // request is resolved by its draw workgroups
-        P.split_pieces = aligned ? 0 : P.splits;
-        const int st = (cfg.logits_dtype == SV_BF16)
-                           ? launch_rows_draw<sv::BF16>(aligned, draw_loop, grid1, grid2, P, stream,
-                                                        prof ? ev[1] : nullptr)
-                           : launch_rows_draw<sv::F32>(aligned, draw_loop, grid1, grid2, P, stream,
-                                                       prof ? ev[1] : nullptr);
-        if (st != SV_OK) return st;
-    }
-    if (prof) {
-        if (hipEventRecord(ev[2], stream) != hipSuccess) return SV_ERR_DEVICE;
-        ctx->prof_n++;
-    }
+    const hipEvent_t* ev = prof ? &ctx->events[4 * ctx->prof_n] : nullptr;
+    int schedule = SV_SCHEDULE_NONE;
+    const int st = enqueue(ctx->geo, ctx->resident_flat, ctx->cus, ctx->resident_draw, cfg.logits_dtype, sc, a,
+                           qmode, stream, ev, &schedule);
+    if (st != SV_OK) return st;
     if (hipGetLastError() != hipSuccess) return SV_ERR_DEVICE;
-    ctx->last_schedule = one_launch ? SV_SCHEDULE_ONE_LAUNCH : (aligned ? SV_SCHEDULE_FLAT : SV_SCHEDULE_SPLIT);
+    if (prof) ctx->prof_n++;
+    // remember where this call ends on its stream (not while a graph is being
+    // captured: a replay is waited for by the caller)
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
+        (void)hipGetLastError();
+        cap = hipStreamCaptureStatusNone;
+    }
+    if (cap == hipStreamCaptureStatusNone) {
+        if (hipEventRecord(ctx->done, stream) != hipSuccess) return SV_ERR_DEVICE;
+        ctx->done_recorded = true;
+    }
+    ctx->last_schedule = schedule;
     return SV_OK;
 }
 
@@ -424,14 +460,16 @@ int spec_verify_last_schedule(const sv_ctx* ctx, int32_t* schedule) {
 int spec_verify_device_errors(sv_ctx* ctx, uint32_t* bits, int clear) {
     if (!ctx || !bits) return SV_ERR_INVALID_ARG;
     DeviceGuard guard(ctx->device);
-    if (hipDeviceSynchronize() != hipSuccess) return SV_ERR_DEVICE;
-    if (hipMemcpy(bits, ctx->err, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess) return SV_ERR_DEVICE;
+    if (wait_context(ctx) != SV_OK) return SV_ERR_DEVICE;
+    if (hipMemcpyAsync(ctx->err_read, ctx->err, sizeof(uint32_t), hipMemcpyDeviceToHost, ctx->aux) != hipSuccess ||
+        hipStreamSynchronize(ctx->aux) != hipSuccess)
+        return SV_ERR_DEVICE;
+    *bits = *ctx->err_read | *reinterpret_cast<volatile uint32_t*>(ctx->err_host);
     if (clear) {
-        // also drop arrival counts a call with inconsistent offsets may have left behind
-        const size_t n = (size_t)ctx->max_rows + 2 * (size_t)ctx->cfg.max_batch + 1;
-        if (hipMemset(ctx->row_cnt, 0, n * sizeof(uint32_t)) != hipSuccess ||
-            hipDeviceSynchronize() != hipSuccess)
+        if (hipMemsetAsync(ctx->err, 0, sizeof(uint32_t), ctx->aux) != hipSuccess ||
+            hipStreamSynchronize(ctx->aux) != hipSuccess)
             return SV_ERR_DEVICE;
+        *reinterpret_cast<volatile uint32_t*>(ctx->err_host) = 0u;
     }
     return SV_OK;
 }

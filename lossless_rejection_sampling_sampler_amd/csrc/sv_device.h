@@ -31,10 +31,8 @@
 //                block scan, rescans that block token by token and writes the
 //                token.
 //
-// An opt-in one-launch schedule (step_kernel) merges and resolves rows inside
-// the same launch through per-row / per-request arrival counters; see the note
-// at wait_stores().  Its counters are reset by their last arrival, so every call
-// leaves the scratch ready for the next.
+// The draw kernel's arrival counters are reset by their last arrival, so every
+// call leaves the scratch ready for the next.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -67,7 +65,7 @@ constexpr double kQFloor = 1e-10;        // page section 5.2: q is floored at 1e
 constexpr double kSignMargin = 1e-5;
 
 enum : int { kDrawNone = 0, kDrawResidual = 1, kDrawBonus = 2, kDrawDegenerate = 3 };
-enum : uint32_t { kErrDraftId = 1u, kErrOffsets = 2u, kErrNonFinite = 4u, kErrStalled = 8u, kErrTopk = 16u };
+enum : uint32_t { kErrDraftId = 1u, kErrOffsets = 2u, kErrNonFinite = 4u, kErrTopk = 16u };
 // How q is given: dense rows [D, V]; sparse (id, prob) entries [D, topk] with q = 0
 // off the list; or a point mass at the drafted token (q(x_i) = 1, a draft proposed
 // without a draft model).
@@ -98,9 +96,6 @@ struct DrawTask {        // written by the resolving workgroup, read by the draw
     float m;             // the draw row's max logit
     double z32;          // the draw row's normaliser (fp32 exponentials)
 };
-
-__device__ __forceinline__ void store_task(DrawTask* p, const DrawTask& t);
-__device__ __forceinline__ DrawTask load_task(const DrawTask* p);
 
 struct BlockRec {        // per (request, draw block) sums
     double se;           // sum of e = exp((l - m) / T) in fp64
@@ -146,15 +141,9 @@ struct Params {
     RowStat* rows;
     DrawTask* tasks;
     BlockRec* recs;
-    uint32_t* row_cnt;
-    uint32_t* req_cnt;
     uint32_t* draw_cnt;
-    uint32_t* err;
-    // phased one-launch step: request b's draw task is complete once
-    // task_tag[b] == epoch (nonzero, new every call)
-    uint32_t* task_tag;
-    uint32_t epoch;
-    int slices;          // one-launch step: request slices
+    uint32_t* err;       // sticky contract-violation word (device)
+    uint32_t* err_host;  // host-mapped copy the host checks before a call, or nullptr
 };
 
 // ----------------------------------------------------------------- element types
@@ -232,28 +221,12 @@ __device__ __forceinline__ void reset_counter(uint32_t* cnt) {
 __device__ __forceinline__ void count_add(uint32_t* p, uint32_t v) {
     __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void flag_error(uint32_t* err, uint32_t bits) {
-    __hip_atomic_fetch_or(err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_task(DrawTask* p, const DrawTask& t) {
-    st_coherent(&p->kind, t.kind);
-    st_coherent(&p->row, t.row);
-    st_coherent(&p->drow, t.drow);
-    st_coherent(&p->pos, t.pos);
-    st_coherent(&p->v, t.v);
-    st_coherent(&p->m, t.m);
-    st_coherent(&p->z32, t.z32);
-}
-__device__ __forceinline__ DrawTask load_task(const DrawTask* p) {
-    DrawTask t;
-    t.kind = ld_coherent(&p->kind);
-    t.row = ld_coherent(&p->row);
-    t.drow = ld_coherent(&p->drow);
-    t.pos = ld_coherent(&p->pos);
-    t.v = ld_coherent(&p->v);
-    t.m = ld_coherent(&p->m);
-    t.z32 = ld_coherent(&p->z32);
-    return t;
+// Sets contract-violation bits in the sticky device word and, when the caller
+// gave one, in the host-mapped word the host checks at its next call (a
+// system-scope store of the word's new value; rare path).
+__device__ __forceinline__ void flag_error(uint32_t* err, uint32_t* err_host, uint32_t bits) {
+    const uint32_t old = __hip_atomic_fetch_or(err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (err_host) __hip_atomic_store(err_host, old | bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 // ----------------------------------------------------------------- fp64 exp2
@@ -659,17 +632,15 @@ struct DraftTok {
 
 // Streams vectors [v0, v1) of target row t (vectors counted from the row's first
 // 16-byte aligned element), adds the scalar head (piece 0) and tail (last piece)
-// and publishes the piece.  Returns, in thread 0, the row's arrival count before
-// this piece (-1 for a row outside the request layout); the caller decides when
-// to look at it, so the counter's round trip can overlap further streaming.
-// The first batch of loads is issued before the request lookup, and the
-// drafted token's logit and q are read once the stream has been taken in, both
-// so that their round trips overlap other work.
-// kArrive = false (rows kernel whose merges are left to the next launch): no
-// arrival count; the piece is stored and, by the row's piece 0, the drafted
-// token's id, logit and q, for a later kernel to read.
-template <typename E, bool kArrive = true>
-__device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0, long v1, int piece, int npieces,
+// and stores the piece; the row's piece 0 also stores the drafted token's id,
+// logit and q for the draw kernel's resolve (x = -2 marks a draft row whose
+// sparse q breaks the contract: an entry id outside [-1, vocab) or the drafted
+// token listed twice).  The first batch of loads is issued before the request
+// lookup, and the drafted token's logit and q are read once the stream has been
+// taken in, both so that their round trips overlap other work.  No arrival is
+// counted: the launch boundary orders these stores before the next kernel.
+template <typename E>
+__device__ __forceinline__ void row_piece_publish(const Params& P, int t, long v0, long v1, int piece, int npieces,
                                                  RowShared& sh, DraftTok& dt) {
     const int tid = threadIdx.x;
     const int V = P.vocab;
@@ -691,15 +662,15 @@ __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0
 
     const RowMap rm = map_row(P, t, sh.red);
     if (!rm.ok) {
-        if (tid == 0 && piece == 0) flag_error(P.err, kErrOffsets);
-        return -1;
+        if (tid == 0 && piece == 0) flag_error(P.err, P.err_host, kErrOffsets);
+        return;
     }
     const int b = rm.b, i = rm.i, gb = rm.gb;
     const float T = rm.T;
     const bool greedy = !(T > 0.0f);
     const float c = greedy ? 0.0f : static_cast<float>(kLog2e / static_cast<double>(T));
     int xd = -1;
-    if (tid == 0 && !greedy && i < gb && (kArrive || piece == 0)) xd = P.ids[rm.d0 + i];
+    if (tid == 0 && !greedy && i < gb && piece == 0) xd = P.ids[rm.d0 + i];
 
     float mloc;          // piece max (sampled) / argmax value (greedy)
     int gloc = -1;       // argmax (greedy)
@@ -734,8 +705,9 @@ __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0
             dt.lx = E::load1(row, xd);
             dt.qx = (P.qmode == kQDense) ? P.q[(size_t)(rm.d0 + i) * V + xd] : 1.0f;
         }
-        if (P.qmode == kQSparse && i < gb && tid < 64) {
-            // wave 0 looks the drafted token up in its row's entries (absent: q = 0)
+        if (P.qmode == kQSparse && i < gb && piece == 0 && tid < 64) {
+            // wave 0 of the row's piece 0 looks the drafted token up in its row's
+            // entries (absent: q = 0) and checks every entry id
             const int xw = __builtin_amdgcn_readfirstlane(xd);
             float qv = 0.0f;
             if (xw >= 0 && xw < V) {
@@ -743,8 +715,12 @@ __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0
                 const int id = tid < P.topk ? P.topk_ids[e0 + tid] : -1;
                 const float pr = tid < P.topk ? P.topk_probs[e0 + tid] : 0.0f;
                 const unsigned long long hit = __ballot(id == xw);
+                const unsigned long long bad = __ballot(id < -1 || id >= V);
                 if (hit != 0ull) qv = rdlane(pr, __ffsll(static_cast<long long>(hit)) - 1);
-                if (tid == 0 && __popcll(hit) > 1) flag_error(P.err, kErrTopk);
+                if (__popcll(hit) > 1 || bad != 0ull) {
+                    if (tid == 0) flag_error(P.err, P.err_host, kErrTopk);
+                    dt.x = -2;
+                }
             }
             if (tid == 0) dt.qx = qv;
         }
@@ -793,169 +769,22 @@ __device__ __forceinline__ int row_piece_publish(const Params& P, int t, long v0
     }
 
     // ---- publish the piece
-    int old = 0;
     if (tid == 0) {
         // the launch geometry keeps piece < kMaxPieces for rows laid out as the
         // offsets promise; inconsistent offsets can break that, and are flagged
         if (piece >= kMaxPieces || npieces > kMaxPieces) {
-            flag_error(P.err, kErrOffsets);
-            return -1;
+            flag_error(P.err, P.err_host, kErrOffsets);
+            return;
         }
         Piece* pp = &P.parts[(size_t)t * kMaxPieces + piece];
         st_coherent(&pp->m, mloc);
         st_coherent(&pp->g, gloc);
         st_coherent(&pp->z, zloc);
-        if (kArrive) {
-            old = static_cast<int>(arrive(&P.row_cnt[t]));
-        } else if (piece == 0) {
+        if (piece == 0) {
             RowStat* rp = &P.rows[t];
             st_coherent(&rp->x, dt.x);
             st_coherent(&rp->lx, dt.lx);
             st_coherent(&rp->qx, dt.qx);
-            if (!greedy && i < gb && dt.x < 0) flag_error(P.err, kErrDraftId);
-        }
-    }
-    return old;
-}
-
-// Merge of row t by the workgroup that landed its last piece: row statistics,
-// the drafted token's logit and q, and, when it is the request's last row to
-// finish, the request's resolve (accept tests, first rejection, outputs, draw task).
-template <typename E>
-__device__ __forceinline__ void row_merge(const Params& P, int t, int npieces, const DraftTok& dt, RowShared& sh) {
-    const int tid = threadIdx.x;
-    const RowMap rm = map_row(P, t, sh.red);
-    if (!rm.ok) return;
-    const int b = rm.b, i = rm.i, gb = rm.gb;
-    const float T = rm.T;
-    const bool greedy = !(T > 0.0f);
-    const float c = greedy ? 0.0f : static_cast<float>(kLog2e / static_cast<double>(T));
-    if (tid == 0) reset_counter(&P.row_cnt[t]);
-
-    RowStat st;
-    st.pad = 0;
-    {
-        float mj = -INFINITY;
-        int gj = 0x7fffffff;
-        double zj = 0.0;
-        if (tid < npieces) {
-            const Piece* pp = &P.parts[(size_t)t * kMaxPieces + tid];
-            mj = ld_coherent(&pp->m);
-            gj = ld_coherent(&pp->g);
-            zj = ld_coherent(&pp->z);
-        }
-        if (!greedy) {
-            const float M = wg_max(mj, sh.red);
-            double zz = 0.0;
-            if (tid < npieces && mj > -INFINITY)
-                zz = zj * exp2((static_cast<double>(mj) - static_cast<double>(M)) * static_cast<double>(c));
-            st.m = M; st.g = -1; st.z = wg_sum(zz, sh.red);
-        } else {
-            wg_argmax(mj, gj, sh.red);
-            st.m = mj; st.g = gj; st.z = 0.0;
-        }
-    }
-    st.lx = 0.0f; st.qx = 0.0f; st.x = -1;
-    if (tid == 0) {
-        if (!greedy && i < gb) {
-            if (dt.x >= 0) {
-                st.x = dt.x;
-                st.lx = dt.lx;
-                st.qx = dt.qx;
-            } else {
-                flag_error(P.err, kErrDraftId);
-            }
-        }
-        RowStat* rp = &P.rows[t];
-        st_coherent(&rp->m, st.m);
-        st_coherent(&rp->g, st.g);
-        st_coherent(&rp->z, st.z);
-        st_coherent(&rp->lx, st.lx);
-        st_coherent(&rp->qx, st.qx);
-        st_coherent(&rp->x, st.x);
-        if (P.diag_m) P.diag_m[t] = st.m;
-        if (P.diag_z) P.diag_z[t] = greedy ? 0.0 : st.z;
-        sh.flag = (arrive(&P.req_cnt[b]) == static_cast<uint32_t>(gb));
-    }
-    __syncthreads();
-    if (!sh.flag) return;
-
-    // ---- resolve request b: accept tests, first rejection, outputs, draw task
-    const int G = P.gamma;
-    const int t0 = rm.d0 + b;
-    if (tid == 0) sh.k = gb;
-    __syncthreads();
-    int xj = -1;
-    if (tid < gb) xj = P.ids[rm.d0 + tid];
-    // every row's statistics (the bonus row's too, for the draw task)
-    float m_t = 0.0f;
-    double z_t = 0.0;
-    if (tid <= gb && !greedy) {
-        m_t = ld_coherent(&P.rows[t0 + tid].m);
-        z_t = ld_coherent(&P.rows[t0 + tid].z);
-    }
-    if (tid < gb) {
-        bool acc;
-        const RowStat* rs = &P.rows[t0 + tid];
-        if (greedy) {
-            const int g = ld_coherent(&rs->g);
-            acc = (xj == g);
-            if (P.diag_r) P.diag_r[rm.d0 + tid] = __uint_as_float(0x7fc00000u);
-        } else {
-            const float m = m_t;
-            const double Z = z_t;
-            const float lx = ld_coherent(&rs->lx);
-            const float qx = ld_coherent(&rs->qx);
-            const int xv = ld_coherent(&rs->x);
-            const double invT = 1.0 / static_cast<double>(T);
-            const double px = exp((static_cast<double>(lx) - static_cast<double>(m)) * invT) / Z;
-            const double r = px / fmax(static_cast<double>(qx), kQFloor);
-            const double u = static_cast<double>(P.uniforms[(size_t)b * (G + 2) + tid]);
-            acc = (xv >= 0) && (u < fmin(1.0, r));
-            if (P.diag_r) P.diag_r[rm.d0 + tid] = static_cast<float>(r);
-        }
-        if (!acc) atomicMin(&sh.k, tid);
-    }
-    __syncthreads();
-    const int k = sh.k;
-    if (tid == k) { sh.mk = m_t; sh.zk = z_t; }
-    if (P.stats) {
-        uint32_t* S = P.stats;
-        if (tid == 0) {
-            count_add(&S[0], 1u);
-            count_add(&S[1], static_cast<uint32_t>(gb));
-            count_add(&S[2], static_cast<uint32_t>(k));
-            if (k == gb) count_add(&S[3], 1u);
-            count_add(&S[4 + k], 1u);
-        }
-        if (tid < gb && tid <= k) count_add(&S[5 + G + tid], 1u);
-        if (tid < k) count_add(&S[5 + 2 * G + tid], 1u);
-    }
-    if (tid <= G) {
-        int tok = -1;
-        if (tid < k) tok = xj;
-        else if (tid == k && greedy) tok = ld_coherent(&P.rows[t0 + k].g);
-        // in a one-launch step the drawn token is stored by the select of the
-        // same launch, possibly on another XCD: a store here as well could land
-        // after it when the L2s write back, so that slot is left to the select
-        if (!(P.task_tag && tid == k && !greedy)) P.out_tokens[(size_t)b * (G + 1) + tid] = tok;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        P.out_num[b] = k;
-        DrawTask tk;
-        tk.kind = greedy ? kDrawNone : (k < gb ? kDrawResidual : kDrawBonus);
-        tk.row = t0 + k;
-        tk.drow = rm.d0 + k;
-        tk.pos = k;
-        tk.v = greedy ? 0.0f : P.uniforms[(size_t)b * (G + 2) + (k < gb ? G : G + 1)];
-        tk.m = sh.mk;
-        tk.z32 = sh.zk;
-        store_task(&P.tasks[b], tk);
-        reset_counter(&P.req_cnt[b]);        // every row of b has arrived: ready for the next call
-        if (P.task_tag) {
-            wait_stores();                   // the task is complete before its tag
-            st_coherent(&P.task_tag[b], P.epoch);
         }
     }
 }
@@ -975,61 +804,13 @@ __global__ __launch_bounds__(kThreads) void rows_split_kernel(Params P) {
     const long nvec = (V - head) / E::kPerVec;
     DraftTok dt;
     // pieces only: the draw kernel merges and resolves (P.split_pieces = S)
-    row_piece_publish<E, false>(P, t, (long)s * nvec / S, (long)(s + 1) * nvec / S, s, S, sh, dt);
+    row_piece_publish<E>(P, t, (long)s * nvec / S, (long)(s + 1) * nvec / S, s, S, sh, dt);
 }
 
 // Workgroup owning vector v when nv vectors are cut into g equal ranges
 // [floor(w nv / g), floor((w+1) nv / g)).
 __device__ __forceinline__ int range_owner(long v, long nv, int g) {
     return static_cast<int>(((v + 1) * (long)g - 1) / nv);
-}
-
-// Aligned rows kernel: the flattened [rows x vectors-per-row] stream is cut into
-// gridDim.x equal contiguous ranges; a range covers pieces of one or more rows.
-// A published piece whose arrival count is looked at later, so that the
-// counter's round trip overlaps further work.
-struct PendingMerge {
-    int t = -1, np = 0, old = 0;   // row, its pieces, arrival count before this piece (thread 0)
-    DraftTok dt;                   // the row's drafted token (thread 0)
-};
-
-// Runs row t's merge if the pending piece was its last to arrive.  Uniform call.
-template <typename E>
-__device__ __forceinline__ void settle_merge(const Params& P, PendingMerge& pm, RowShared& sh) {
-    if (pm.t < 0) return;
-    if (threadIdx.x == 0) sh.flag = (pm.old == pm.np - 1);
-    __syncthreads();
-    if (sh.flag) row_merge<E>(P, pm.t, pm.np, pm.dt, sh);
-    __syncthreads();
-    pm.t = -1;
-}
-
-// This workgroup's share of the aligned rows [r0, r1): their flattened [rows x
-// vectors-per-row] stream is cut into gridDim.x equal contiguous ranges (a range
-// covers pieces of one or more rows).  A piece's merge check waits until the
-// next piece has streamed; the last one is left in pm.
-template <typename E>
-__device__ __forceinline__ void rows_share(const Params& P, long r0, long r1, PendingMerge& pm, RowShared& sh) {
-    const int w = blockIdx.x;
-    const int G = gridDim.x;
-    const long VPR = P.flat_vpr, NV = (r1 - r0) * VPR;
-    const long a = (long)w * NV / G, e = (long)(w + 1) * NV / G;
-    long r = a / VPR;
-    for (long s0 = a; s0 < e; ++r) {
-        const long rs = r * VPR, re = rs + VPR;
-        const long s1 = e < re ? e : re;
-        const int wf = range_owner(rs, NV, G), wl = range_owner(re - 1, NV, G);
-        const int np = wl - wf + 1;
-        DraftTok dt;
-        const int old = row_piece_publish<E>(P, static_cast<int>(r0 + r), s0 - rs, s1 - rs, w - wf, np, sh, dt);
-        __syncthreads();
-        settle_merge<E>(P, pm, sh);
-        pm.t = static_cast<int>(r0 + r);
-        pm.np = np;
-        pm.old = old;
-        pm.dt = dt;
-        s0 = s1;
-    }
 }
 
 // Rows streamed only: every piece of this workgroup's range is stored
@@ -1049,7 +830,7 @@ __global__ __launch_bounds__(kThreads) void rows_flat_kernel(Params P) {
         const long s1 = e < re ? e : re;
         const int wf = range_owner(rs, NV, G), wl = range_owner(re - 1, NV, G);
         DraftTok dt;
-        row_piece_publish<E, false>(P, static_cast<int>(r), s0 - rs, s1 - rs, w - wf, wl - wf + 1, sh, dt);
+        row_piece_publish<E>(P, static_cast<int>(r), s0 - rs, s1 - rs, w - wf, wl - wf + 1, sh, dt);
         __syncthreads();
         s0 = s1;
     }
@@ -1509,7 +1290,7 @@ struct SelBlock {
 
 template <typename E>
 __device__ __forceinline__ SelBlock select_block(const DrawRow<E>& d, int V, int NB, const BlockRec* recs,
-                                                 const double* tab, uint32_t* err) {
+                                                 const double* tab, uint32_t* err, uint32_t* err_host) {
     const int lane = threadIdx.x & 63;
     const bool residual = (d.kind == kDrawResidual);
     // every field of this lane's records in one round of loads
@@ -1547,7 +1328,7 @@ __device__ __forceinline__ SelBlock select_block(const DrawRow<E>& d, int V, int
             qq = d.sq ? d.sq[lane] : 1.0f;
         }
         qvalid = qid >= 0 && qid < V;
-        if (lane < d.nq && !qvalid && qid != -1) flag_error(err, kErrTopk);
+        if (lane < d.nq && !qvalid && qid != -1) flag_error(err, err_host, kErrTopk);
         double cs = 0.0;
         if (qvalid) cs = fmin(draw_e<E>(d, E::load1(d.lrow, qid), tab) * invZ64, static_cast<double>(qq));
         const int qblk = qvalid ? qid / kBlockElems : -1;
@@ -1660,7 +1441,7 @@ __device__ __forceinline__ SelBlock select_block(const DrawRow<E>& d, int V, int
         jsel = 0;
         base = 0.0;
         block_fallback = true;
-        if (lane == 0) flag_error(err, kErrNonFinite);
+        if (lane == 0) flag_error(err, err_host, kErrNonFinite);
     }
     SelBlock sb;
     sb.jsel = jsel;
@@ -1729,37 +1510,6 @@ __device__ __forceinline__ int select_token(int ycand, int ylast, int V, int jse
     return y;
 }
 
-// Token scan of the selected block by one wave (token order: sub-block, lane,
-// position); every lane returns the token.
-template <typename E>
-__device__ __forceinline__ int draw_select_wave(const DrawRow<E>& d, int V, int NB, const BlockRec* recs,
-                                                const double* tab, uint32_t* err) {
-    const SelBlock sb = select_block<E>(d, V, NB, recs, tab, err);
-    const long xb = (long)sb.jsel * kBlockElems;
-    double run_base = sb.base;
-    int ycand = 0x7fffffff, ylast = -1;
-    // two sub-blocks per round of loads; the second round only when the first
-    // half holds no crossing (or the rounding fallback needs the last positive
-    // token of the whole block)
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        if (half == 1 && !sb.fallback && __ballot(ycand != 0x7fffffff) != 0ull) break;
-        RawSub<E> raw[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) issue_sub_any<E>(d, sub_first(xb, 2 * half + h), V, sb.with_q, raw[h]);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const long x0 = sub_first(xb, 2 * half + h);
-            double w[kSubTokens];
-            const double tsum = sub_weights<E>(d, raw[h], x0, V, sb, tab, w);
-            const double ti = wave_inclusive_scan(tsum);
-            sub_find(w, x0, run_base + (ti - tsum), sb, ycand, ylast);
-            run_base += rdlane(ti, 63);
-        }
-    }
-    return select_token(wave_min_int(ycand), wave_max_int(ylast), V, sb.jsel);
-}
-
 // The same select by a whole workgroup: every wave makes the (identical) block
 // choice, then wave u scans sub-block u, so the block is loaded in one round;
 // the sub-block sums and each wave's finds meet in LDS.  Every thread returns
@@ -1772,9 +1522,10 @@ struct SelShared {
 
 template <typename E>
 __device__ __forceinline__ int draw_select_wg(const DrawRow<E>& d, int V, int NB, const BlockRec* recs,
-                                              const double* tab, uint32_t* err, SelShared& ss) {
+                                              const double* tab, uint32_t* err, uint32_t* err_host,
+                                              SelShared& ss) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const SelBlock sb = select_block<E>(d, V, NB, recs, tab, err);
+    const SelBlock sb = select_block<E>(d, V, NB, recs, tab, err, err_host);
     const long x0 = sub_first((long)sb.jsel * kBlockElems, wv);
     RawSub<E> raw;
     issue_sub_any<E>(d, x0, V, sb.with_q, raw);
@@ -1849,14 +1600,27 @@ struct ResolveShared {
     float rm[kMaxReqRows];       // row max (sampled) / argmax value (greedy)
     double rz[kMaxReqRows];      // row normaliser
     int rej[kMaxReqRows];        // draft i rejected
+    uint32_t bad[kMaxReqRows];   // contract violations found on row i (kErr* bits)
 };
 
+// Outputs of a request that breaks the device-side contract: every token and
+// num_accepted are -1 (written by the request's writer workgroup only).
+__device__ __forceinline__ void write_violation(const Params& P, int b) {
+    const int tid = threadIdx.x;
+    for (int j = tid; j <= P.gamma; j += kThreads) P.out_tokens[(size_t)b * (P.gamma + 1) + j] = -1;
+    if (tid == 0) P.out_num[b] = -1;
+}
+
 // Uniform call.  Returns request b's draw task (kDrawNone: greedy, nothing to
-// draw, or an inconsistent layout, which is flagged); `writer` workgroups store
-// the outputs, counters and diagnostics.  Thread i owns row i of the request:
-// it loads the row's pieces and its draft's id, logit, q and uniform in one
-// round, merges the pieces and runs the accept test, so that a single barrier
-// publishes the rows' results.
+// draw, or a request that breaks the device-side contract); `writer`
+// workgroups store the outputs, counters and diagnostics.  Thread i owns row i
+// of the request: it loads the row's pieces and its draft's id, logit, q and
+// uniform in one round, merges the pieces and runs the accept test, so that a
+// single barrier publishes the rows' results.  A request is a contract
+// violation when its offsets are inconsistent, a draft id lies outside
+// [0, vocab), its sparse q breaks the entry rules, or one of its sampled rows
+// has no positive finite normaliser (no finite logit, or NaN logits); its
+// outputs are then all -1, the bits are flagged, and it is not counted.
 template <typename E>
 __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool writer, float T, ResolveShared& rs,
                                                    const double* tab) {
@@ -1877,7 +1641,10 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
     }
     const int gb = o1 - o0;
     if (!(o0 >= 0 && o1 <= P.total_draft && gb >= 0 && gb <= G && gb < kMaxReqRows)) {
-        if (writer && tid == 0) flag_error(P.err, kErrOffsets);
+        if (writer) {
+            write_violation(P, b);
+            if (tid == 0) flag_error(P.err, P.err_host, kErrOffsets);
+        }
         return tk;
     }
     const int t0 = o0 + b;
@@ -1962,24 +1729,39 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
                 for (int q = 0; q < kResolveChunk; ++q) argmax_merge(M, g, mm[q], gg[q]);
             }
         }
-        // accept test (page section 5.2: q floored at 1e-10, strict "<"); p(x)
-        // by the draw weights' own expression
+        // accept test (page section 5.2: q floored at 1e-10, strict comparison);
+        // p(x) by the draw weights' own expression
+        uint32_t bad = 0u;
         if (tid < gb) {
             bool acc;
+            if (xid < 0 || xid >= P.vocab) bad |= kErrDraftId;
             if (greedy) {
                 acc = (xid == g);
             } else {
+                if (xs == -2) bad |= kErrTopk;
                 const double px = exp2_tab(fma(static_cast<double>(lx), c2, -(static_cast<double>(M) * c2)), tab) / Z;
                 r = px / fmax(static_cast<double>(qx), kQFloor);
                 acc = (xs >= 0) && (static_cast<double>(u) < fmin(1.0, r));
             }
             rej = !acc;
         }
+        if (!greedy && !(Z > 0.0 && Z < INFINITY && fabsf(M) < INFINITY)) bad |= kErrNonFinite;
         rs.rm[tid] = M;
         rs.rz[tid] = Z;
         rs.rej[tid] = rej ? 1 : 0;
+        rs.bad[tid] = bad;
     }
     __syncthreads();
+    // contract violations anywhere in the request (every wave finds the same)
+    uint32_t badq = 0u;
+    for (int j = 0; j <= gb; ++j) badq |= rs.bad[j];
+    if (badq != 0u) {
+        if (writer) {
+            write_violation(P, b);
+            if (tid == 0) flag_error(P.err, P.err_host, badq);
+        }
+        return tk;
+    }
     // k = the first rejected draft (every wave finds the same)
     const int lane = tid & 63;
     int k = gb;
@@ -2075,119 +1857,10 @@ __global__ __launch_bounds__(kThreads, kLoop ? 3 : 4) void draw_kernel(Params P)
         if (!sh.flag) return;
         if (tid == 0) reset_counter(&P.draw_cnt[b]);
     }
-    const int y = draw_select_wg<E>(d, P.vocab, NB, recs, sh.tab, P.err, sh.sel);
+    const int y = draw_select_wg<E>(d, P.vocab, NB, recs, sh.tab, P.err, P.err_host, sh.sel);
     if (tid == 0) {
         P.out_tokens[(size_t)b * (P.gamma + 1) + tk.pos] = y;
     }
-}
-
-// ----------------------------------------------------------------- one-launch step
-// One launch of at most as many workgroups as the device holds at once (so all
-// of them are resident together on an otherwise idle device; every wait below
-// is bounded, and an expired wait is reported as a stall).  The requests are cut
-// into P.slices consecutive slices.  Every workgroup streams its share of slice
-// 0's rows, then of slice 1's, then takes its share of slice 0's draw blocks,
-// then slice 2's rows, slice 1's draw blocks, and so on: the fp64 draw work of
-// early requests runs beside the memory-bound stream of later ones, and only the
-// last slice's draws are left once the stream ends.  The last piece of a row
-// to arrive merges the row (row_merge) and the last row of a request resolves
-// it; a resolve publishes its request's draw task with this call's epoch, and a wave waits only for the task of the request whose blocks
-// it holds.  The wave that lands a request's last block record runs that
-// request's select.
-constexpr int kPhaseSpinLimit = 1 << 20;   // bounded wait for a draw task (seconds)
-
-// Lane 0 waits until request b's task carries this call's epoch.  Gives up when
-// a row was rejected for inconsistent offsets (its request never resolves;
-// looked at every 16th poll) or when the wait limit expires (flagged as a
-// stall).  Polls are spaced out so that waiting waves add little traffic next
-// to the merges they wait for.
-__device__ __forceinline__ bool wait_task(const Params& P, int b) {
-    int ok = 1;
-    if ((threadIdx.x & 63) == 0) {
-        int spins = 0;
-        while (ld_coherent(&P.task_tag[b]) != P.epoch) {
-            if ((spins & 15) == 15 && (ld_coherent(P.err) & kErrOffsets) != 0u) { ok = 0; break; }
-            if (++spins >= kPhaseSpinLimit) { flag_error(P.err, kErrStalled); ok = 0; break; }
-            __builtin_amdgcn_s_sleep(8);
-        }
-    }
-    return __builtin_amdgcn_readfirstlane(ok) != 0;
-}
-
-// This wave's draw blocks among those of requests [b0, b1): blocks g = first,
-// first + kWaves, ... of their request-major list that fall in the workgroup's
-// gridDim.x-th share.
-template <typename E>
-__device__ __forceinline__ void draw_share(const Params& P, int b0, int b1, const double* tab) {
-    const int lane = threadIdx.x & 63;
-    const int NB = P.nblocks;
-    const long DB = (long)(b1 - b0) * NB;
-    const long g1 = (long)(blockIdx.x + 1) * DB / gridDim.x;
-    long g = (long)blockIdx.x * DB / gridDim.x + (threadIdx.x >> 6);
-    while (g < g1) {
-        const int bi = static_cast<int>(g / NB);
-        const long gb0 = (long)bi * NB;
-        const long gend = g1 < gb0 + NB ? g1 : gb0 + NB;
-        const int j0 = static_cast<int>(g - gb0), j1 = static_cast<int>(gend - gb0);
-        const int n = (j1 - j0 + kWaves - 1) / kWaves;          // this wave's blocks of request b
-        g += (long)n * kWaves;
-        const int b = b0 + bi;
-        if (!wait_task(P, b)) continue;
-        const DrawTask tk = load_task(&P.tasks[b]);
-        const bool residual = (tk.kind == kDrawResidual);
-        if (tk.kind == kDrawNone || tk.row < 0 || tk.row >= P.total_draft + P.batch || tk.pos < 0 ||
-            tk.pos > P.gamma || (residual && (tk.drow < 0 || tk.drow >= P.total_draft)))
-            continue;
-        DrawRow<E> d;
-        init_draw_row<E>(d, P, tk.kind, tk.row, tk.drow, tk.pos, tk.v, tk.m, tk.z32, P.temperature[b]);
-        BlockRec* recs = P.recs + (size_t)b * NB;
-        draw_blocks<E>(d, P.vocab, recs, j0, kWaves, j1, tab);
-        uint32_t old = 0;
-        if (lane == 0) old = arrive_n(&P.draw_cnt[b], static_cast<uint32_t>(n));
-        old = __builtin_amdgcn_readfirstlane(old);
-        if (old + static_cast<uint32_t>(n) != static_cast<uint32_t>(NB)) continue;
-        if (lane == 0) reset_counter(&P.draw_cnt[b]);
-        const int y = draw_select_wave<E>(d, P.vocab, NB, recs, tab, P.err);
-        if (lane == 0) P.out_tokens[(size_t)b * (P.gamma + 1) + tk.pos] = y;
-    }
-}
-
-// First request of slice s, and the first target row of request b (the row
-// count for b == batch), clamped so that slices cover the rows once, in order,
-// whatever the offsets hold.
-__device__ __forceinline__ int slice_first_request(const Params& P, int s) {
-    return static_cast<int>((long)s * P.batch / P.slices);
-}
-__device__ __forceinline__ long request_first_row(const Params& P, int b) {
-    const long total = (long)P.total_draft + P.batch;
-    if (b >= P.batch) return total;
-    const long t = P.offsets ? (long)P.offsets[b] + b : (long)b * (P.gamma + 1);
-    return t < 0 ? 0 : (t > total ? total : t);
-}
-
-template <typename E>
-__global__ __launch_bounds__(kThreads, 3) void step_kernel(Params P) {
-    __shared__ RowShared sh;
-    __shared__ double tab[kExp2TableSize];
-    for (int j = threadIdx.x; j < kExp2TableSize; j += kThreads) tab[j] = kExp2Table[j];
-    __syncthreads();
-    const int S = P.slices;
-    PendingMerge pm;
-    long r0 = 0;
-    for (int s = 0; s < S; ++s) {
-        long r1 = request_first_row(P, slice_first_request(P, s + 1));
-        if (r1 < r0) r1 = r0;
-        rows_share<E>(P, r0, r1, pm, sh);
-        // a merge still pending from an earlier slice (this workgroup had no
-        // piece of slice s) is settled before waiting on that slice's tasks,
-        // which may depend on it
-        if (pm.t >= 0 && pm.t < r0) settle_merge<E>(P, pm, sh);
-        if (s > 0) draw_share<E>(P, slice_first_request(P, s - 1), slice_first_request(P, s), tab);
-        __syncthreads();
-        settle_merge<E>(P, pm, sh);
-        r0 = r1;
-    }
-    draw_share<E>(P, slice_first_request(P, S - 1), slice_first_request(P, S), tab);
 }
 
 }  // namespace sv

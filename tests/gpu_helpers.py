@@ -55,8 +55,7 @@ def upload_inputs(inp, device="cuda:0", diag=True, stats=False):
 
 
 def make_verifier(inp, max_batch=None, max_gamma=None, profile=False, schedule=None):
-    """A context for ``inp``; schedule None is the library's choice, else "onelaunch"
-    or "twokernel"."""
+    """A context for ``inp``; schedule None is the library's choice, else "twokernel"."""
     from lossless_rejection_sampling_sampler_amd import SpecVerify
     return SpecVerify(max_batch or inp.batch, inp.gamma if max_gamma is None else max_gamma,
                       inp.vocab, inp.dtype, device=0, profile=profile, schedule=schedule)

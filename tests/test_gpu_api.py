@@ -85,40 +85,149 @@ def test_zero_batch_leaves_outputs_untouched():
     assert torch.all(db.out_tokens == -7) and torch.all(db.out_num_accepted == -7)
 
 
-SCHEDULES = ["onelaunch", "twokernel"]
-
-
-@pytest.mark.parametrize("schedule", SCHEDULES)
-def test_out_of_range_draft_id_sets_error_word(schedule):
+def _run_once(sv, inp):
+    """One call; returns (tokens, num_accepted) after synchronising."""
     import torch
-    from lossless_rejection_sampling_sampler_amd._lib import SV_DEVERR_DRAFT_ID
-    inp = make_config(2, replicate=1, vocab=1000, batch=4)
-    inp.draft_ids[0] = 1000
-    inp.draft_ids[6] = -3
-    log(f"[api] out-of-range draft ids, schedule={schedule}")
-    res, _, sv = run_gpu(inp, diag=False, schedule=schedule)
-    assert sv.device_errors(clear=True) & SV_DEVERR_DRAFT_ID
+    db = upload_inputs(inp, diag=False)
+    db.run(sv)
+    torch.cuda.synchronize()
+    return db.results()
+
+
+def _expect_blocked_then_cleared(sv, inp, want_bits):
+    """After a violating call has run, the next call is refused with
+    SV_ERR_DEVICE_CONTRACT and enqueues nothing; clearing the word unblocks it."""
+    import torch
+    from lossless_rejection_sampling_sampler_amd import SpecVerifyError
+    from lossless_rejection_sampling_sampler_amd._lib import SV_ERR_DEVICE_CONTRACT
+    db = upload_inputs(inp, diag=False)
+    with pytest.raises(SpecVerifyError) as ei:
+        db.run(sv)
+    assert ei.value.status == SV_ERR_DEVICE_CONTRACT
+    torch.cuda.synchronize()
+    assert torch.all(db.out_tokens == -7) and torch.all(db.out_num_accepted == -7)   # nothing ran
+    bits = sv.device_errors(clear=True)
+    assert bits & want_bits, bits
     assert sv.device_errors() == 0
-    tok, num = res[0]
-    assert num[0] == 0 and num[1] <= 0        # an invalid draft counts as rejected
-    assert np.all((tok >= -1) & (tok < 1000))
 
 
-@pytest.mark.parametrize("schedule", SCHEDULES)
+def _valid_rest_matches_oracle(inp, tok, num, first_valid):
+    import bench
+    import oracle
+    o = oracle.verify(bench.sub_batch(inp, first_valid, inp.batch))
+    assert np.array_equal(tok[first_valid:], o.tokens) and np.array_equal(num[first_valid:], o.num_accepted)
+
+
+@pytest.mark.parametrize("greedy", [False, True], ids=["sampled", "greedy"])
+def test_out_of_range_draft_id_poisons_its_request(greedy):
+    from lossless_rejection_sampling_sampler_amd._lib import SV_DEVERR_DRAFT_ID
+    inp = make_config(2, replicate=1, vocab=1000, batch=6)
+    if greedy:
+        inp.temperature[:] = 0.0
+    good_ids = inp.draft_ids.copy()
+    inp.draft_ids[0] = 1000          # request 0, draft 0
+    inp.draft_ids[6] = -3            # request 1, draft 1
+    log(f"[api] out-of-range draft ids, greedy={greedy}")
+    from tests.gpu_helpers import make_verifier
+    sv = make_verifier(inp)
+    tok, num = _run_once(sv, inp)
+    assert np.all(tok[:2] == -1) and np.all(num[:2] == -1)
+    _valid_rest_matches_oracle(inp, tok, num, 2)
+    inp.draft_ids[:] = good_ids
+    _expect_blocked_then_cleared(sv, inp, SV_DEVERR_DRAFT_ID)
+    tok2, num2 = _run_once(sv, inp)          # unblocked and exact again
+    import oracle
+    o = oracle.verify(inp)
+    assert np.array_equal(tok2, o.tokens) and np.array_equal(num2, o.num_accepted)
+
+
 @pytest.mark.parametrize("batch,bad", [(8, 3), (300, 270)])   # 300: a thread counts two starts
-def test_bad_offsets_set_error_word_without_faulting(schedule, batch, bad):
+def test_bad_offsets_poison_the_request_without_faulting(batch, bad):
     from lossless_rejection_sampling_sampler_amd._lib import SV_DEVERR_OFFSETS
     inp = make_config(5, replicate=1, vocab=600, batch=batch)
     inp.offsets[bad] = inp.offsets[bad + 1] + 3    # gamma_bad negative
-    log(f"[api] inconsistent offsets B={batch} at {bad}, schedule={schedule}")
-    res, _, sv = run_gpu(inp, diag=False, schedule=schedule)
-    assert sv.device_errors(clear=True) & SV_DEVERR_OFFSETS
-    assert sv.device_errors() == 0
-    # a following valid call on the same context is exact again
+    log(f"[api] inconsistent offsets B={batch} at {bad}")
+    res, _, sv = run_gpu(inp, diag=False)
+    tok, num = res[0]
+    assert num[bad] == -1 and np.all(tok[bad] == -1)
     good = make_config(5, replicate=1, vocab=600, batch=batch)
+    _expect_blocked_then_cleared(sv, good, SV_DEVERR_OFFSETS)
+    # a following valid call on the same context is exact again
     res2, _, _ = run_gpu(good, sv=sv)
-    res3, _, _ = run_gpu(good, schedule=schedule)
+    res3, _, _ = run_gpu(good)
     assert np.array_equal(res2[0][0], res3[0][0]) and np.array_equal(res2[0][1], res3[0][1])
+
+
+def test_nonfinite_sampled_row_poisons_its_request():
+    from lossless_rejection_sampling_sampler_amd._lib import SV_DEVERR_NONFINITE
+    inp = make_config(3, replicate=2, vocab=5000, batch=6)
+    V = inp.vocab
+    g1 = inp.gamma + 1
+    neg_inf_bf16 = np.uint16(0xff80)
+    inp.logits[1 * g1 + 2, :] = neg_inf_bf16        # request 1: a row with no finite logit
+    inp.logits[3 * g1 + 0, 17] = np.uint16(0x7fc0)   # request 3: a NaN logit
+    log("[api] non-finite sampled rows")
+    from tests.gpu_helpers import make_verifier
+    sv = make_verifier(inp)
+    tok, num = _run_once(sv, inp)
+    for b in (1, 3):
+        assert num[b] == -1 and np.all(tok[b] == -1)
+    import bench
+    import oracle
+    for b0, b1 in ((0, 1), (2, 3), (4, 6)):
+        o = oracle.verify(bench.sub_batch(inp, b0, b1))
+        assert np.array_equal(tok[b0:b1], o.tokens) and np.array_equal(num[b0:b1], o.num_accepted)
+    bits = sv.device_errors(clear=True)
+    assert bits & SV_DEVERR_NONFINITE
+
+
+def test_sparse_entry_violations_poison_the_request():
+    from lossless_rejection_sampling_sampler_amd._lib import SV_DEVERR_TOPK
+    from synth import make_sparse_config
+    inp = make_sparse_config(replicate=3, vocab=3000, batch=8)
+    off = inp.draft_offsets
+    gam = inp.gammas
+    bs = [b for b in range(inp.batch) if gam[b] > 0][:2]
+    assert len(bs) == 2
+    d0 = off[bs[0]]
+    inp.topk_ids[d0, 1] = inp.vocab + 5              # an entry id outside [-1, V)
+    d1 = off[bs[1]]
+    x = inp.draft_ids[d1]
+    inp.topk_ids[d1, :2] = x                          # the drafted token listed twice
+    log(f"[api] sparse entry violations in requests {bs}")
+    from tests.gpu_helpers import make_verifier
+    sv = make_verifier(inp)
+    tok, num = _run_once(sv, inp)
+    for b in bs:
+        assert num[b] == -1 and np.all(tok[b] == -1)
+    assert sv.device_errors(clear=True) & SV_DEVERR_TOPK
+
+
+def test_device_errors_waits_for_this_context_only():
+    """spec_verify_device_errors returns while another stream is still busy: it
+    waits for the context's last call and its own stream, not the device."""
+    import time
+    import torch
+    inp = make_config(2, replicate=1, vocab=1000, batch=4)
+    from tests.gpu_helpers import make_verifier
+    sv = make_verifier(inp)
+    _run_once(sv, inp)
+    other = torch.cuda.Stream()
+    a = torch.randn(8192, 8192, device="cuda:0")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(other):
+        for _ in range(30):
+            a = a @ a
+            a = a / a.norm()
+        busy_end = torch.cuda.Event()
+        busy_end.record(other)
+    t0 = time.perf_counter()
+    assert sv.device_errors() == 0
+    dt = time.perf_counter() - t0
+    still_busy = not busy_end.query()
+    torch.cuda.synchronize()
+    log(f"[api] device_errors took {dt * 1e3:.2f} ms; other stream still busy: {still_busy}")
+    assert still_busy, "the other stream finished before device_errors returned"
 
 
 def test_profile_counters():

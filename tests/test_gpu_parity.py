@@ -49,7 +49,7 @@ def _aligned(inp) -> bool:
     return inp.vocab * esize % 16 == 0
 
 
-SCHEDULES = ["onelaunch", "twokernel"]
+SCHEDULES = ["twokernel"]
 
 
 @pytest.mark.parametrize("schedule", SCHEDULES)
@@ -61,10 +61,8 @@ def test_small_parity(name, kw, schedule):
     sets = [inp.uniforms] + [uniforms_from_seed(inp.uniforms.shape, s) for s in range(15)]
     rep, errs, sv = parity_check(inp, sets, label=name, schedule=schedule)
     _assert_ok(rep, errs)
-    from lossless_rejection_sampling_sampler_amd._lib import (SV_SCHEDULE_FLAT, SV_SCHEDULE_ONE_LAUNCH,
-                                                              SV_SCHEDULE_SPLIT)
-    aligned_want = {"onelaunch": SV_SCHEDULE_ONE_LAUNCH, "twokernel": SV_SCHEDULE_FLAT}[schedule]
-    want = aligned_want if _aligned(inp) else SV_SCHEDULE_SPLIT
+    from lossless_rejection_sampling_sampler_amd._lib import SV_SCHEDULE_FLAT, SV_SCHEDULE_SPLIT
+    want = SV_SCHEDULE_FLAT if _aligned(inp) else SV_SCHEDULE_SPLIT
     assert sv.last_schedule() == want
 
 

@@ -46,7 +46,7 @@ def _case(k, wide=False):
     return spec, inp, fmt
 
 
-@pytest.mark.parametrize("schedule", ["twokernel", "onelaunch"])
+@pytest.mark.parametrize("schedule", ["twokernel"])
 @pytest.mark.parametrize("k", range(N_CASES))
 def test_random_case(k, schedule):
     spec, inp, fmt = _case(k)
@@ -60,7 +60,7 @@ def test_random_case(k, schedule):
     assert sv.device_errors() == 0
 
 
-@pytest.mark.parametrize("schedule", ["twokernel", "onelaunch"])
+@pytest.mark.parametrize("schedule", ["twokernel"])
 @pytest.mark.parametrize("k", range(N_WIDE))
 def test_random_wide_case(k, schedule):
     spec, inp, fmt = _case(k, wide=True)
