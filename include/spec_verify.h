@@ -210,16 +210,17 @@ int spec_verify_create(const sv_config *cfg, int device, sv_ctx **out);
 int spec_verify_run(sv_ctx *ctx, const sv_args *args, void *stream);
 
 /* Releases what spec_verify_create allocated (lifecycle only; the page defines
- * no such step).  Waits for the context's last eagerly launched call and its
- * internal stream first, not for other work on the device (freeing device
- * memory may itself synchronise the device).  NULL is a no-op. */
+ * no such step).  Waits for the stream of the context's last eagerly launched
+ * call (it must still exist) and for the context's internal stream first, not
+ * for other streams (freeing device memory may itself synchronise the device).
+ * NULL is a no-op. */
 int spec_verify_destroy(sv_ctx *ctx);
 
-/* Reads (and, if clear != 0, resets) the sticky SV_DEVERR_* word.  Waits for the
- * context's last eagerly launched call (the point of its stream where that call
- * ended; synchronise a replayed graph yourself) and uses the context's internal
- * stream for the read and the reset, so other streams are not waited for.  Do
- * not call it while a call on this context may still be enqueued elsewhere. */
+/* Reads (and, if clear != 0, resets) the sticky SV_DEVERR_* word.  Synchronises
+ * the stream of the context's last eagerly launched call (it must still exist;
+ * synchronise a replayed graph yourself) and uses the context's internal stream
+ * for the read and the reset, so other streams are not waited for.  Do not call
+ * it while a call on this context may still be enqueued elsewhere. */
 int spec_verify_device_errors(sv_ctx *ctx, uint32_t *bits, int clear);
 
 /* With SV_FLAG_PROFILE: waits for the recorded events and returns the summed

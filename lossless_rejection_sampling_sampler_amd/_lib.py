@@ -103,6 +103,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    # torch first: the library then binds to the HIP runtime torch has loaded,
+    # so device pointers and streams from torch are valid in it
+    import torch  # noqa: F401
     if not os.path.exists(path):
         raise ImportError(
             f"{path} is missing: build it with `python -m lossless_rejection_sampling_sampler_amd.build` "

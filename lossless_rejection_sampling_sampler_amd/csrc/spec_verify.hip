@@ -19,12 +19,10 @@ namespace {
 
 constexpr int kRowVecsPerThread = 8;    // target 16-byte vectors per thread per row split
 constexpr int kProfileRing = 2048;      // calls between forced event folds
-constexpr int kDrawBlocksPerWave = 2;   // draw kernel: blocks per wave in straight-line code
-constexpr int kDrawPerCU = 3;           // draw kernel: workgroups per CU aimed at
+constexpr int kDrawWavesPerSimd = 3;    // draw kernel: waves per SIMD aimed at (one resident round)
 
 struct Geometry {
     int splits;          // split rows kernel: workgroups per row
-    int nblocks;         // draw blocks per row
 };
 
 Geometry geometry_for(int vocab, int dtype) {
@@ -34,7 +32,6 @@ Geometry geometry_for(int vocab, int dtype) {
     s = std::max(1L, std::min(s, (long)sv::kMaxPieces));
     Geometry g;
     g.splits = static_cast<int>(s);
-    g.nblocks = (vocab + sv::kBlockElems - 1) / sv::kBlockElems;
     return g;
 }
 
@@ -58,17 +55,20 @@ int flat_workgroups(long nv, long vpr, int resident) {
 // that the dispatches themselves stamp: rows start / end, draw start / end (the
 // kernels' own execution, without the gap between dispatches).
 template <typename E>
-int launch_rows_draw(bool aligned, bool loop, long grid1, long grid2, const sv::Params& P, hipStream_t stream,
+int launch_rows_draw(bool aligned, long grid1, long grid2, const sv::Params& P, hipStream_t stream,
                      const hipEvent_t* ev) {
     const dim3 g1((unsigned)grid1), g2((unsigned)grid2), blk(sv::kThreads);
-    hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
-    hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
+    if (!ev) {
+        if (aligned) hipLaunchKernelGGL(sv::rows_flat_kernel<E>, g1, blk, 0, stream, P);
+        else hipLaunchKernelGGL(sv::rows_split_kernel<E>, g1, blk, 0, stream, P);
+        hipLaunchKernelGGL(sv::draw_kernel<E>, g2, blk, 0, stream, P);
+        return SV_OK;
+    }
     if (aligned)
-        hipExtLaunchKernelGGL(sv::rows_flat_kernel<E>, g1, blk, 0, stream, e0, e1, 0, P);
+        hipExtLaunchKernelGGL(sv::rows_flat_kernel<E>, g1, blk, 0, stream, ev[0], ev[1], 0, P);
     else
-        hipExtLaunchKernelGGL(sv::rows_split_kernel<E>, g1, blk, 0, stream, e0, e1, 0, P);
-    if (loop) hipExtLaunchKernelGGL((sv::draw_kernel<E, true>), g2, blk, 0, stream, e2, e3, 0, P);
-    else hipExtLaunchKernelGGL((sv::draw_kernel<E, false>), g2, blk, 0, stream, e2, e3, 0, P);
+        hipExtLaunchKernelGGL(sv::rows_split_kernel<E>, g1, blk, 0, stream, ev[0], ev[1], 0, P);
+    hipExtLaunchKernelGGL(sv::draw_kernel<E>, g2, blk, 0, stream, ev[2], ev[3], 0, P);
     return SV_OK;
 }
 
@@ -79,8 +79,7 @@ static_assert(SV_MAX_GAMMA + 1 <= sv::kMaxReqRows, "a request's rows fit the dra
 struct Scratch {
     sv::Piece* parts;
     sv::RowStat* rows;
-    sv::DrawTask* tasks;
-    sv::BlockRec* recs;
+    sv::RangeRec* recs;
     uint32_t* draw_cnt;
     uint32_t* err;
     uint32_t* err_host;
@@ -144,27 +143,19 @@ int enqueue(const Geometry& geo, int resident_flat, int cus, int resident_draw, 
     P.total_draft = a->total_draft;
     P.vocab = a->vocab;
     P.splits = geo.splits;
-    P.nblocks = geo.nblocks;
-    // draw workgroups per request: three per CU over the call (one resident
-    // round) where that keeps between one and kDrawBlocksPerWave blocks per
-    // wave (an even count per CU balances the fp64 work across the SIMDs).  A
-    // call with more draw rows than that round can hold at two blocks per wave
-    // (B = 128 or 256 at V = 151936 / 128256) takes a second round of
-    // workgroups when its residual blocks stream a dense q row too; with sparse
-    // or point-mass q (every block streams logits only, so a workgroup's
-    // fixed latency outweighs its bytes) its waves take pairs of blocks in a
-    // loop instead (measured: 100 against 110 us at B = 256 with top-50 lists,
-    // 114 against 109 us with dense q)
-    const int c_min = std::max(1, (geo.nblocks + sv::kWaves * kDrawBlocksPerWave - 1) /
-                                      (sv::kWaves * kDrawBlocksPerWave));
-    const int c_max = std::max(1, (geo.nblocks + sv::kWaves - 1) / sv::kWaves);
-    const int c_fit = kDrawPerCU * cus / a->batch;
-    const bool draw_loop = c_fit < c_min && qmode != sv::kQDense;
-    const int C = draw_loop ? std::max(1, c_fit) : std::max(c_min, std::min(c_max, c_fit));
-    P.draw_wgs = C;
+    // draw ranges per row: about kDrawWavesPerSimd waves per SIMD over the call
+    // (one resident round, every wave one range), each range at most
+    // kRangeSubs sub-blocks and at least one sub-block, at most kMaxRanges, and
+    // a multiple of four (a workgroup's four waves take four ranges of one request)
+    const long n8 = ((long)a->vocab + 7) / 8;
+    const long nr_min = std::max(1L, (n8 + sv::kRangeSubs * 64 - 1) / (sv::kRangeSubs * 64));
+    const long nr_max = std::max(nr_min, std::min<long>(sv::kMaxRanges, std::max(1L, n8 / 64)));
+    const long waves_target = (long)kDrawWavesPerSimd * 4 * cus;
+    long nr = std::max(nr_min, std::min(nr_max, waves_target / a->batch));
+    if (nr > sv::kWaves) nr = std::min<long>(sv::kMaxRanges, (nr + sv::kWaves - 1) / sv::kWaves * sv::kWaves);
+    P.nranges = static_cast<int>(nr);
     P.parts = sc.parts;
     P.rows = sc.rows;
-    P.tasks = sc.tasks;
     P.recs = sc.recs;
     P.draw_cnt = sc.draw_cnt;
     P.err = sc.err;
@@ -176,17 +167,20 @@ int enqueue(const Geometry& geo, int resident_flat, int cus, int resident_draw, 
                          (((long)a->vocab * (long)esize) % 16 == 0);
     P.flat_vpr = (long)a->vocab * (long)esize / 16;
     P.flat_nv = rows * P.flat_vpr;
-    const long grid1 = aligned ? flat_workgroups(P.flat_nv, P.flat_vpr, resident_flat) : rows * P.splits;
-    const long grid2 = (long)a->batch * C;
-    P.rows_grid = static_cast<int>(grid1);
-    P.draw_cmajor = grid2 <= resident_draw ? 1 : 0;
     // rows are streamed without any hand-off between workgroups (flattened
     // ranges for 16-byte aligned rows, per-row splits otherwise) and every
     // request is resolved by its draw workgroups
     P.split_pieces = aligned ? 0 : P.splits;
+    const long qr = (nr + sv::kWaves - 1) / sv::kWaves;   // quads per request
+    const long grid1 = aligned ? flat_workgroups(P.flat_nv, P.flat_vpr, resident_flat) : rows * P.splits;
+    // one workgroup per quad of ranges (four waves) up to what the device holds
+    // at once; past that, every workgroup takes a contiguous run of quads
+    const long quads = (long)a->batch * qr;
+    const long grid2 = std::max(1L, std::min(quads, (long)resident_draw));
+    P.rows_grid = static_cast<int>(grid1);
     const int st = (dtype == SV_BF16)
-                       ? launch_rows_draw<sv::BF16>(aligned, draw_loop, grid1, grid2, P, stream, ev)
-                       : launch_rows_draw<sv::F32>(aligned, draw_loop, grid1, grid2, P, stream, ev);
+                       ? launch_rows_draw<sv::BF16>(aligned, grid1, grid2, P, stream, ev)
+                       : launch_rows_draw<sv::F32>(aligned, grid1, grid2, P, stream, ev);
     if (st != SV_OK) return st;
     *schedule = aligned ? SV_SCHEDULE_FLAT : SV_SCHEDULE_SPLIT;
     return SV_OK;
@@ -207,8 +201,7 @@ struct sv_ctx {
     void* scratch = nullptr;
     sv::Piece* parts = nullptr;
     sv::RowStat* rows = nullptr;
-    sv::DrawTask* tasks = nullptr;
-    sv::BlockRec* recs = nullptr;
+    sv::RangeRec* recs = nullptr;
     uint32_t* draw_cnt = nullptr;
     uint32_t* err = nullptr;
     // host-mapped pinned word the kernels set on a contract violation (checked by run)
@@ -216,8 +209,8 @@ struct sv_ctx {
     uint32_t* err_host_dev = nullptr;   // its device-side address
     uint32_t* err_read = nullptr;       // pinned staging word for spec_verify_device_errors
     hipStream_t aux = nullptr;          // internal non-blocking stream: clears and reads of the error word
-    hipEvent_t done = nullptr;          // recorded after every eager run on the caller's stream
-    bool done_recorded = false;
+    hipStream_t last_stream = nullptr;  // stream of the last eagerly enqueued call
+    bool have_last = false;
     // profiling
     std::vector<hipEvent_t> events;    // 4 per call: rows start / end, draw start / end
     int prof_n = 0;
@@ -228,6 +221,7 @@ struct sv_ctx {
 namespace {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+constexpr size_t align_up_c(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int fold_profile(sv_ctx* ctx) {
     if (ctx->prof_n == 0) return SV_OK;
@@ -251,7 +245,6 @@ void free_ctx(sv_ctx* ctx) {
     (void)hipGetDevice(&prev);
     (void)hipSetDevice(ctx->device);
     for (hipEvent_t e : ctx->events) (void)hipEventDestroy(e);
-    if (ctx->done) (void)hipEventDestroy(ctx->done);
     if (ctx->aux) (void)hipStreamDestroy(ctx->aux);
     if (ctx->err_host) (void)hipHostFree(ctx->err_host);
     if (ctx->err_read) (void)hipHostFree(ctx->err_read);
@@ -260,10 +253,10 @@ void free_ctx(sv_ctx* ctx) {
     delete ctx;
 }
 
-// Waits for the last eagerly launched call of this context (its stream up to that
-// call) and for the context's internal stream; no other stream is waited for.
+// Waits for the stream of the context's last eagerly launched call and for the
+// context's internal stream; no other stream is waited for.
 int wait_context(sv_ctx* ctx) {
-    if (ctx->done_recorded && hipEventSynchronize(ctx->done) != hipSuccess) return SV_ERR_DEVICE;
+    if (ctx->have_last && hipStreamSynchronize(ctx->last_stream) != hipSuccess) return SV_ERR_DEVICE;
     if (ctx->aux && hipStreamSynchronize(ctx->aux) != hipSuccess) return SV_ERR_DEVICE;
     return SV_OK;
 }
@@ -305,7 +298,7 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
     if (cfg->max_batch < 1 || cfg->max_gamma < 0 || cfg->max_gamma > SV_MAX_GAMMA || cfg->vocab < 1)
         return SV_ERR_INVALID_ARG;
     if (cfg->logits_dtype != SV_F32 && cfg->logits_dtype != SV_BF16) return SV_ERR_UNSUPPORTED;
-    if ((long)cfg->vocab > (long)sv::kMaxDrawBlocks * sv::kBlockElems) return SV_ERR_UNSUPPORTED;
+    if ((long)cfg->vocab > (long)sv::kMaxVocab) return SV_ERR_UNSUPPORTED;
     // row indices are 32-bit: max_batch * (max_gamma + 1) target rows must fit
     if ((long)cfg->max_batch * ((long)cfg->max_gamma + 1) > (long)INT32_MAX) return SV_ERR_UNSUPPORTED;
     int ndev = 0;
@@ -331,9 +324,10 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
         ctx->cus = std::max(1, cus);
 
         int per_draw = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_draw, sv::draw_kernel<sv::BF16, false>,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_draw, sv::draw_kernel<sv::BF16>,
                                                          sv::kThreads, 0) == hipSuccess)
             ctx->resident_draw = cus * per_draw;
+        if (ctx->resident_draw <= 0) ctx->resident_draw = 3 * std::max(1, cus);
         (void)hipGetLastError();
     }
     const size_t n_rows = (size_t)ctx->max_rows;
@@ -341,8 +335,7 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
     size_t off = 0;
     const size_t o_parts = off; off = align_up(off + n_rows * sv::kMaxPieces * sizeof(sv::Piece), 256);
     const size_t o_rows = off;  off = align_up(off + n_rows * sizeof(sv::RowStat), 256);
-    const size_t o_tasks = off; off = align_up(off + n_b * sizeof(sv::DrawTask), 256);
-    const size_t o_recs = off;  off = align_up(off + n_b * ctx->geo.nblocks * sizeof(sv::BlockRec), 256);
+    const size_t o_recs = off;  off = align_up(off + n_b * sv::kMaxRanges * sizeof(sv::RangeRec), 256);
     const size_t o_cnt = off;   off = align_up(off + (n_b + 1) * sizeof(uint32_t), 256);
     const size_t total = off;
     if (hipMalloc(&ctx->scratch, total) != hipSuccess) {
@@ -353,8 +346,7 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
     char* base = static_cast<char*>(ctx->scratch);
     ctx->parts = reinterpret_cast<sv::Piece*>(base + o_parts);
     ctx->rows = reinterpret_cast<sv::RowStat*>(base + o_rows);
-    ctx->tasks = reinterpret_cast<sv::DrawTask*>(base + o_tasks);
-    ctx->recs = reinterpret_cast<sv::BlockRec*>(base + o_recs);
+    ctx->recs = reinterpret_cast<sv::RangeRec*>(base + o_recs);
     ctx->draw_cnt = reinterpret_cast<uint32_t*>(base + o_cnt);
     ctx->err = ctx->draw_cnt + n_b;
     if (hipHostMalloc(reinterpret_cast<void**>(&ctx->err_host), sizeof(uint32_t),
@@ -366,8 +358,7 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
     }
     *reinterpret_cast<volatile uint32_t*>(ctx->err_host) = 0u;
     if (hipHostGetDevicePointer(reinterpret_cast<void**>(&ctx->err_host_dev), ctx->err_host, 0) != hipSuccess ||
-        hipStreamCreateWithFlags(&ctx->aux, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&ctx->done, hipEventDisableTiming) != hipSuccess) {
+        hipStreamCreateWithFlags(&ctx->aux, hipStreamNonBlocking) != hipSuccess) {
         free_ctx(ctx);
         return SV_ERR_DEVICE;
     }
@@ -418,7 +409,6 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
     Scratch sc;
     sc.parts = ctx->parts;
     sc.rows = ctx->rows;
-    sc.tasks = ctx->tasks;
     sc.recs = ctx->recs;
     sc.draw_cnt = ctx->draw_cnt;
     sc.err = ctx->err;
@@ -436,16 +426,17 @@ int spec_verify_run(sv_ctx* ctx, const sv_args* a, void* stream_ptr) {
     if (st != SV_OK) return st;
     if (hipGetLastError() != hipSuccess) return SV_ERR_DEVICE;
     if (prof) ctx->prof_n++;
-    // remember where this call ends on its stream (not while a graph is being
-    // captured: a replay is waited for by the caller)
+    // remember the stream this call was enqueued on (not while a graph is being
+    // captured: a replay is waited for by the caller); an event per call would
+    // add a marker between consecutive steps
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
         (void)hipGetLastError();
         cap = hipStreamCaptureStatusNone;
     }
     if (cap == hipStreamCaptureStatusNone) {
-        if (hipEventRecord(ctx->done, stream) != hipSuccess) return SV_ERR_DEVICE;
-        ctx->done_recorded = true;
+        ctx->last_stream = stream;
+        ctx->have_last = true;
     }
     ctx->last_schedule = schedule;
     return SV_OK;
