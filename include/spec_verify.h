@@ -244,6 +244,27 @@ int spec_verify_last_schedule(const sv_ctx *ctx, int32_t *schedule);
 /* Static, human-readable name of a status code. */
 const char *spec_verify_status_string(int status);
 
+/* Limits of spec_verify_run_static. */
+#define SV_STATIC_MAX_BATCH 256          /* requests per call */
+#define SV_STATIC_MAX_ROWS 4096          /* target rows per call (total_draft + batch) */
+#define SV_STATIC_SCRATCH_BYTES (8u << 20) /* device scratch per GPU, held until the process ends */
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * verify step as spec_verify_run, with no context.  Its kernels use a
+ * file-scope device array of SV_STATIC_SCRATCH_BYTES (one per GPU, set up on
+ * the first call on that device, which must be the current device; no
+ * hipMalloc, hipFree or allocating routine is ever called).  logits_dtype is
+ * SV_F32 or SV_BF16; args->vocab may be any size up to 524288.  Returns
+ * SV_ERR_CAPACITY for batch > SV_STATIC_MAX_BATCH, gamma > SV_MAX_GAMMA or more
+ * than SV_STATIC_MAX_ROWS target rows, else the statuses of spec_verify_run
+ * (nothing is enqueued unless SV_OK).  Every call on one GPU shares that GPU's
+ * array and leaves it ready for the next: calls that overlap on one GPU (two
+ * streams, or two threads) race and must be serialised by the caller.  A
+ * request that breaks the device-side contract gets -1 outputs as with
+ * spec_verify_run; no error word is reported. */
+int spec_verify_run_static(int logits_dtype, const sv_args *args, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -52,7 +52,10 @@ EXPORTS = (
     "spec_verify_profile_read",
     "spec_verify_last_schedule",
     "spec_verify_status_string",
+    "spec_verify_run_static",
 )
+SV_STATIC_MAX_BATCH = 256
+SV_STATIC_MAX_ROWS = 4096
 
 
 class SVConfig(ctypes.Structure):
@@ -127,12 +130,22 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_verify_last_schedule.restype = ctypes.c_int
     lib.spec_verify_status_string.argtypes = [ctypes.c_int]
     lib.spec_verify_status_string.restype = ctypes.c_char_p
+    lib.spec_verify_run_static.argtypes = [ctypes.c_int, ctypes.POINTER(SVArgs), ctypes.c_void_p]
+    lib.spec_verify_run_static.restype = ctypes.c_int
     _lib = lib
     return lib
 
 
 def status_string(status: int) -> str:
     return load_library().spec_verify_status_string(status).decode()
+
+
+def run_static(logits_dtype: str, args: "SVArgs", stream_handle: int) -> int:
+    """spec_verify_run_static: the verify step with the library's static device
+    scratch (no context, nothing allocated); returns the status."""
+    lib = load_library()
+    return lib.spec_verify_run_static(SV_BF16 if logits_dtype == "bf16" else SV_F32, ctypes.byref(args),
+                                      ctypes.c_void_p(stream_handle))
 
 
 def _ptr(t) -> int:

@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -276,6 +277,66 @@ struct DeviceGuard {
 
 }  // namespace
 
+// ----------------------------------------------------------------- entry point without allocation
+// spec_verify_run_static keeps its scratch in this file-scope device array:
+// each GPU the library runs on holds its own copy until the process ends.  In
+// host code `scratch` is only a stand-in for the symbol; the device address is
+// looked up once per device with hipGetSymbolAddress and used everywhere.
+namespace {
+
+constexpr size_t kStaticRows = SV_STATIC_MAX_ROWS;
+constexpr size_t kStaticBatch = SV_STATIC_MAX_BATCH;
+constexpr size_t kOffParts = 0;
+constexpr size_t kOffRows = align_up_c(kOffParts + kStaticRows * sv::kMaxPieces * sizeof(sv::Piece), 256);
+constexpr size_t kOffRecs = align_up_c(kOffRows + kStaticRows * sizeof(sv::RowStat), 256);
+constexpr size_t kOffCnt = align_up_c(kOffRecs + kStaticBatch * sv::kMaxRanges * sizeof(sv::RangeRec), 256);
+constexpr size_t kStaticBytes = align_up_c(kOffCnt + (kStaticBatch + 1) * sizeof(uint32_t), 256);
+static_assert(kStaticBytes <= SV_STATIC_SCRATCH_BYTES, "the static scratch holds its layout");
+
+static __device__ __align__(256) unsigned char scratch[SV_STATIC_SCRATCH_BYTES];
+
+constexpr int kStaticDevices = 64;
+struct StaticDevice {
+    bool ready = false;
+    unsigned char* base = nullptr;     // device address of this device's `scratch`
+    int cus = 0, resident_flat = 0, resident_draw = 0;
+};
+StaticDevice g_static[kStaticDevices];
+std::mutex g_static_mu;
+
+// Set-up on the current device, once: the scratch array's device address and
+// the occupancy figures the launch geometry uses.
+int static_device(int dev, StaticDevice** out) {
+    if (dev < 0 || dev >= kStaticDevices) return SV_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    StaticDevice& sd = g_static[dev];
+    if (!sd.ready) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+            (void)hipGetLastError();
+            return SV_ERR_DEVICE;
+        }
+        int cus = 0, per_cu = 0, per_draw = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sv::rows_flat_kernel<sv::BF16>, sv::kThreads, 0) !=
+                hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_draw, sv::draw_kernel<sv::BF16>, sv::kThreads, 0) !=
+                hipSuccess) {
+            (void)hipGetLastError();
+            return SV_ERR_DEVICE;
+        }
+        sd.base = static_cast<unsigned char*>(ptr);
+        sd.cus = std::max(1, cus);
+        sd.resident_flat = sd.cus * std::min(3, std::max(1, per_cu));
+        sd.resident_draw = per_draw > 0 ? sd.cus * per_draw : 3 * sd.cus;
+        sd.ready = true;
+    }
+    *out = &sd;
+    return SV_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* spec_verify_status_string(int status) {
@@ -477,6 +538,37 @@ int spec_verify_profile_read(sv_ctx* ctx, double* rows_ms, double* draw_ms, int3
     ctx->prof_rows_ms = ctx->prof_draw_ms = 0.0;
     ctx->prof_calls = 0;
     return SV_OK;
+}
+
+int spec_verify_run_static(int logits_dtype, const sv_args* a, void* stream_ptr) {
+    if (!a) return SV_ERR_INVALID_ARG;
+    if (logits_dtype != SV_F32 && logits_dtype != SV_BF16) return SV_ERR_UNSUPPORTED;
+    if (a->vocab < 1) return SV_ERR_INVALID_ARG;
+    if ((long)a->vocab > (long)sv::kMaxVocab) return SV_ERR_UNSUPPORTED;
+    if (a->batch > SV_STATIC_MAX_BATCH || a->gamma > SV_MAX_GAMMA ||
+        (long)a->total_draft + (long)a->batch > (long)SV_STATIC_MAX_ROWS)
+        return SV_ERR_CAPACITY;
+    int qmode = 0;
+    const int st0 = check_args(SV_STATIC_MAX_BATCH, SV_MAX_GAMMA, a->vocab, logits_dtype, a, &qmode);
+    if (st0 != SV_OK) return st0;
+    if (a->batch == 0) return SV_OK;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SV_ERR_DEVICE;
+    StaticDevice* sd = nullptr;
+    const int st1 = static_device(dev, &sd);
+    if (st1 != SV_OK) return st1;
+    Scratch sc;
+    sc.parts = reinterpret_cast<sv::Piece*>(sd->base + kOffParts);
+    sc.rows = reinterpret_cast<sv::RowStat*>(sd->base + kOffRows);
+    sc.recs = reinterpret_cast<sv::RangeRec*>(sd->base + kOffRecs);
+    sc.draw_cnt = reinterpret_cast<uint32_t*>(sd->base + kOffCnt);
+    sc.err = sc.draw_cnt + kStaticBatch;
+    sc.err_host = nullptr;
+    int schedule = SV_SCHEDULE_NONE;
+    const int st = enqueue(geometry_for(a->vocab, logits_dtype), sd->resident_flat, sd->cus, sd->resident_draw,
+                           logits_dtype, sc, a, qmode, static_cast<hipStream_t>(stream_ptr), nullptr, &schedule);
+    if (st != SV_OK) return st;
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_DEVICE;
 }
 
 }  // extern "C"
