@@ -305,38 +305,47 @@ def profiled_avg_ms(kernel: str):
     return None if k is None else k["avg_ms"]
 
 
+# Read-probe layouts the ceiling is taken over: (name, mode, workgroups per CU).
+# Grid-stride (the grid reads one dense window at a time) is the fastest form on
+# this device; spans (one contiguous range per workgroup, the rows kernel's
+# layout) and chunks (contiguous chunks interleaved over the grid) for context.
+CEILING_LAYOUTS = (("stride8nt", 0, 1), ("stride8nt", 0, 3), ("stride8nt", 0, 6), ("stride8nt", 0, 8),
+                   ("stride16nt", 4, 3), ("stride16nt", 4, 8), ("span8nt", 1, 3), ("chunk8nt", 8, 3))
+
+
 def read_ceiling(torch, nbytes_list, reps=5):
-    """GB/s of the plain streaming-read probe over buffers of the given sizes."""
+    """Streaming-read GB/s per probe layout over buffers of the given sizes: the
+    median of ``reps`` launches, each on a different buffer of a set larger than
+    the Infinity Cache, so that no launch reads what the previous one left there.
+    Returns {nbytes: {layout: GB/s}}."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "lossless_rejection_sampling_sampler_amd", "libhbmprobe.so"))
-    lib.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
-    lib.hbm_read_probe.restype = ctypes.c_int
-    props = torch.cuda.get_device_properties(0)
-    grid = 4 * props.multi_processor_count
-    out = torch.empty(grid, dtype=torch.int32, device="cuda:0")
-    sh = torch.cuda.current_stream().cuda_stream
+    lib.hbm_read_probe_time.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
+    lib.hbm_read_probe_time.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(16 * cus, dtype=torch.int32, device="cuda:0")
     res = {}
     for nb in nbytes_list:
         nb = nb // 16 * 16
-        # several buffers, so the Infinity Cache cannot serve a repeat
-        bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda:0") for _ in range(max(1, (1 << 30) // nb + 1))]
+        bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda:0") for _ in range(max(2, (320 << 20) // nb + 1))]
         for b in bufs:
             b.fill_(1)
-        times = []
-        for r in range(reps + 1):
-            b = bufs[r % len(bufs)]
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            st = lib.hbm_read_probe(ctypes.c_void_p(b.data_ptr()), nb, ctypes.c_void_p(out.data_ptr()), grid,
-                                    ctypes.c_void_p(sh))
-            e1.record()
-            if st:
-                raise RuntimeError(f"hbm_read_probe status {st}")
-            torch.cuda.synchronize()
-            if r:
-                times.append(e0.elapsed_time(e1))
-        times.sort()
-        res[nb] = nb / (times[len(times) // 2] * 1e-3) / 1e9
+        torch.cuda.synchronize()
+        row = {}
+        for name, mode, per in CEILING_LAYOUTS:
+            times = []
+            for r in range(reps):
+                b = bufs[r % len(bufs)]
+                ms = ctypes.c_float()
+                st = lib.hbm_read_probe_time(ctypes.c_void_p(b.data_ptr()), nb, ctypes.c_void_p(out.data_ptr()),
+                                             per * cus, mode, 1 if r == 0 else 0, 1, ctypes.byref(ms))
+                if st:
+                    raise RuntimeError(f"hbm_read_probe_time status {st}")
+                times.append(ms.value)
+            times.sort()
+            row[f"{name}_{per}perCU"] = round(nb / (times[len(times) // 2] * 1e-3) / 1e9, 1)
+        res[nb] = row
         del bufs
         torch.cuda.empty_cache()
     return res
@@ -532,9 +541,11 @@ def main():
         packed = packed[:1]
         torch.cuda.empty_cache()
         cz = read_ceiling(torch, [1 << 30, step_bytes])
-        ceiling = {"read_1GiB_gbps": round(cz[(1 << 30) // 16 * 16], 1),
-                   "read_step_bytes_gbps": round(cz[step_bytes // 16 * 16], 1),
-                   "kernel": "16-byte non-temporal loads, 4 workgroups of 256 per CU, one launch per buffer"}
+        big, small = cz[(1 << 30) // 16 * 16], cz[step_bytes // 16 * 16]
+        ceiling = {"read_1GiB_gbps": max(big.values()), "read_step_bytes_gbps": max(small.values()),
+                   "best_layout_1GiB": max(big, key=big.get), "best_layout_step_bytes": max(small, key=small.get),
+                   "layouts_1GiB_gbps": big, "layouts_step_bytes_gbps": small,
+                   "kernel": "16-byte loads; median of 5 launches, each on another buffer (set > Infinity Cache)"}
         log(f"[bench] read ceiling {ceiling}")
 
     def roofline(kname, kbytes, kms):

@@ -189,8 +189,9 @@ typedef struct sv_ctx sv_ctx;    /* opaque; owns the device scratch of one strea
  * vocabulary shared by draft and target, section 8 pitfall 1) on HIP device
  * `device`, and allocates what every call reuses: device scratch for the row
  * statistics, draw records and arrival counters sized for cfg's limits, a
- * pinned host word for contract violations, an internal non-blocking stream
- * and an event.  On success *out holds the context (free it with
+ * pinned host word for contract violations (and one for reading it back) and
+ * an internal non-blocking stream (with SV_FLAG_PROFILE also a ring of
+ * events).  On success *out holds the context (free it with
  * spec_verify_destroy).  Returns SV_ERR_INVALID_ARG for bad limits,
  * SV_ERR_UNSUPPORTED for a dtype, vocab or row count (max_batch *
  * (max_gamma + 1) above 2^31 - 1) the library does not handle,
@@ -247,6 +248,7 @@ const char *spec_verify_status_string(int status);
 /* Limits of spec_verify_run_static. */
 #define SV_STATIC_MAX_BATCH 256          /* requests per call */
 #define SV_STATIC_MAX_ROWS 4096          /* target rows per call (total_draft + batch) */
+#define SV_STATIC_MAX_DRAW_BLOCKS 32768  /* batch * ceil(vocab / 2048) per call */
 #define SV_STATIC_SCRATCH_BYTES (8u << 20) /* device scratch per GPU, held until the process ends */
 
 /* For callers that cannot allocate device memory (code under HIP graph
@@ -256,8 +258,10 @@ const char *spec_verify_status_string(int status);
  * the first call on that device, which must be the current device; no
  * hipMalloc, hipFree or allocating routine is ever called).  logits_dtype is
  * SV_F32 or SV_BF16; args->vocab may be any size up to 524288.  Returns
- * SV_ERR_CAPACITY for batch > SV_STATIC_MAX_BATCH, gamma > SV_MAX_GAMMA or more
- * than SV_STATIC_MAX_ROWS target rows, else the statuses of spec_verify_run
+ * SV_ERR_CAPACITY for batch > SV_STATIC_MAX_BATCH, gamma > SV_MAX_GAMMA, more
+ * than SV_STATIC_MAX_ROWS target rows or batch * ceil(vocab / 2048) above
+ * SV_STATIC_MAX_DRAW_BLOCKS (128 requests at the largest vocab), else the
+ * statuses of spec_verify_run
  * (nothing is enqueued unless SV_OK).  Every call on one GPU shares that GPU's
  * array and leaves it ready for the next: calls that overlap on one GPU (two
  * streams, or two threads) race and must be serialised by the caller.  A

@@ -20,10 +20,12 @@ namespace {
 
 constexpr int kRowVecsPerThread = 8;    // target 16-byte vectors per thread per row split
 constexpr int kProfileRing = 2048;      // calls between forced event folds
-constexpr int kDrawWavesPerSimd = 3;    // draw kernel: waves per SIMD aimed at (one resident round)
+constexpr int kDrawBlocksPerWave = 2;   // draw kernel: blocks per wave in straight-line code
+constexpr int kDrawPerCU = 3;           // draw kernel: workgroups per CU aimed at
 
 struct Geometry {
     int splits;          // split rows kernel: workgroups per row
+    int nblocks;         // draw blocks per row
 };
 
 Geometry geometry_for(int vocab, int dtype) {
@@ -33,6 +35,7 @@ Geometry geometry_for(int vocab, int dtype) {
     s = std::max(1L, std::min(s, (long)sv::kMaxPieces));
     Geometry g;
     g.splits = static_cast<int>(s);
+    g.nblocks = (vocab + sv::kBlockElems - 1) / sv::kBlockElems;
     return g;
 }
 
@@ -56,20 +59,22 @@ int flat_workgroups(long nv, long vpr, int resident) {
 // that the dispatches themselves stamp: rows start / end, draw start / end (the
 // kernels' own execution, without the gap between dispatches).
 template <typename E>
-int launch_rows_draw(bool aligned, long grid1, long grid2, const sv::Params& P, hipStream_t stream,
+int launch_rows_draw(bool aligned, bool loop, long grid1, long grid2, const sv::Params& P, hipStream_t stream,
                      const hipEvent_t* ev) {
     const dim3 g1((unsigned)grid1), g2((unsigned)grid2), blk(sv::kThreads);
     if (!ev) {
         if (aligned) hipLaunchKernelGGL(sv::rows_flat_kernel<E>, g1, blk, 0, stream, P);
         else hipLaunchKernelGGL(sv::rows_split_kernel<E>, g1, blk, 0, stream, P);
-        hipLaunchKernelGGL(sv::draw_kernel<E>, g2, blk, 0, stream, P);
+        if (loop) hipLaunchKernelGGL((sv::draw_kernel<E, true>), g2, blk, 0, stream, P);
+        else hipLaunchKernelGGL((sv::draw_kernel<E, false>), g2, blk, 0, stream, P);
         return SV_OK;
     }
     if (aligned)
         hipExtLaunchKernelGGL(sv::rows_flat_kernel<E>, g1, blk, 0, stream, ev[0], ev[1], 0, P);
     else
         hipExtLaunchKernelGGL(sv::rows_split_kernel<E>, g1, blk, 0, stream, ev[0], ev[1], 0, P);
-    hipExtLaunchKernelGGL(sv::draw_kernel<E>, g2, blk, 0, stream, ev[2], ev[3], 0, P);
+    if (loop) hipExtLaunchKernelGGL((sv::draw_kernel<E, true>), g2, blk, 0, stream, ev[2], ev[3], 0, P);
+    else hipExtLaunchKernelGGL((sv::draw_kernel<E, false>), g2, blk, 0, stream, ev[2], ev[3], 0, P);
     return SV_OK;
 }
 
@@ -80,7 +85,7 @@ static_assert(SV_MAX_GAMMA + 1 <= sv::kMaxReqRows, "a request's rows fit the dra
 struct Scratch {
     sv::Piece* parts;
     sv::RowStat* rows;
-    sv::RangeRec* recs;
+    sv::BlockRec* recs;
     uint32_t* draw_cnt;
     uint32_t* err;
     uint32_t* err_host;
@@ -144,17 +149,24 @@ int enqueue(const Geometry& geo, int resident_flat, int cus, int resident_draw, 
     P.total_draft = a->total_draft;
     P.vocab = a->vocab;
     P.splits = geo.splits;
-    // draw ranges per row: about kDrawWavesPerSimd waves per SIMD over the call
-    // (one resident round, every wave one range), each range at most
-    // kRangeSubs sub-blocks and at least one sub-block, at most kMaxRanges, and
-    // a multiple of four (a workgroup's four waves take four ranges of one request)
-    const long n8 = ((long)a->vocab + 7) / 8;
-    const long nr_min = std::max(1L, (n8 + sv::kRangeSubs * 64 - 1) / (sv::kRangeSubs * 64));
-    const long nr_max = std::max(nr_min, std::min<long>(sv::kMaxRanges, std::max(1L, n8 / 64)));
-    const long waves_target = (long)kDrawWavesPerSimd * 4 * cus;
-    long nr = std::max(nr_min, std::min(nr_max, waves_target / a->batch));
-    if (nr > sv::kWaves) nr = std::min<long>(sv::kMaxRanges, (nr + sv::kWaves - 1) / sv::kWaves * sv::kWaves);
-    P.nranges = static_cast<int>(nr);
+    P.nblocks = geo.nblocks;
+    // draw workgroups per request: three per CU over the call (one resident
+    // round) where that keeps between one and kDrawBlocksPerWave blocks per
+    // wave (an even count per CU balances the fp64 work across the SIMDs).  A
+    // call with more draw rows than that round can hold at two blocks per wave
+    // (B = 128 or 256 at V = 151936 / 128256) takes a second round of
+    // workgroups when its residual blocks stream a dense q row too; with sparse
+    // or point-mass q (every block streams logits only, so a workgroup's
+    // fixed latency outweighs its bytes) its waves take pairs of blocks in a
+    // loop instead (measured: 100 against 110 us at B = 256 with top-50 lists,
+    // 114 against 109 us with dense q)
+    const int c_min = std::max(1, (geo.nblocks + sv::kWaves * kDrawBlocksPerWave - 1) /
+                                      (sv::kWaves * kDrawBlocksPerWave));
+    const int c_max = std::max(1, (geo.nblocks + sv::kWaves - 1) / sv::kWaves);
+    const int c_fit = kDrawPerCU * cus / a->batch;
+    const bool draw_loop = c_fit < c_min && qmode != sv::kQDense;
+    const int C = draw_loop ? std::max(1, c_fit) : std::max(c_min, std::min(c_max, c_fit));
+    P.draw_wgs = C;
     P.parts = sc.parts;
     P.rows = sc.rows;
     P.recs = sc.recs;
@@ -172,16 +184,13 @@ int enqueue(const Geometry& geo, int resident_flat, int cus, int resident_draw, 
     // ranges for 16-byte aligned rows, per-row splits otherwise) and every
     // request is resolved by its draw workgroups
     P.split_pieces = aligned ? 0 : P.splits;
-    const long qr = (nr + sv::kWaves - 1) / sv::kWaves;   // quads per request
     const long grid1 = aligned ? flat_workgroups(P.flat_nv, P.flat_vpr, resident_flat) : rows * P.splits;
-    // one workgroup per quad of ranges (four waves) up to what the device holds
-    // at once; past that, every workgroup takes a contiguous run of quads
-    const long quads = (long)a->batch * qr;
-    const long grid2 = std::max(1L, std::min(quads, (long)resident_draw));
+    const long grid2 = (long)a->batch * C;
     P.rows_grid = static_cast<int>(grid1);
+    P.draw_cmajor = grid2 <= resident_draw ? 1 : 0;
     const int st = (dtype == SV_BF16)
-                       ? launch_rows_draw<sv::BF16>(aligned, grid1, grid2, P, stream, ev)
-                       : launch_rows_draw<sv::F32>(aligned, grid1, grid2, P, stream, ev);
+                       ? launch_rows_draw<sv::BF16>(aligned, draw_loop, grid1, grid2, P, stream, ev)
+                       : launch_rows_draw<sv::F32>(aligned, draw_loop, grid1, grid2, P, stream, ev);
     if (st != SV_OK) return st;
     *schedule = aligned ? SV_SCHEDULE_FLAT : SV_SCHEDULE_SPLIT;
     return SV_OK;
@@ -202,7 +211,7 @@ struct sv_ctx {
     void* scratch = nullptr;
     sv::Piece* parts = nullptr;
     sv::RowStat* rows = nullptr;
-    sv::RangeRec* recs = nullptr;
+    sv::BlockRec* recs = nullptr;
     uint32_t* draw_cnt = nullptr;
     uint32_t* err = nullptr;
     // host-mapped pinned word the kernels set on a contract violation (checked by run)
@@ -289,7 +298,8 @@ constexpr size_t kStaticBatch = SV_STATIC_MAX_BATCH;
 constexpr size_t kOffParts = 0;
 constexpr size_t kOffRows = align_up_c(kOffParts + kStaticRows * sv::kMaxPieces * sizeof(sv::Piece), 256);
 constexpr size_t kOffRecs = align_up_c(kOffRows + kStaticRows * sizeof(sv::RowStat), 256);
-constexpr size_t kOffCnt = align_up_c(kOffRecs + kStaticBatch * sv::kMaxRanges * sizeof(sv::RangeRec), 256);
+constexpr size_t kStaticRecs = SV_STATIC_MAX_DRAW_BLOCKS;   // draw block records (batch times blocks per row) at most
+constexpr size_t kOffCnt = align_up_c(kOffRecs + kStaticRecs * sizeof(sv::BlockRec), 256);
 constexpr size_t kStaticBytes = align_up_c(kOffCnt + (kStaticBatch + 1) * sizeof(uint32_t), 256);
 static_assert(kStaticBytes <= SV_STATIC_SCRATCH_BYTES, "the static scratch holds its layout");
 
@@ -320,7 +330,7 @@ int static_device(int dev, StaticDevice** out) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sv::rows_flat_kernel<sv::BF16>, sv::kThreads, 0) !=
                 hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_draw, sv::draw_kernel<sv::BF16>, sv::kThreads, 0) !=
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_draw, sv::draw_kernel<sv::BF16, false>, sv::kThreads, 0) !=
                 hipSuccess) {
             (void)hipGetLastError();
             return SV_ERR_DEVICE;
@@ -385,7 +395,7 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
         ctx->cus = std::max(1, cus);
 
         int per_draw = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_draw, sv::draw_kernel<sv::BF16>,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_draw, sv::draw_kernel<sv::BF16, false>,
                                                          sv::kThreads, 0) == hipSuccess)
             ctx->resident_draw = cus * per_draw;
         if (ctx->resident_draw <= 0) ctx->resident_draw = 3 * std::max(1, cus);
@@ -396,7 +406,7 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
     size_t off = 0;
     const size_t o_parts = off; off = align_up(off + n_rows * sv::kMaxPieces * sizeof(sv::Piece), 256);
     const size_t o_rows = off;  off = align_up(off + n_rows * sizeof(sv::RowStat), 256);
-    const size_t o_recs = off;  off = align_up(off + n_b * sv::kMaxRanges * sizeof(sv::RangeRec), 256);
+    const size_t o_recs = off;  off = align_up(off + n_b * ctx->geo.nblocks * sizeof(sv::BlockRec), 256);
     const size_t o_cnt = off;   off = align_up(off + (n_b + 1) * sizeof(uint32_t), 256);
     const size_t total = off;
     if (hipMalloc(&ctx->scratch, total) != hipSuccess) {
@@ -407,7 +417,7 @@ int spec_verify_create(const sv_config* cfg, int device, sv_ctx** out) {
     char* base = static_cast<char*>(ctx->scratch);
     ctx->parts = reinterpret_cast<sv::Piece*>(base + o_parts);
     ctx->rows = reinterpret_cast<sv::RowStat*>(base + o_rows);
-    ctx->recs = reinterpret_cast<sv::RangeRec*>(base + o_recs);
+    ctx->recs = reinterpret_cast<sv::BlockRec*>(base + o_recs);
     ctx->draw_cnt = reinterpret_cast<uint32_t*>(base + o_cnt);
     ctx->err = ctx->draw_cnt + n_b;
     if (hipHostMalloc(reinterpret_cast<void**>(&ctx->err_host), sizeof(uint32_t),
@@ -546,7 +556,8 @@ int spec_verify_run_static(int logits_dtype, const sv_args* a, void* stream_ptr)
     if (a->vocab < 1) return SV_ERR_INVALID_ARG;
     if ((long)a->vocab > (long)sv::kMaxVocab) return SV_ERR_UNSUPPORTED;
     if (a->batch > SV_STATIC_MAX_BATCH || a->gamma > SV_MAX_GAMMA ||
-        (long)a->total_draft + (long)a->batch > (long)SV_STATIC_MAX_ROWS)
+        (long)a->total_draft + (long)a->batch > (long)SV_STATIC_MAX_ROWS ||
+        (long)a->batch * ((a->vocab + sv::kBlockElems - 1) / sv::kBlockElems) > (long)kStaticRecs)
         return SV_ERR_CAPACITY;
     int qmode = 0;
     const int st0 = check_args(SV_STATIC_MAX_BATCH, SV_MAX_GAMMA, a->vocab, logits_dtype, a, &qmode);
@@ -560,7 +571,7 @@ int spec_verify_run_static(int logits_dtype, const sv_args* a, void* stream_ptr)
     Scratch sc;
     sc.parts = reinterpret_cast<sv::Piece*>(sd->base + kOffParts);
     sc.rows = reinterpret_cast<sv::RowStat*>(sd->base + kOffRows);
-    sc.recs = reinterpret_cast<sv::RangeRec*>(sd->base + kOffRecs);
+    sc.recs = reinterpret_cast<sv::BlockRec*>(sd->base + kOffRecs);
     sc.draw_cnt = reinterpret_cast<uint32_t*>(sd->base + kOffCnt);
     sc.err = sc.draw_cnt + kStaticBatch;
     sc.err_host = nullptr;

@@ -47,12 +47,17 @@ constexpr int kThreads = 256;            // 4 waves of 64
 constexpr int kWaves = kThreads / 64;
 constexpr int kRowUnroll = 4;            // 16-byte vectors per thread per batch (two batches in flight)
 constexpr int kMaxPieces = 64;           // partials per row (at most one per merging thread)
-// The draw streams a row in sub-blocks of 512 consecutive tokens, lane L
-// holding tokens 8L .. 8L+7, so every 16-byte load instruction of the wave
-// reads one contiguous span.
+// A draw block is 2048 consecutive tokens of a draw row, worked on by one wave:
+// four sub-blocks of 512 tokens, lane L holding tokens 8L .. 8L+7 of each, so
+// every 16-byte load instruction of the wave reads one contiguous span.
 constexpr int kSubTokens = 8;                        // tokens per lane per sub-block
+constexpr int kSubBlocks = 4;
 constexpr int kSubElems = 64 * kSubTokens;           // 512
-constexpr int kMarginSlots = 2;          // marginal tokens kept inline per range record (code assumes 2)
+constexpr int kBlockElems = kSubBlocks * kSubElems;  // 2048
+constexpr int kMaxDrawBlocks = 256;                  // vocab up to 2^19 tokens
+constexpr int kMaxVocab = kMaxDrawBlocks * kBlockElems;   // 524288
+constexpr int kSelPer = kMaxDrawBlocks / 64;         // blocks per lane in the select
+constexpr int kMarginSlots = 2;          // marginal tokens kept inline per block record (code assumes 2)
 constexpr double kLog2e = 1.4426950408889634;
 constexpr double kQFloor = 1e-10;        // page section 5.2: q is floored at 1e-10 before dividing
 // Relative margin within which a residual weight's sign could depend on the
@@ -73,14 +78,36 @@ struct Piece {           // one (row, piece) partial
     double z;            // sum of exp2((l - m) * c) over the piece
 };
 
-struct RowStat {         // what a target row's piece 0 stores for the draw kernel's resolve
+struct RowStat {         // merged statistics of one target row
+    float m;             // max raw logit
+    int g;               // argmax (greedy rows), -1 otherwise
+    double z;            // normaliser Z (fp32 exponentials, fp64 sum)
     float lx;            // logit of the drafted token of this position
     float qx;            // q of the drafted token
-    int x;               // drafted token, -1 if invalid / none, -2 if its sparse q breaks the contract
-    int np;              // pieces the row was cut into
+    int x;               // drafted token, -1 if invalid / none
+    int pad;
 };
 
-struct RangeRec;         // per (request, draw range) sums, defined with the draw code
+struct DrawTask {        // written by the resolving workgroup, read by the draw kernel
+    int kind;            // kDraw*
+    int row;             // target row holding the draw distribution
+    int drow;            // draft row of q (residual only)
+    int pos;             // output column k
+    float v;             // uniform of the draw
+    float m;             // the draw row's max logit
+    double z32;          // the draw row's normaliser (fp32 exponentials)
+};
+
+struct BlockRec {        // per (request, draw block) sums
+    double se;           // sum of e = exp((l - m) / T) in fp64
+    double ea;           // sum of e over tokens whose residual is clearly positive
+    double qa;           // sum of q over the same tokens
+    int nm;              // tokens whose residual sign is marginal
+    int mx[kMarginSlots];        // their ids (first kMarginSlots, in token order)
+    float mq[kMarginSlots];      // their q
+    int pad;
+    double me[kMarginSlots];     // their e
+};
 
 struct Params {
     // problem
@@ -105,13 +132,15 @@ struct Params {
     int splits;          // split rows kernel: workgroups per row
     long flat_nv;        // flat rows kernel: total 16-byte vectors
     long flat_vpr;       // flat rows kernel: vectors per row
+    int draw_wgs;        // draw kernel: workgroups per request
+    int draw_cmajor;     // draw kernel: workgroup w serves request w % batch (else w / draw_wgs)
     int rows_grid;       // flat rows kernel: its grid (the piece geometry the draw kernel's resolve reads)
     int split_pieces;    // split rows kernel: pieces per row (0: the flat geometry)
-    int nranges;         // draw ranges per row (at most kMaxRanges)
+    int nblocks;         // draw blocks per row
     // scratch
     Piece* parts;        // [rows][kMaxPieces]
     RowStat* rows;
-    RangeRec* recs;      // [batch][kMaxRanges]
+    BlockRec* recs;
     uint32_t* draw_cnt;
     uint32_t* err;       // sticky contract-violation word (device)
     uint32_t* err_host;  // host-mapped copy the host checks before a call, or nullptr
@@ -756,7 +785,6 @@ __device__ __forceinline__ void row_piece_publish(const Params& P, int t, long v
             st_coherent(&rp->x, dt.x);
             st_coherent(&rp->lx, dt.lx);
             st_coherent(&rp->qx, dt.qx);
-            st_coherent(&rp->np, npieces);
         }
     }
 }
@@ -808,28 +836,7 @@ __global__ __launch_bounds__(kThreads) void rows_flat_kernel(Params P) {
     }
 }
 
-// ----------------------------------------------------------------- draw ranges
-// The draw of a request streams its draw row (residual (p - q)_+ at the first
-// rejection k, or the bonus p at gamma_b) in fp64.  The row is cut into
-// P.nranges contiguous token ranges of at most kRangeSubs sub-blocks of 512
-// tokens; every (request, range) pair is one unit of work for one wave, and a
-// wave holds a contiguous run of units (so consecutive units mostly belong to
-// one request, which the wave resolves once).  Waves never wait on each other:
-// each unit's sums go to its range record, and the wave that lands a request's
-// last record selects the token.
-constexpr int kRangeSubs = 8;                          // sub-blocks per range at most (4096 tokens)
-constexpr int kMaxRanges = 128;                        // ranges per draw row at most
-constexpr int kSelPer = kMaxRanges / 64;               // range records per lane in the select
-constexpr int kMaxVocab = kMaxRanges * kRangeSubs * kSubElems;   // 524288
-
-// First token of range j of nr over a row of V tokens: ranges start on
-// multiples of 8 tokens and differ in length by at most 8 tokens.
-__device__ __forceinline__ int range_start(int j, int nr, int V) {
-    if (j >= nr) return V;
-    const long n8 = (V + 7) >> 3;
-    return static_cast<int>(((long)j * n8) / nr) * 8;
-}
-
+// ----------------------------------------------------------------- draw blocks
 // Everything a wave needs to work on one request's draw row.
 template <typename E>
 struct DrawRow {
@@ -843,7 +850,7 @@ struct DrawRow {
     const typename E::T* lrow;
     const float* qrow;   // residual with dense q: q row, else nullptr
     bool lalign, qalign;
-    // residual with sparse or point-mass q: the range sums are those of p, and the
+    // residual with sparse or point-mass q: the block sums are those of p, and the
     // select takes the listed tokens' q off them; entry s of the draft row is
     // token sid[s] with q = sq[s] (point mass: sid = the drafted token, sq null, q = 1)
     bool qlist;
@@ -858,20 +865,24 @@ __device__ __forceinline__ double draw_e(const DrawRow<E>& d, float l, const dou
     return exp2_tab(fma(static_cast<double>(l), d.c2, -d.mc2), tab);
 }
 
-// One lane's 8 tokens of one sub-block as loaded (raw element bits).
+// One lane's 8 tokens of one sub-block as loaded (raw element bits), and its
+// 32 tokens of a whole block.
 template <typename E>
 struct RawSub {
     v4u l[kSubTokens / E::kPerVec];
     v4u q[kSubTokens / 4];
 };
-
-// Loads of this lane's tokens [x0, x0 + 8) of any row, element by element where
-// the row's alignment or its end require it (tokens at or past xend read as
-// -inf logits and q = 0).
 template <typename E>
-__device__ __forceinline__ void issue_sub_any(const DrawRow<E>& d, long x0, int xend, bool with_q, RawSub<E>& r) {
+struct RawBlock {
+    RawSub<E> s[kSubBlocks];
+};
+
+// Loads of this lane's tokens [x0, x0 + 8) of any row: vectors where the row
+// allows, else element by element (logits past V read as -inf, q as 0).
+template <typename E>
+__device__ __forceinline__ void issue_sub_any(const DrawRow<E>& d, long x0, int V, bool with_q, RawSub<E>& r) {
     constexpr int NL = kSubTokens / E::kPerVec;
-    const bool full = x0 + kSubTokens <= xend;
+    const bool full = x0 + kSubTokens <= V;
     if (full && d.lalign) {
         const v4u* lp = reinterpret_cast<const v4u*>(d.lrow + x0);
 #pragma unroll
@@ -882,7 +893,7 @@ __device__ __forceinline__ void issue_sub_any(const DrawRow<E>& d, long x0, int 
         for (int k = 0; k < 4 * NL; ++k) w[k] = 0u;
 #pragma unroll
         for (int k = 0; k < kSubTokens; ++k) {
-            const uint32_t bits = (x0 + k < xend) ? E::bits1(d.lrow, x0 + k) : E::kNegInfBits;
+            const uint32_t bits = (x0 + k < V) ? E::bits1(d.lrow, x0 + k) : E::kNegInfBits;
             if (E::kBits == 16) w[k >> 1] |= bits << (16 * (k & 1));
             else w[k] = bits;
         }
@@ -897,7 +908,7 @@ __device__ __forceinline__ void issue_sub_any(const DrawRow<E>& d, long x0, int 
         } else {
             uint32_t w[kSubTokens];
 #pragma unroll
-            for (int k = 0; k < kSubTokens; ++k) w[k] = (x0 + k < xend) ? __float_as_uint(d.qrow[x0 + k]) : 0u;
+            for (int k = 0; k < kSubTokens; ++k) w[k] = (x0 + k < V) ? __float_as_uint(d.qrow[x0 + k]) : 0u;
 #pragma unroll
             for (int h = 0; h < kSubTokens / 4; ++h) r.q[h] = v4u{w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]};
         }
@@ -907,29 +918,15 @@ __device__ __forceinline__ void issue_sub_any(const DrawRow<E>& d, long x0, int 
     }
 }
 
-// Vector loads of this lane's tokens [x, x + 8) of a 16-byte aligned row (and q
-// row); a lane past the range's end loads the range's first tokens instead and
-// has them replaced by mask_sub.
-template <typename E, bool kWithQ>
-__device__ __forceinline__ void issue_sub_fast(const DrawRow<E>& d, int x, int x0, int x1, RawSub<E>& r) {
-    const int xa = x < x1 ? x : x0;
-    const v4u* lp = reinterpret_cast<const v4u*>(d.lrow + xa);
-#pragma unroll
-    for (int h = 0; h < kSubTokens / E::kPerVec; ++h) r.l[h] = __builtin_nontemporal_load(lp + h);
-    if (kWithQ) {
-        const v4u* qp = reinterpret_cast<const v4u*>(d.qrow + xa);
-#pragma unroll
-        for (int h = 0; h < kSubTokens / 4; ++h) r.q[h] = __builtin_nontemporal_load(qp + h);
-    }
+// This lane's first token of sub-block u of the block starting at xb.
+__device__ __forceinline__ long sub_first(long xb, int u) {
+    return xb + u * kSubElems + (threadIdx.x & 63) * kSubTokens;
 }
-template <typename E, bool kWithQ>
-__device__ __forceinline__ void mask_sub(RawSub<E>& r, bool in) {
+
+template <typename E>
+__device__ __forceinline__ void issue_block_any(const DrawRow<E>& d, long xb, int V, bool with_q, RawBlock<E>& r) {
 #pragma unroll
-    for (int h = 0; h < kSubTokens / E::kPerVec; ++h) r.l[h] = in ? r.l[h] : v4u(E::kNegInfWord);
-    if (kWithQ) {
-#pragma unroll
-        for (int h = 0; h < kSubTokens / 4; ++h) r.q[h] = in ? r.q[h] : v4u(0u);
-    }
+    for (int u = 0; u < kSubBlocks; ++u) issue_sub_any<E>(d, sub_first(xb, u), V, with_q, r.s[u]);
 }
 
 template <typename E>
@@ -957,17 +954,50 @@ __device__ __forceinline__ float sub_q(const RawSub<E>& r, int k) {
     return __uint_as_float(r.q[k >> 2][k & 3]);
 }
 
-// Range sums: residual rows split the tokens three ways with the fp32-pass
+// Rare path of block_record: stores the block's first kMarginSlots marginal
+// tokens in token order (sub-block, then lane, then position in the lane),
+// reloading each from memory.  Kept out of line so that the common path's
+// register allocation does not carry it.
+template <typename E>
+__device__ __noinline__ void record_marginal(const typename E::T* lrow, const float* qrow, double c2, double mc2,
+                                             long xb, uint32_t mmask, const double* tab, BlockRec* rec) {
+    const int lane = threadIdx.x & 63;
+    int slot = 0;
+    for (int u = 0; u < kSubBlocks && slot < kMarginSlots; ++u) {
+        const uint32_t mu = (mmask >> (u * kSubTokens)) & 0xffu;
+        unsigned long long lanes = __ballot(mu != 0u);
+        while (lanes != 0ull && slot < kMarginSlots) {
+            const int L = __ffsll(static_cast<long long>(lanes)) - 1;
+            lanes &= lanes - 1ull;
+            uint32_t bits = static_cast<uint32_t>(rdlane(static_cast<int>(mu), L));
+            while (bits != 0u && slot < kMarginSlots) {
+                const int k = __ffs(static_cast<int>(bits)) - 1;
+                bits &= bits - 1u;
+                if (lane == 0) {
+                    const long x = xb + u * kSubElems + L * kSubTokens + k;
+                    st_coherent(&rec->mx[slot], static_cast<int>(x));
+                    st_coherent(&rec->mq[slot], qrow[x]);
+                    st_coherent(&rec->me[slot],
+                                exp2_tab(fma(static_cast<double>(E::load1(lrow, x)), c2, -mc2), tab));
+                }
+                ++slot;
+            }
+        }
+    }
+}
+
+// Block sums: residual rows split the tokens three ways with the fp32-pass
 // normaliser: clearly positive residual (e / Z32 * (1 - margin) > q: summed
 // into ea and qa), clearly non-positive (e / Z32 * (1 + margin) <= q: dropped)
 // and marginal (the rest: counted, the first kMarginSlots in token order kept
-// in the record).  Branch-free except for the marginal capture, which only runs
-// when the wave has a marginal token.
+// inline).  Branch-free except for the marginal capture, which only runs when
+// the wave has a marginal token.
 struct BlockSums {
     double se = -0.0, ea = -0.0, qa = -0.0;   // -0.0 + x is x: the first adds fold away
-    uint64_t mmask = 0ull;                    // bit 8s + k: token k of this lane's sub-block s is marginal
+    uint32_t mmask = 0u;                      // bit 8u + k: token k of sub-block u is marginal
 };
 
+// Adds one lane's 8 decoded tokens of sub-block u, two at a time.
 template <typename E, bool kResidual>
 __device__ __forceinline__ void accumulate_token(const DrawRow<E>& d, float l, float q, int bit, double apos,
                                                  double aneg, const double* tab, BlockSums& b) {
@@ -980,14 +1010,30 @@ __device__ __forceinline__ void accumulate_token(const DrawRow<E>& d, float l, f
         const double wpos = pos ? 1.0 : 0.0;
         b.ea = fma(e, wpos, b.ea);
         b.qa = fma(qd, wpos, b.qa);
-        b.mmask |= static_cast<uint64_t>(marg) << bit;
+        b.mmask |= static_cast<uint32_t>(marg) << bit;
     }
 }
 
-// The sums of one loaded sub-block (sub-block s of the range), four (bf16) or two
-// (fp32) tokens at a time, with no decoded copy of the sub-block held in registers.
 template <typename E, bool kResidual>
-__device__ __forceinline__ void accumulate_raw(const DrawRow<E>& d, const RawSub<E>& r, int s, double apos,
+__device__ __forceinline__ void accumulate_sub(const DrawRow<E>& d, const float* l, const float* q, int u, double apos,
+                                               double aneg, const double* tab, BlockSums& b) {
+#pragma unroll
+    for (int k = 0; k < kSubTokens; k += 2) {
+        float la = l[k], lb = l[k + 1];
+        // each pair starts once the previous pair is summed: the unrolled
+        // chains would otherwise be interleaved before scheduling, with every
+        // token's temporaries live at once
+        if (k > 0) asm volatile("" : "+v"(la), "+v"(lb) : "v"(b.se));
+        accumulate_token<E, kResidual>(d, la, q[k], u * kSubTokens + k, apos, aneg, tab, b);
+        accumulate_token<E, kResidual>(d, lb, q[k + 1], u * kSubTokens + k + 1, apos, aneg, tab, b);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The same sums taken straight from a loaded sub-block, four (bf16) or two (fp32) tokens at a time,
+// with no decoded copy of the sub-block held in registers.
+template <typename E, bool kResidual>
+__device__ __forceinline__ void accumulate_raw(const DrawRow<E>& d, const RawSub<E>& r, int u, double apos,
                                                double aneg, const double* tab, BlockSums& b) {
     if constexpr (sizeof(typename E::T) == 2) {
         // bf16: four tokens at a time (more independent fp64 chains per wave;
@@ -996,17 +1042,14 @@ __device__ __forceinline__ void accumulate_raw(const DrawRow<E>& d, const RawSub
         for (int k = 0; k < kSubTokens; k += 4) {
             float la = sub_logit<E>(r, k), lb = sub_logit<E>(r, k + 1);
             float lc = sub_logit<E>(r, k + 2), ld = sub_logit<E>(r, k + 3);
-            // each group starts once the previous one is summed: the unrolled
-            // chains would otherwise be interleaved before scheduling, with every
-            // token's temporaries live at once
             if (k > 0) asm volatile("" : "+v"(la), "+v"(lb), "+v"(lc), "+v"(ld) : "v"(b.se));
-            accumulate_token<E, kResidual>(d, la, kResidual ? sub_q<E>(r, k) : 0.0f, s * kSubTokens + k, apos,
+            accumulate_token<E, kResidual>(d, la, kResidual ? sub_q<E>(r, k) : 0.0f, u * kSubTokens + k, apos,
                                            aneg, tab, b);
-            accumulate_token<E, kResidual>(d, lb, kResidual ? sub_q<E>(r, k + 1) : 0.0f, s * kSubTokens + k + 1,
+            accumulate_token<E, kResidual>(d, lb, kResidual ? sub_q<E>(r, k + 1) : 0.0f, u * kSubTokens + k + 1,
                                            apos, aneg, tab, b);
-            accumulate_token<E, kResidual>(d, lc, kResidual ? sub_q<E>(r, k + 2) : 0.0f, s * kSubTokens + k + 2,
+            accumulate_token<E, kResidual>(d, lc, kResidual ? sub_q<E>(r, k + 2) : 0.0f, u * kSubTokens + k + 2,
                                            apos, aneg, tab, b);
-            accumulate_token<E, kResidual>(d, ld, kResidual ? sub_q<E>(r, k + 3) : 0.0f, s * kSubTokens + k + 3,
+            accumulate_token<E, kResidual>(d, ld, kResidual ? sub_q<E>(r, k + 3) : 0.0f, u * kSubTokens + k + 3,
                                            apos, aneg, tab, b);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -1015,112 +1058,103 @@ __device__ __forceinline__ void accumulate_raw(const DrawRow<E>& d, const RawSub
         for (int k = 0; k < kSubTokens; k += 2) {
             float la = sub_logit<E>(r, k), lb = sub_logit<E>(r, k + 1);
             if (k > 0) asm volatile("" : "+v"(la), "+v"(lb) : "v"(b.se));
-            accumulate_token<E, kResidual>(d, la, kResidual ? sub_q<E>(r, k) : 0.0f, s * kSubTokens + k, apos,
+            accumulate_token<E, kResidual>(d, la, kResidual ? sub_q<E>(r, k) : 0.0f, u * kSubTokens + k, apos,
                                            aneg, tab, b);
-            accumulate_token<E, kResidual>(d, lb, kResidual ? sub_q<E>(r, k + 1) : 0.0f, s * kSubTokens + k + 1,
+            accumulate_token<E, kResidual>(d, lb, kResidual ? sub_q<E>(r, k + 1) : 0.0f, u * kSubTokens + k + 1,
                                            apos, aneg, tab, b);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
 
-// This lane's first token of sub-block s of the range starting at x0.
-__device__ __forceinline__ int sub_first(int x0, int s) {
-    return x0 + s * kSubElems + (threadIdx.x & 63) * kSubTokens;
+// Wave totals of a block's sums, written to its record with device-scope
+// stores (plus the inline marginal tokens).  Wave-uniform call.
+template <typename E, bool kResidual>
+__device__ __forceinline__ void store_record(const DrawRow<E>& d, long xb, BlockSums b, const double* tab,
+                                             BlockRec* rec) {
+    const int lane = threadIdx.x & 63;
+    const double se = wave_sum(b.se);
+    double ea = 0.0, qa = 0.0;
+    int nmw = 0;
+    if (kResidual) {
+        ea = wave_sum(b.ea);
+        qa = wave_sum(b.qa);
+        if (__ballot(b.mmask != 0u) != 0ull) nmw = wave_sum_int(__popc(b.mmask));
+    }
+    if (lane == 0) {
+        st_coherent(&rec->se, se);
+        st_coherent(&rec->ea, ea);
+        st_coherent(&rec->qa, qa);
+        st_coherent(&rec->nm, nmw);
+    }
+    if (kResidual && nmw > 0 && nmw <= kMarginSlots)
+        record_marginal<E>(d.lrow, d.qrow, d.c2, d.mc2, xb, b.mmask, tab, rec);
 }
 
-// Sums over tokens [x0, x1) of the draw row (at most kRangeSubs sub-blocks).  In
-// 16-byte aligned rows whose range ends on a multiple of 8 tokens, four
-// sub-blocks of loads stay in flight: each sub-block's registers are refilled
-// with the sub-block four ahead once its tokens are summed.  Every load is
-// issued outside any branch (lanes and sub-blocks past the range load the
-// range's first tokens and are masked or skipped), so the compiler waits for
-// exactly the sub-block it needs; a branch around a load would leave it
-// waiting for all of them.  Other ranges load element by element.
+// Sums of one loaded block (any row layout).
 template <typename E, bool kResidual>
-__device__ __forceinline__ BlockSums range_sums(const DrawRow<E>& d, int x0, int x1, double apos, double aneg,
-                                                const double* tab) {
-    const int ns = (x1 - x0 + kSubElems - 1) / kSubElems;    // wave-uniform, 1..kRangeSubs
+__device__ __forceinline__ void block_record(const DrawRow<E>& d, const RawBlock<E>& r, long xb, double apos,
+                                             double aneg, const double* tab, BlockRec* rec) {
     BlockSums b;
-    const bool fast = d.lalign && (!kResidual || d.qalign) && (x1 & 7) == 0;
-    if (fast) {
-        RawSub<E> r[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) issue_sub_fast<E, kResidual>(d, sub_first(x0, s), x0, x1, r[s]);
-        // keeps the loads where they are issued: without it the compiler sinks
-        // a load next to its first use inside a branch, behind the later loads
-        asm volatile("" ::: "memory");
+    for (int u = 0; u < kSubBlocks; ++u) {
+        float l[kSubTokens], q[kSubTokens];
+        decode_sub<E>(r.s[u], kResidual, l, q);
+        accumulate_sub<E, kResidual>(d, l, q, u, apos, aneg, tab, b);
+    }
+    store_record<E, kResidual>(d, xb, b, tab, rec);
+}
+
+// Loads of this lane's tokens [x0, x0 + 8) of a block lying wholly inside a
+// 16-byte aligned row (and q row): plain vector loads.
+template <typename E, bool kWithQ>
+__device__ __forceinline__ void issue_sub_full(const DrawRow<E>& d, int x0, RawSub<E>& r) {
+    const v4u* lp = reinterpret_cast<const v4u*>(d.lrow + x0);
 #pragma unroll
-        for (int s = 0; s < kRangeSubs; ++s) {
-            if (s < ns) {
-                if (s == ns - 1) mask_sub<E, kResidual>(r[s & 3], sub_first(x0, s) < x1);
-                accumulate_raw<E, kResidual>(d, r[s & 3], s, apos, aneg, tab, b);
-            }
-            if (s + 4 < kRangeSubs) {
-                issue_sub_fast<E, kResidual>(d, sub_first(x0, s + 4), x0, x1, r[s & 3]);
-                asm volatile("" ::: "memory");
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    } else {
-        for (int s = 0; s < ns; ++s) {
-            RawSub<E> r;
-            issue_sub_any<E>(d, sub_first(x0, s), x1, kResidual, r);
-            accumulate_raw<E, kResidual>(d, r, s, apos, aneg, tab, b);
-        }
+    for (int h = 0; h < kSubTokens / E::kPerVec; ++h) r.l[h] = __builtin_nontemporal_load(lp + h);
+    if (kWithQ) {
+        const v4u* qp = reinterpret_cast<const v4u*>(d.qrow + x0);
+#pragma unroll
+        for (int h = 0; h < kSubTokens / 4; ++h) r.q[h] = __builtin_nontemporal_load(qp + h);
+    }
+}
+
+// This lane's first token of sub-block u of the block starting at xb (32-bit:
+// rows hold at most 2^19 tokens).
+__device__ __forceinline__ int sub_first32(int xb, int u) {
+    return xb + u * kSubElems + (threadIdx.x & 63) * kSubTokens;
+}
+
+// Sums of one block of a whole-vector row whose loads are in r; once a
+// sub-block's tokens are summed, its registers are refilled with that sub-block
+// of block xn (kRefill), so the wave keeps about a block's loads in flight.
+// No calls: a call would leave the compiler unable to wait for one refill
+// while the later ones stay in flight.
+template <typename E, bool kResidual, bool kRefill>
+__device__ __forceinline__ BlockSums block_stream(const DrawRow<E>& d, RawBlock<E>& r, int xb, int xn, int V,
+                                                  double apos, double aneg, const double* tab) {
+    BlockSums b;
+#pragma unroll
+    for (int u = 0; u < kSubBlocks; ++u) {
+        accumulate_raw<E, kResidual>(d, r.s[u], u, apos, aneg, tab, b);
+        if (kRefill) issue_sub_full<E, kResidual>(d, sub_first32(xn, u), r.s[u]);
+        __builtin_amdgcn_sched_barrier(0);
     }
     return b;
 }
 
-// Per (request, range) sums of the draw row.
-struct RangeRec {
-    double se;           // sum of e = exp((l - m) / T) in fp64
-    double ea;           // sum of e over tokens whose residual is clearly positive
-    double qa;           // sum of q over the same tokens
-    int nm;              // tokens whose residual sign is marginal
-    int mx[kMarginSlots];        // their ids (first kMarginSlots, in token order)
-    float mq[kMarginSlots];      // their q
-    int pad;
-    double me[kMarginSlots];     // their e
+// Wave totals of one streamed block, stored to its record; a block with inline
+// marginal tokens is remembered (at most two per stream; further ones are left
+// for the select to re-evaluate from their tokens) and captured after the
+// stream has ended.
+struct StreamCaps {
+    int n = 0;                    // wave-uniform
+    int j0 = 0, j1 = 0;           // blocks to capture
+    uint32_t m0 = 0u, m1 = 0u;    // their marginal masks (per lane)
 };
 
-// Rare path of range_finish: stores the range's first kMarginSlots marginal
-// tokens in token order (sub-block, then lane, then position in the lane),
-// reloading each from memory.  Kept out of line so that the common path's
-// register allocation does not carry it.
-template <typename E>
-__device__ __noinline__ void record_marginal(const typename E::T* lrow, const float* qrow, double c2, double mc2,
-                                             int x0, uint64_t mmask, const double* tab, RangeRec* rec) {
-    const int lane = threadIdx.x & 63;
-    int slot = 0;
-    for (int s = 0; s < kRangeSubs && slot < kMarginSlots; ++s) {
-        const uint32_t ms = static_cast<uint32_t>(mmask >> (s * kSubTokens)) & 0xffu;
-        unsigned long long lanes = __ballot(ms != 0u);
-        while (lanes != 0ull && slot < kMarginSlots) {
-            const int L = __ffsll(static_cast<long long>(lanes)) - 1;
-            lanes &= lanes - 1ull;
-            uint32_t bits = static_cast<uint32_t>(rdlane(static_cast<int>(ms), L));
-            while (bits != 0u && slot < kMarginSlots) {
-                const int k = __ffs(static_cast<int>(bits)) - 1;
-                bits &= bits - 1u;
-                if (lane == 0) {
-                    const long x = (long)x0 + s * kSubElems + L * kSubTokens + k;
-                    st_coherent(&rec->mx[slot], static_cast<int>(x));
-                    st_coherent(&rec->mq[slot], qrow[x]);
-                    st_coherent(&rec->me[slot],
-                                exp2_tab(fma(static_cast<double>(E::load1(lrow, x)), c2, -mc2), tab));
-                }
-                ++slot;
-            }
-        }
-    }
-}
-
-// Wave totals of a range's sums, written to its record with device-scope stores
-// (plus the inline marginal tokens).  Wave-uniform call.
-template <typename E, bool kResidual>
-__device__ __forceinline__ void range_finish(const DrawRow<E>& d, int x0, const BlockSums& b, const double* tab,
-                                             RangeRec* rec) {
+template <bool kResidual>
+__device__ __forceinline__ void stream_finish(const BlockSums& b, int j, BlockRec* recs, StreamCaps& c) {
     const int lane = threadIdx.x & 63;
     const double se = wave_sum(b.se);
     double ea = 0.0, qa = 0.0;
@@ -1128,16 +1162,392 @@ __device__ __forceinline__ void range_finish(const DrawRow<E>& d, int x0, const 
     if (kResidual) {
         ea = wave_sum(b.ea);
         qa = wave_sum(b.qa);
-        if (__ballot(b.mmask != 0ull) != 0ull) nm = wave_sum_int(__popcll(b.mmask));
+        if (__ballot(b.mmask != 0u) != 0ull) nm = wave_sum_int(__popc(b.mmask));
+    }
+    if (kResidual && nm > 0 && nm <= kMarginSlots) {
+        // selects rather than branches, so the fields stay in registers
+        const bool first = (c.n == 0), second = (c.n == 1);
+        c.j0 = first ? j : c.j0;
+        c.m0 = first ? b.mmask : c.m0;
+        c.j1 = second ? j : c.j1;
+        c.m1 = second ? b.mmask : c.m1;
+        if (c.n >= 2) nm = kMarginSlots + 1;
+        c.n = min(c.n + 1, 2);
     }
     if (lane == 0) {
+        BlockRec* rec = &recs[j];
         st_coherent(&rec->se, se);
         st_coherent(&rec->ea, ea);
         st_coherent(&rec->qa, qa);
         st_coherent(&rec->nm, nm);
     }
-    if (kResidual && nm > 0 && nm <= kMarginSlots)
-        record_marginal<E>(d.lrow, d.qrow, d.c2, d.mc2, x0, b.mmask, tab, rec);
+}
+
+// Blocks jfirst and, if n == 2, jfirst + jstride of a whole-vector row, all of
+// their loads issued before the first is summed.  Straight-line code: with a
+// loop around it the compiler's allocation spills.
+template <typename E, bool kResidual>
+__device__ __forceinline__ void draw_blocks_upto2(const DrawRow<E>& d, int V, BlockRec* recs, int j, int jstride,
+                                                  int n, double apos, double aneg, const double* tab,
+                                                  StreamCaps& c) {
+    RawBlock<E> r;
+#pragma unroll
+    for (int u = 0; u < kSubBlocks; ++u) issue_sub_full<E, kResidual>(d, sub_first32(j * kBlockElems, u), r.s[u]);
+    if (n >= 2) {
+        const int j2 = j + jstride;
+        const BlockSums b1 = block_stream<E, kResidual, true>(d, r, j * kBlockElems, j2 * kBlockElems, V, apos, aneg,
+                                                             tab);
+        stream_finish<kResidual>(b1, j, recs, c);
+        const BlockSums b2 = block_stream<E, kResidual, false>(d, r, j2 * kBlockElems, 0, V, apos, aneg, tab);
+        stream_finish<kResidual>(b2, j2, recs, c);
+    } else {
+        const BlockSums b = block_stream<E, kResidual, false>(d, r, j * kBlockElems, 0, V, apos, aneg, tab);
+        stream_finish<kResidual>(b, j, recs, c);
+    }
+}
+
+template <typename E, bool kResidual>
+__device__ __forceinline__ void capture_marginals(const DrawRow<E>& d, BlockRec* recs, const StreamCaps& c,
+                                                  const double* tab) {
+    if (kResidual && c.n > 0)
+        record_marginal<E>(d.lrow, d.qrow, d.c2, d.mc2, (long)c.j0 * kBlockElems, c.m0, tab, &recs[c.j0]);
+    if (kResidual && c.n > 1)
+        record_marginal<E>(d.lrow, d.qrow, d.c2, d.mc2, (long)c.j1 * kBlockElems, c.m1, tab, &recs[c.j1]);
+}
+
+// Per-block sums of draw blocks jfirst, jfirst + jstride, ... < jend, written to
+// recs.  In 16-byte aligned rows, blocks lying wholly inside the row are taken
+// two at a time with all of their loads in flight together (kUpTo2: the caller
+// guarantees at most two blocks, and no loop is generated around them); the
+// row's ragged last block, and every block of other rows, is taken on its own.
+template <typename E, bool kResidual, bool kUpTo2>
+__device__ __forceinline__ void draw_blocks_kind(const DrawRow<E>& d, int V, BlockRec* recs, int jfirst, int jstride,
+                                                 int jend, const double* tab) {
+    const double invZ32 = 1.0 / d.z32;
+    const double apos = invZ32 * (1.0 - kSignMargin), aneg = invZ32 * (1.0 + kSignMargin);
+    const bool fastrow = d.lalign && (!kResidual || d.qalign);
+    int jany = jfirst;                             // first block taken on its own
+    if (fastrow) {
+        const int jfull = V / kBlockElems;         // blocks wholly inside the row
+        const int jend_full = jend < jfull ? jend : jfull;
+        StreamCaps c;
+        int j = jfirst;
+        if (kUpTo2) {
+            if (j < jend_full) {
+                const int n = j + jstride < jend_full ? 2 : 1;
+                draw_blocks_upto2<E, kResidual>(d, V, recs, j, jstride, n, apos, aneg, tab, c);
+                j += n * jstride;
+            }
+        } else {
+            while (j < jend_full) {
+                const int n = j + jstride < jend_full ? 2 : 1;
+                draw_blocks_upto2<E, kResidual>(d, V, recs, j, jstride, n, apos, aneg, tab, c);
+                j += n * jstride;
+            }
+        }
+        capture_marginals<E, kResidual>(d, recs, c, tab);
+        jany = j;
+    }
+    for (int j = jany; j < jend; j += jstride) {
+        RawBlock<E> r;
+        const long xb = (long)j * kBlockElems;
+        issue_block_any<E>(d, xb, V, kResidual, r);
+        block_record<E, kResidual>(d, r, xb, apos, aneg, tab, &recs[j]);
+    }
+}
+
+template <typename E, bool kUpTo2 = false>
+__device__ __forceinline__ void draw_blocks(const DrawRow<E>& d, int V, BlockRec* recs, int jfirst, int jstride, int jend,
+                            const double* tab) {
+    if (d.kind == kDrawResidual && !d.qlist) draw_blocks_kind<E, true, kUpTo2>(d, V, recs, jfirst, jstride, jend, tab);
+    else draw_blocks_kind<E, false, kUpTo2>(d, V, recs, jfirst, jstride, jend, tab);
+}
+
+// The select for one request, once all its draw blocks are recorded: the block
+// holding the draw, then the token inside it.
+//
+// Block choice, by one wave (no LDS besides the exponential table; every lane
+// gets the result).  Rebuilds the exact fp64 normaliser Z64 and every block's
+// weight (e / Z64 - q summed over the clearly positive tokens plus the inline
+// marginal ones; blocks with more marginal tokens than slots, or every block
+// when the fp32-pass normaliser is off by more than half the margin, are
+// re-evaluated from their tokens) and finds the block holding v * S by a scan
+// over blocks (kSelPer consecutive blocks per lane).
+struct SelBlock {
+    int jsel;            // selected block
+    double base;         // weight of the blocks before it
+    double tsel;         // v * S
+    double invZ64;
+    bool res_w;          // token weights are residuals (else e)
+    bool with_q;         // residual weights read a dense q row (else q = 0 off the list)
+    bool fallback;       // rounding left no crossing: take the block's last positive token
+    // listed q (sparse or point mass): lane s holds entry s; qmask: the entries
+    // inside the selected block (wave-uniform)
+    int qid;
+    float qq;
+    unsigned long long qmask;
+};
+
+template <typename E>
+__device__ __forceinline__ SelBlock select_block(const DrawRow<E>& d, int V, int NB, const BlockRec* recs,
+                                                 const double* tab, uint32_t* err, uint32_t* err_host) {
+    const int lane = threadIdx.x & 63;
+    const bool residual = (d.kind == kDrawResidual);
+    // every field of this lane's records in one round of loads
+    double se_t[kSelPer], ea_t[kSelPer], qa_t[kSelPer];
+    int nm_t[kSelPer];
+#pragma unroll
+    for (int r = 0; r < kSelPer; ++r) {
+        const int j = lane * kSelPer + r;
+        const bool in = j < NB;
+        const BlockRec* rc = &recs[in ? j : 0];
+        se_t[r] = in ? ld_coherent(&rc->se) : 0.0;
+        ea_t[r] = qa_t[r] = 0.0;
+        nm_t[r] = 0;
+        if (residual && !d.qlist && in) {
+            ea_t[r] = ld_coherent(&rc->ea);
+            qa_t[r] = ld_coherent(&rc->qa);
+            nm_t[r] = ld_coherent(&rc->nm);
+        }
+    }
+    double zpart = 0.0;
+#pragma unroll
+    for (int r = 0; r < kSelPer; ++r) zpart += se_t[r];
+    const double Z64 = wave_sum(zpart);
+    const double invZ64 = 1.0 / Z64;
+    int kind = d.kind;
+    double wt[kSelPer];
+    int qid = -1;
+    float qq = 0.0f;
+    bool qvalid = false;
+    if (residual && d.qlist) {
+        // q is zero except at the listed tokens: block weights are the blocks' p
+        // mass less min(p, q) of the listed tokens they hold (p - (p - q)_+)
+        if (lane < d.nq) {
+            qid = d.sid[lane];
+            qq = d.sq ? d.sq[lane] : 1.0f;
+        }
+        qvalid = qid >= 0 && qid < V;
+        if (lane < d.nq && !qvalid && qid != -1) flag_error(err, err_host, kErrTopk);
+        double cs = 0.0;
+        if (qvalid) cs = fmin(draw_e<E>(d, E::load1(d.lrow, qid), tab) * invZ64, static_cast<double>(qq));
+        const int qblk = qvalid ? qid / kBlockElems : -1;
+#pragma unroll
+        for (int r = 0; r < kSelPer; ++r) wt[r] = se_t[r] * invZ64;
+        for (int s = 0; s < d.nq; ++s) {
+            const int js = rdlane(qblk, s);
+            if (js < 0) continue;
+            const double c = rdlane(cs, s);
+#pragma unroll
+            for (int r = 0; r < kSelPer; ++r)
+                if (lane * kSelPer + r == js) wt[r] -= c;
+        }
+    } else if (residual) {
+        const bool full = !(fabs(Z64 - d.z32) <= 0.5 * kSignMargin * Z64);
+#pragma unroll
+        for (int r = 0; r < kSelPer; ++r) wt[r] = ea_t[r] * invZ64 - qa_t[r];
+        // blocks with inline marginal tokens (a slot is only meaningful when the
+        // block recorded it): one more round of loads, only when there are any
+        bool any_slots = false;
+#pragma unroll
+        for (int r = 0; r < kSelPer; ++r) any_slots |= (nm_t[r] > 0 && nm_t[r] <= kMarginSlots);
+        if (__ballot(any_slots) != 0ull) {
+#pragma unroll
+            for (int r = 0; r < kSelPer; ++r) {
+                const int j = lane * kSelPer + r;
+                if (j < NB && nm_t[r] > 0 && nm_t[r] <= kMarginSlots) {
+                    const BlockRec* rc = &recs[j];
+                    wt[r] += fmax(ld_coherent(&rc->me[0]) * invZ64 - static_cast<double>(ld_coherent(&rc->mq[0])), 0.0);
+                    if (nm_t[r] > 1)
+                        wt[r] += fmax(ld_coherent(&rc->me[1]) * invZ64 - static_cast<double>(ld_coherent(&rc->mq[1])), 0.0);
+                }
+            }
+        }
+        // rare: blocks re-evaluated from their tokens, one at a time by the wave
+#pragma unroll
+        for (int r = 0; r < kSelPer; ++r) {
+            const int j = lane * kSelPer + r;
+            unsigned long long need = __ballot(j < NB && (full || nm_t[r] > kMarginSlots));
+            while (need != 0ull) {
+                const int L = __ffsll(static_cast<long long>(need)) - 1;
+                need &= need - 1ull;
+                const long xb = (long)(L * kSelPer + r) * kBlockElems;
+                RawBlock<E> raw;
+                issue_block_any<E>(d, xb, V, true, raw);
+                double w = 0.0;
+#pragma unroll
+                for (int u = 0; u < kSubBlocks; ++u) {
+                    float l[kSubTokens], q[kSubTokens];
+                    decode_sub<E>(raw.s[u], true, l, q);
+#pragma unroll
+                    for (int k = 0; k < kSubTokens; ++k) {
+                        w += fmax(draw_e<E>(d, l[k], tab) * invZ64 - static_cast<double>(q[k]), 0.0);
+                        if (k & 1) __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+                w = wave_sum(w);
+                if (lane == L) wt[r] = w;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < kSelPer; ++r) wt[r] = se_t[r];
+    }
+    // ---- block scan
+    double own = 0.0;
+#pragma unroll
+    for (int r = 0; r < kSelPer; ++r) own += wt[r];
+    double incl = wave_inclusive_scan(own);
+    double Stot = rdlane(incl, 63);
+    if (residual && !(Stot > 0.0)) {
+        // residual lost to rounding: draw from p itself
+        kind = kDrawDegenerate;
+        own = 0.0;
+#pragma unroll
+        for (int r = 0; r < kSelPer; ++r) { wt[r] = se_t[r]; own += wt[r]; }
+        incl = wave_inclusive_scan(own);
+        Stot = rdlane(incl, 63);
+    }
+    const double tsel = static_cast<double>(d.v) * Stot;
+    // this lane's first block whose inclusive sum passes tsel, and its last block
+    // of positive weight, each with the sum before it
+    int cand = -1, lastpos = -1;
+    double cand_before = 0.0, last_before = 0.0;
+    {
+        double run = incl - own;
+#pragma unroll
+        for (int r = 0; r < kSelPer; ++r) {
+            const int j = lane * kSelPer + r;
+            const double before = run;
+            run += wt[r];
+            if (j < NB && wt[r] > 0.0) { lastpos = j; last_before = before; }
+            if (j < NB && cand < 0 && run > tsel) { cand = j; cand_before = before; }
+        }
+    }
+    const unsigned long long cm = __ballot(cand >= 0), lm = __ballot(lastpos >= 0);
+    int jsel;
+    double base;
+    bool block_fallback = false;
+    if (cm != 0ull) {
+        const int L = __ffsll(static_cast<long long>(cm)) - 1;
+        jsel = rdlane(cand, L);
+        base = rdlane(cand_before, L);
+    } else if (lm != 0ull) {            // rounding left no block above v * S: the last positive one
+        const int L = 63 - __clzll(static_cast<long long>(lm));
+        jsel = rdlane(lastpos, L);
+        base = rdlane(last_before, L);
+        block_fallback = true;
+    } else {                            // no positive finite weight (non-finite logits)
+        jsel = 0;
+        base = 0.0;
+        block_fallback = true;
+        if (lane == 0) flag_error(err, err_host, kErrNonFinite);
+    }
+    SelBlock sb;
+    sb.jsel = jsel;
+    sb.base = base;
+    sb.tsel = tsel;
+    sb.invZ64 = invZ64;
+    sb.res_w = (kind == kDrawResidual);
+    sb.with_q = sb.res_w && !d.qlist;
+    sb.fallback = block_fallback;
+    sb.qid = qid;
+    sb.qq = qq;
+    sb.qmask = sb.res_w ? __ballot(qvalid && qid / kBlockElems == jsel) : 0ull;
+    return sb;
+}
+
+// Token weights of one lane's 8 tokens of sub-block u of the selected block, and
+// their sum (tokens past the row's end weigh nothing).
+template <typename E>
+__device__ __forceinline__ double sub_weights(const DrawRow<E>& d, const RawSub<E>& raw, long x0, int V,
+                                              const SelBlock& sb, const double* tab, double* w) {
+    float l[kSubTokens], q[kSubTokens];
+    decode_sub<E>(raw, sb.with_q, l, q);
+#pragma unroll
+    for (int k = 0; k < kSubTokens; ++k) {
+        const double e = draw_e<E>(d, l[k], tab);
+        w[k] = sb.res_w ? fmax(e * sb.invZ64 - static_cast<double>(q[k]), 0.0) : e;
+        if (x0 + k >= V) w[k] = 0.0;
+        if (k & 1) __builtin_amdgcn_sched_barrier(0);
+    }
+    // listed q entries among this lane's tokens (q was taken as 0 above)
+    unsigned long long m = sb.qmask;
+    while (m != 0ull) {
+        const int s = __ffsll(static_cast<long long>(m)) - 1;
+        m &= m - 1ull;
+        const int xi = rdlane(sb.qid, s);
+        const double qv = static_cast<double>(rdlane(sb.qq, s));
+#pragma unroll
+        for (int k = 0; k < kSubTokens; ++k)
+            if (x0 + k == xi) w[k] = fmax(w[k] - qv, 0.0);
+    }
+    double tsum = 0.0;
+#pragma unroll
+    for (int k = 0; k < kSubTokens; ++k) tsum += w[k];
+    return tsum;
+}
+
+// Walks one lane's weights in token order from run (the sum before its first
+// token): the first token whose running sum passes tsel, and the last token of
+// positive weight.
+__device__ __forceinline__ void sub_find(const double* w, long x0, double run, const SelBlock& sb, int& ycand,
+                                         int& ylast) {
+#pragma unroll
+    for (int k = 0; k < kSubTokens; ++k) {
+        run += w[k];
+        const int x = static_cast<int>(x0) + k;
+        if (w[k] > 0.0) ylast = x;
+        if (!sb.fallback && ycand == 0x7fffffff && run > sb.tsel) ycand = x;
+    }
+}
+
+// The token, given the first crossing and the last positive token found.
+__device__ __forceinline__ int select_token(int ycand, int ylast, int V, int jsel) {
+    int y = ycand;
+    if (y == 0x7fffffff) y = ylast;
+    if (y < 0) y = min(V - 1, jsel * kBlockElems + kBlockElems - 1);
+    return y;
+}
+
+// The same select by a whole workgroup: every wave makes the (identical) block
+// choice, then wave u scans sub-block u, so the block is loaded in one round;
+// the sub-block sums and each wave's finds meet in LDS.  Every thread returns
+// the token.  Uniform call.
+static_assert(kSubBlocks == kWaves, "one sub-block per wave");
+struct SelShared {
+    double tot[kWaves];
+    int yc[kWaves], yl[kWaves];
+};
+
+template <typename E>
+__device__ __forceinline__ int draw_select_wg(const DrawRow<E>& d, int V, int NB, const BlockRec* recs,
+                                              const double* tab, uint32_t* err, uint32_t* err_host,
+                                              SelShared& ss) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const SelBlock sb = select_block<E>(d, V, NB, recs, tab, err, err_host);
+    const long x0 = sub_first((long)sb.jsel * kBlockElems, wv);
+    RawSub<E> raw;
+    issue_sub_any<E>(d, x0, V, sb.with_q, raw);
+    double w[kSubTokens];
+    const double tsum = sub_weights<E>(d, raw, x0, V, sb, tab, w);
+    const double ti = wave_inclusive_scan(tsum);
+    if (lane == 63) ss.tot[wv] = ti;
+    __syncthreads();
+    // the sums before this sub-block, added in sub-block order
+    double run_base = sb.base;
+#pragma unroll
+    for (int u = 0; u < kWaves; ++u) run_base += (u < wv) ? ss.tot[u] : 0.0;
+    int ycand = 0x7fffffff, ylast = -1;
+    sub_find(w, x0, run_base + (ti - tsum), sb, ycand, ylast);
+    ycand = wave_min_int(ycand);
+    ylast = wave_max_int(ylast);
+    if (lane == 0) { ss.yc[wv] = ycand; ss.yl[wv] = ylast; }
+    __syncthreads();
+    int yc = ss.yc[0], yl = ss.yl[0];
+#pragma unroll
+    for (int u = 1; u < kWaves; ++u) { yc = min(yc, ss.yc[u]); yl = max(yl, ss.yl[u]); }
+    return select_token(yc, yl, V, sb.jsel);
 }
 
 template <typename E>
@@ -1168,410 +1578,58 @@ __device__ __forceinline__ void init_draw_row(DrawRow<E>& d, const Params& P, in
     }
 }
 
-// ----------------------------------------------------------------- select
-// The select for one request, once all its range records are stored, by one
-// wave (every lane returns the token).
-//
-// Range choice: rebuilds the exact fp64 normaliser Z64 and every range's
-// weight (e / Z64 - q summed over the clearly positive tokens plus the inline
-// marginal ones; ranges with more marginal tokens than slots, or every range
-// when the fp32-pass normaliser is off by more than half the margin, are
-// re-evaluated from their tokens) and finds the range holding v * S by a scan
-// over ranges (kSelPer consecutive ranges per lane).  Then the chosen range is
-// loaded in one round and scanned token by token in token order.
-struct SelRange {
-    int jsel;            // selected range
-    double base;         // weight of the ranges before it
-    double tsel;         // v * S
-    double invZ64;
-    bool res_w;          // token weights are residuals (else e)
-    bool with_q;         // residual weights read a dense q row (else q = 0 off the list)
-    bool fallback;       // rounding left no crossing: take the range's last positive token
-    // listed q (sparse or point mass): lane s holds entry s; qmask: the entries
-    // inside the selected range (wave-uniform)
-    int qid;
-    float qq;
-    unsigned long long qmask;
+static_assert(kExp2TableSize % kThreads == 0, "whole table entries per draw thread");
+constexpr int kTabPerThread = kExp2TableSize / kThreads;
+struct DrawShared {
+    double tab[kExp2TableSize];
+    SelShared sel;
+    int flag;
 };
 
-// Range of token x (the inverse of range_start).
-__device__ __forceinline__ int range_of(int x, int nr, int V) {
-    int j = static_cast<int>(((long)(x >> 3) * nr) / ((V + 7) >> 3));
-    while (j + 1 < nr && range_start(j + 1, nr, V) <= x) ++j;
-    while (j > 0 && range_start(j, nr, V) > x) --j;
-    return j;
-}
-
-// The weight of range [x0, x1) re-evaluated token by token with the exact
-// normaliser.  Out of line, with the row's fields passed by value (a reference
-// to the caller's DrawRow would put that struct on the stack).
-template <typename E>
-__device__ __noinline__ double range_weight_exact(const typename E::T* lrow, const float* qrow, double c2, double mc2,
-                                                  bool lalign, bool qalign, int x0, int x1, double invZ64,
-                                                  const double* tab) {
-    DrawRow<E> d;
-    d.lrow = lrow;
-    d.qrow = qrow;
-    d.c2 = c2;
-    d.mc2 = mc2;
-    d.lalign = lalign;
-    d.qalign = qalign;
-    const int ns = (x1 - x0 + kSubElems - 1) / kSubElems;
-    double w = 0.0;
-    for (int s = 0; s < ns; ++s) {
-        RawSub<E> raw;
-        issue_sub_any<E>(d, sub_first(x0, s), x1, true, raw);
-        float l[kSubTokens], q[kSubTokens];
-        decode_sub<E>(raw, true, l, q);
-#pragma unroll
-        for (int k = 0; k < kSubTokens; ++k) w += fmax(draw_e<E>(d, l[k], tab) * invZ64 - static_cast<double>(q[k]), 0.0);
-    }
-    return wave_sum(w);
-}
-
-template <typename E>
-__device__ __forceinline__ SelRange select_range(const DrawRow<E>& d, int V, int NR, const RangeRec* recs,
-                                                 const double* tab, uint32_t* err, uint32_t* err_host) {
-    const int lane = threadIdx.x & 63;
-    const bool residual = (d.kind == kDrawResidual);
-    // every field of this lane's records in one round of loads
-    double se_t[kSelPer], ea_t[kSelPer], qa_t[kSelPer];
-    int nm_t[kSelPer];
-#pragma unroll
-    for (int r = 0; r < kSelPer; ++r) {
-        const int j = lane * kSelPer + r;
-        const bool in = j < NR;
-        const RangeRec* rc = &recs[in ? j : 0];
-        se_t[r] = in ? ld_coherent(&rc->se) : 0.0;
-        ea_t[r] = qa_t[r] = 0.0;
-        nm_t[r] = 0;
-        if (residual && !d.qlist && in) {
-            ea_t[r] = ld_coherent(&rc->ea);
-            qa_t[r] = ld_coherent(&rc->qa);
-            nm_t[r] = ld_coherent(&rc->nm);
-        }
-    }
-    double zpart = 0.0;
-#pragma unroll
-    for (int r = 0; r < kSelPer; ++r) zpart += se_t[r];
-    const double Z64 = wave_sum(zpart);
-    const double invZ64 = 1.0 / Z64;
-    int kind = d.kind;
-    double wt[kSelPer];
-    int qid = -1;
-    float qq = 0.0f;
-    bool qvalid = false;
-    if (residual && d.qlist) {
-        // q is zero except at the listed tokens: range weights are the ranges' p
-        // mass less min(p, q) of the listed tokens they hold (p - (p - q)_+)
-        if (lane < d.nq) {
-            qid = d.sid[lane];
-            qq = d.sq ? d.sq[lane] : 1.0f;
-        }
-        qvalid = qid >= 0 && qid < V;
-        if (lane < d.nq && !qvalid && qid != -1) flag_error(err, err_host, kErrTopk);
-        double cs = 0.0;
-        if (qvalid) cs = fmin(draw_e<E>(d, E::load1(d.lrow, qid), tab) * invZ64, static_cast<double>(qq));
-        const int qr = qvalid ? range_of(qid, NR, V) : -1;
-#pragma unroll
-        for (int r = 0; r < kSelPer; ++r) wt[r] = se_t[r] * invZ64;
-        for (int s = 0; s < d.nq; ++s) {
-            const int js = rdlane(qr, s);
-            if (js < 0) continue;
-            const double c = rdlane(cs, s);
-#pragma unroll
-            for (int r = 0; r < kSelPer; ++r)
-                if (lane * kSelPer + r == js) wt[r] -= c;
-        }
-    } else if (residual) {
-        const bool full = !(fabs(Z64 - d.z32) <= 0.5 * kSignMargin * Z64);
-#pragma unroll
-        for (int r = 0; r < kSelPer; ++r) wt[r] = ea_t[r] * invZ64 - qa_t[r];
-        // ranges with inline marginal tokens (a slot is only meaningful when the
-        // range recorded it): one more round of loads, only when there are any
-        bool any_slots = false;
-#pragma unroll
-        for (int r = 0; r < kSelPer; ++r) any_slots |= (nm_t[r] > 0 && nm_t[r] <= kMarginSlots);
-        if (__ballot(any_slots) != 0ull) {
-#pragma unroll
-            for (int r = 0; r < kSelPer; ++r) {
-                const int j = lane * kSelPer + r;
-                if (j < NR && nm_t[r] > 0 && nm_t[r] <= kMarginSlots) {
-                    const RangeRec* rc = &recs[j];
-                    wt[r] += fmax(ld_coherent(&rc->me[0]) * invZ64 - static_cast<double>(ld_coherent(&rc->mq[0])), 0.0);
-                    if (nm_t[r] > 1)
-                        wt[r] += fmax(ld_coherent(&rc->me[1]) * invZ64 - static_cast<double>(ld_coherent(&rc->mq[1])), 0.0);
-                }
-            }
-        }
-        // rare: ranges re-evaluated from their tokens, one at a time by the wave
-#pragma unroll
-        for (int r = 0; r < kSelPer; ++r) {
-            const int j = lane * kSelPer + r;
-            unsigned long long need = __ballot(j < NR && (full || nm_t[r] > kMarginSlots));
-            while (need != 0ull) {
-                const int L = __ffsll(static_cast<long long>(need)) - 1;
-                need &= need - 1ull;
-                const int jr = L * kSelPer + r;
-                const double w = range_weight_exact<E>(d.lrow, d.qrow, d.c2, d.mc2, d.lalign, d.qalign,
-                                                       range_start(jr, NR, V), range_start(jr + 1, NR, V), invZ64, tab);
-                if (lane == L) wt[r] = w;
-            }
-        }
-    } else {
-#pragma unroll
-        for (int r = 0; r < kSelPer; ++r) wt[r] = se_t[r];
-    }
-    // ---- range scan
-    double own = 0.0;
-#pragma unroll
-    for (int r = 0; r < kSelPer; ++r) own += wt[r];
-    double incl = wave_inclusive_scan(own);
-    double Stot = rdlane(incl, 63);
-    if (residual && !(Stot > 0.0)) {
-        // residual lost to rounding: draw from p itself
-        kind = kDrawDegenerate;
-        own = 0.0;
-#pragma unroll
-        for (int r = 0; r < kSelPer; ++r) { wt[r] = se_t[r]; own += wt[r]; }
-        incl = wave_inclusive_scan(own);
-        Stot = rdlane(incl, 63);
-    }
-    const double tsel = static_cast<double>(d.v) * Stot;
-    // this lane's first range whose inclusive sum passes tsel, and its last range
-    // of positive weight, each with the sum before it
-    int cand = -1, lastpos = -1;
-    double cand_before = 0.0, last_before = 0.0;
-    {
-        double run = incl - own;
-#pragma unroll
-        for (int r = 0; r < kSelPer; ++r) {
-            const int j = lane * kSelPer + r;
-            const double before = run;
-            run += wt[r];
-            if (j < NR && wt[r] > 0.0) { lastpos = j; last_before = before; }
-            if (j < NR && cand < 0 && run > tsel) { cand = j; cand_before = before; }
-        }
-    }
-    const unsigned long long cm = __ballot(cand >= 0), lm = __ballot(lastpos >= 0);
-    int jsel;
-    double base;
-    bool fb = false;
-    if (cm != 0ull) {
-        const int L = __ffsll(static_cast<long long>(cm)) - 1;
-        jsel = rdlane(cand, L);
-        base = rdlane(cand_before, L);
-    } else if (lm != 0ull) {            // rounding left no range above v * S: the last positive one
-        const int L = 63 - __clzll(static_cast<long long>(lm));
-        jsel = rdlane(lastpos, L);
-        base = rdlane(last_before, L);
-        fb = true;
-    } else {                            // no positive finite weight (excluded by the resolve's checks)
-        jsel = 0;
-        base = 0.0;
-        fb = true;
-        if (lane == 0) flag_error(err, err_host, kErrNonFinite);
-    }
-    SelRange sr;
-    sr.jsel = jsel;
-    sr.base = base;
-    sr.tsel = tsel;
-    sr.invZ64 = invZ64;
-    sr.res_w = (kind == kDrawResidual);
-    sr.with_q = sr.res_w && !d.qlist;
-    sr.fallback = fb;
-    sr.qid = qid;
-    sr.qq = qq;
-    const int x0 = range_start(jsel, NR, V), x1 = range_start(jsel + 1, NR, V);
-    sr.qmask = sr.res_w ? __ballot(qvalid && qid >= x0 && qid < x1) : 0ull;
-    return sr;
-}
-
-// Token weights of one lane's 8 tokens at x (sub-block of the selected range),
-// and their sum (tokens at or past x1 weigh nothing).
-template <typename E>
-__device__ __forceinline__ double sub_weights(const DrawRow<E>& d, const RawSub<E>& raw, int x, int x1,
-                                              const SelRange& sr, const double* tab, double* w) {
-    float l[kSubTokens], q[kSubTokens];
-    decode_sub<E>(raw, sr.with_q, l, q);
-#pragma unroll
-    for (int k = 0; k < kSubTokens; ++k) {
-        const double e = draw_e<E>(d, l[k], tab);
-        w[k] = sr.res_w ? fmax(e * sr.invZ64 - static_cast<double>(q[k]), 0.0) : e;
-        if (x + k >= x1) w[k] = 0.0;
-        if (k & 1) __builtin_amdgcn_sched_barrier(0);
-    }
-    // listed q entries among this lane's tokens (q was taken as 0 above)
-    unsigned long long m = sr.qmask;
-    while (m != 0ull) {
-        const int s = __ffsll(static_cast<long long>(m)) - 1;
-        m &= m - 1ull;
-        const int xi = rdlane(sr.qid, s);
-        const double qv = static_cast<double>(rdlane(sr.qq, s));
-#pragma unroll
-        for (int k = 0; k < kSubTokens; ++k)
-            if (x + k == xi) w[k] = fmax(w[k] - qv, 0.0);
-    }
-    double tsum = 0.0;
-#pragma unroll
-    for (int k = 0; k < kSubTokens; ++k) tsum += w[k];
-    return tsum;
-}
-
-// Walks one lane's weights in token order from run (the sum before its first
-// token): the first token whose running sum passes tsel, and the last token of
-// positive weight.
-__device__ __forceinline__ void sub_find(const double* w, int x, double run, const SelRange& sr, int& ycand,
-                                         int& ylast) {
-#pragma unroll
-    for (int k = 0; k < kSubTokens; ++k) {
-        run += w[k];
-        if (w[k] > 0.0) ylast = x + k;
-        if (!sr.fallback && ycand == 0x7fffffff && run > sr.tsel) ycand = x + k;
-    }
-}
-
-// The select by the whole workgroup: every wave makes the (identical) range
-// choice, then wave u scans sub-blocks 2u and 2u + 1 of the chosen range (all of
-// its loads in one round; sub-blocks past the range weigh nothing), and the
-// waves' sums and finds meet in LDS.  Every thread returns the token.  Uniform
-// call.
-static_assert(kRangeSubs == 2 * kWaves, "two sub-blocks of the chosen range per wave");
-struct SelShared {
-    double tot[kWaves];
-    int yc[kWaves], yl[kWaves];
-};
-
-template <typename E>
-__device__ __forceinline__ int select_wg(const DrawRow<E>& d, int V, int NR, const RangeRec* recs,
-                                         const double* tab, uint32_t* err, uint32_t* err_host, SelShared& ss) {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const SelRange sr = select_range<E>(d, V, NR, recs, tab, err, err_host);
-    const int x0 = range_start(sr.jsel, NR, V), x1 = range_start(sr.jsel + 1, NR, V);
-    const int xa = sub_first(x0, 2 * wv), xb = sub_first(x0, 2 * wv + 1);
-    RawSub<E> ra, rb;
-    if (d.lalign && (!sr.with_q || d.qalign) && (x1 & 7) == 0) {
-        if (sr.with_q) {
-            issue_sub_fast<E, true>(d, xa, x0, x1, ra);
-            issue_sub_fast<E, true>(d, xb, x0, x1, rb);
-        } else {
-            issue_sub_fast<E, false>(d, xa, x0, x1, ra);
-            issue_sub_fast<E, false>(d, xb, x0, x1, rb);
-#pragma unroll
-            for (int h = 0; h < kSubTokens / 4; ++h) ra.q[h] = rb.q[h] = v4u(0u);
-        }
-    } else {
-        issue_sub_any<E>(d, xa, x1, sr.with_q, ra);
-        issue_sub_any<E>(d, xb, x1, sr.with_q, rb);
-    }
-    double wa[kSubTokens], wb[kSubTokens];
-    const double ta = sub_weights<E>(d, ra, xa, x1, sr, tab, wa);
-    const double tb = sub_weights<E>(d, rb, xb, x1, sr, tab, wb);
-    const double ia = wave_inclusive_scan(ta);
-    const double ib = wave_inclusive_scan(tb);
-    const double tot_a = rdlane(ia, 63);
-    if (lane == 0) ss.tot[wv] = tot_a + rdlane(ib, 63);
-    __syncthreads();
-    // the sums before this wave's first sub-block, added in sub-block order
-    double run_base = sr.base;
-#pragma unroll
-    for (int u = 0; u < kWaves; ++u) run_base += (u < wv) ? ss.tot[u] : 0.0;
-    int ycand = 0x7fffffff, ylast = -1;
-    sub_find(wa, xa, run_base + (ia - ta), sr, ycand, ylast);
-    sub_find(wb, xb, run_base + tot_a + (ib - tb), sr, ycand, ylast);
-    ycand = wave_min_int(ycand);
-    ylast = wave_max_int(ylast);
-    if (lane == 0) { ss.yc[wv] = ycand; ss.yl[wv] = ylast; }
-    __syncthreads();
-    int yc = ss.yc[0], yl = ss.yl[0];
-#pragma unroll
-    for (int u = 1; u < kWaves; ++u) { yc = min(yc, ss.yc[u]); yl = max(yl, ss.yl[u]); }
-    int y = yc;
-    if (y == 0x7fffffff) y = yl;
-    if (y < 0) y = min(V - 1, x0);
-    return y;
-}
-
-// ----------------------------------------------------------------- resolve by one wave
-// After the stream-only rows kernel, a wave rebuilds request b's row statistics
-// from the stored pieces, runs the accept tests and finds the first rejection
-// itself (a few hundred bytes of loads and a handful of fp64 exponentials:
-// cheaper than a hand-off between waves).  Lane i owns row base + i of the
-// request (rows in chunks of 64); it loads the row's pieces, its draft's id,
-// logit, q and uniform in one round, merges the pieces and runs the accept test.
-// The `writer` wave (the one holding the request's range 0) stores the
-// outputs, counters and diagnostics, except the drawn token, which the select
-// writes.
+// ----------------------------------------------------------------- resolve in the draw kernel
+// After the stream-only rows kernel, every draw workgroup of request b rebuilds
+// the request's row statistics from the stored pieces, runs the accept tests
+// and finds the first rejection itself (a few hundred bytes of loads and a
+// handful of fp64 exponentials: cheaper than a hand-off between workgroups);
+// the request's workgroup 0 writes the outputs, except the drawn token, which
+// the select writes.
 constexpr int kMaxReqRows = 129;          // gamma_b + 1 rows of one request at most
-constexpr int kResolveChunk = 8;          // pieces a lane loads in one round
+constexpr int kResolveChunk = 8;          // pieces a thread loads in one round
 
-struct WaveTask {
-    int kind;            // kDraw*: kDrawNone for greedy requests and contract violations
-    int row, drow, pos;  // draw row (target), its draft row (residual), output column k
-    float v, m;          // uniform of the draw, the draw row's max logit
-    double z32;          // the draw row's normaliser
-    float T;             // the request's temperature
+struct ResolveShared {
+    float rm[kMaxReqRows];       // row max (sampled) / argmax value (greedy)
+    double rz[kMaxReqRows];      // row normaliser
+    int rej[kMaxReqRows];        // draft i rejected
+    uint32_t bad[kMaxReqRows];   // contract violations found on row i (kErr* bits)
 };
-
-__device__ __forceinline__ int op_ori(int a, int b) { return a | b; }
-__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
-    int x = static_cast<int>(v);
-    SV_WAVE_REDUCE(int, dpp_i, op_ori, x);
-    return static_cast<uint32_t>(x);
-}
 
 // Outputs of a request that breaks the device-side contract: every token and
-// num_accepted are -1 (written by the request's writer wave only).
+// num_accepted are -1 (written by the request's writer workgroup only).
 __device__ __forceinline__ void write_violation(const Params& P, int b) {
-    const int lane = threadIdx.x & 63;
-    for (int j = lane; j <= P.gamma; j += 64) P.out_tokens[(size_t)b * (P.gamma + 1) + j] = -1;
-    if (lane == 0) P.out_num[b] = -1;
+    const int tid = threadIdx.x;
+    for (int j = tid; j <= P.gamma; j += kThreads) P.out_tokens[(size_t)b * (P.gamma + 1) + j] = -1;
+    if (tid == 0) P.out_num[b] = -1;
 }
 
-// What lane i loads for row base + i of a request in the resolve: every address
-// valid whatever the lane (rows past the request read its last row, columns
-// past the uniforms' row its last column), so that no branch holds a load and
-// one wait covers them all.
-struct ResolveLoads {
-    int np;                      // pieces of the row
-    int xs;                      // drafted token as the rows kernel stored it (-2: sparse q broken)
-    float lx, qx, u;             // its logit, its q, its uniform
-    int xid;                     // draft id
-    float mm[kResolveChunk];     // pieces: max / argmax value
-    int gg[kResolveChunk];       // argmax
-    double zz[kResolveChunk];    // sum
-};
-
-__device__ __forceinline__ void resolve_loads(const Params& P, const float* ub, int t0, int o0, int gb, int base,
-                                              ResolveLoads& L) {
-    const int i = base + (threadIdx.x & 63);
-    const int t = t0 + min(i, gb);
-    L.u = ub[min(i, P.gamma + 1)];
-    const RowStat* rp = &P.rows[t];
-    L.xs = rp->x;
-    L.lx = rp->lx;
-    L.qx = rp->qx;
-    L.np = rp->np;
-    L.xid = -1;
-    if (gb > 0) L.xid = P.ids[o0 + min(i, gb - 1)];
-    const Piece* pp = &P.parts[(size_t)t * kMaxPieces];
-#pragma unroll
-    for (int q = 0; q < kResolveChunk; ++q) {
-        L.mm[q] = pp[q].m;
-        L.gg[q] = pp[q].g;
-        L.zz[q] = pp[q].z;
-    }
-}
-
+// Uniform call.  Returns request b's draw task (kDrawNone: greedy, nothing to
+// draw, or a request that breaks the device-side contract); `writer`
+// workgroups store the outputs, counters and diagnostics.  Thread i owns row i
+// of the request: it loads the row's pieces and its draft's id, logit, q and
+// uniform in one round, merges the pieces and runs the accept test, so that a
+// single barrier publishes the rows' results.  A request is a contract
+// violation when its offsets are inconsistent, a draft id lies outside
+// [0, vocab), its sparse q breaks the entry rules, or one of its sampled rows
+// has no positive finite normaliser (no finite logit, or NaN logits); its
+// outputs are then all -1, the bits are flagged, and it is not counted.
 template <typename E>
-__device__ WaveTask resolve_wave(const Params& P, int b, bool writer, const double* tab) {
-    const int lane = threadIdx.x & 63;
+__device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool writer, float T, ResolveShared& rs,
+                                                   const double* tab) {
+    const int tid = threadIdx.x;
     const int G = P.gamma;
-    const int V = P.vocab;
-    WaveTask tk;
+    DrawTask tk;
     tk.kind = kDrawNone;
     tk.row = tk.drow = tk.pos = 0;
-    tk.v = tk.m = tk.T = 0.0f;
+    tk.v = tk.m = 0.0f;
     tk.z32 = 0.0;
     int o0, o1;
     if (P.offsets) {
@@ -1581,92 +1639,102 @@ __device__ WaveTask resolve_wave(const Params& P, int b, bool writer, const doub
         o0 = b * G;
         o1 = o0 + G;
     }
-    const float* ub = P.uniforms + (size_t)b * (G + 2);
     const int gb = o1 - o0;
     if (!(o0 >= 0 && o1 <= P.total_draft && gb >= 0 && gb <= G && gb < kMaxReqRows)) {
         if (writer) {
             write_violation(P, b);
-            if (lane == 0) flag_error(P.err, P.err_host, kErrOffsets);
+            if (tid == 0) flag_error(P.err, P.err_host, kErrOffsets);
         }
         return tk;
     }
     const int t0 = o0 + b;
-    // the first chunk's loads go out before the temperature's: what is computed
-    // from T would otherwise be hoisted ahead of them, with a wait for T first
-    ResolveLoads L;
-    resolve_loads(P, ub, t0, o0, gb, 0, L);
-    asm volatile("" ::: "memory");
-    const float T = P.temperature[b];
-    const float v_res = ub[G];
-    const float v_bonus = ub[G + 1];
-    const Piece* parts = P.parts;
-    int k = gb;
-    bool found = false;
-    uint32_t badq = 0u;
-    float Mk = 0.0f;
-    double Zk = 0.0;
-    int gk = -1;
-    for (int base = 0; base <= gb; base += 64) {
-        const int i = base + lane;
-        const bool owner = i <= gb;
-        const bool draft = i < gb;
-        const int t = t0 + min(i, gb);
-        if (base > 0) resolve_loads(P, ub, t0, o0, gb, base, L);
-        const int xs = L.xs;
-        const float lx = L.lx, qx = L.qx, u = L.u;
-        const int xid = L.xid;
-        const Piece* pp = &parts[(size_t)t * kMaxPieces];
-        float mm[kResolveChunk];
-        int gg[kResolveChunk];
-        double zz[kResolveChunk];
+    const bool greedy = !(T > 0.0f);
+    // 1024 times the pieces' scale log2(e) / T as the rows kernel rounded it
+    // (exact), and 1024 log2(e) / T for the accept ratio: exponentials by the
+    // same table-based exp2 as the draw weights
+    const double cpz = greedy ? 0.0 : kExp2Scale * static_cast<double>(static_cast<float>(kLog2e / static_cast<double>(T)));
+    const double c2 = greedy ? 0.0 : kExp2Scale * (kLog2e / static_cast<double>(T));
+    const float v_res = P.uniforms[(size_t)b * (G + 2) + G];
+    const float v_bonus = P.uniforms[(size_t)b * (G + 2) + G + 1];
+    const bool owner = tid <= gb;
+    float M = -INFINITY;          // row max, or the argmax value
+    int g = 0x7fffffff;           // argmax
+    double Z = 0.0;
+    int xid = -1;
+    bool rej = false;
+    double r = 0.0;
+    int xs = -1, np = 0;
+    float lx = 0.0f, qx = 0.0f, u = 0.0f;
+    const Piece* pp = nullptr;
+    float mm[kResolveChunk];
+    int gg[kResolveChunk];
+    double zz[kResolveChunk];
+    if (owner) {
+        const int t = t0 + tid;
+        if (P.split_pieces > 0) {
+            np = P.split_pieces;
+        } else {
+            const long rsv = (long)t * P.flat_vpr;
+            np = range_owner(rsv + P.flat_vpr - 1, P.flat_nv, P.rows_grid) - range_owner(rsv, P.flat_nv, P.rows_grid) + 1;
+        }
+        if (tid < gb) {
+            xid = P.ids[o0 + tid];
+            if (!greedy) {
+                // stored by the rows kernel: the launch boundary orders those
+                // stores before these plain loads
+                const RowStat* rp = &P.rows[t];
+                xs = rp->x;
+                lx = rp->lx;
+                qx = rp->qx;
+                u = P.uniforms[(size_t)b * (G + 2) + tid];
+            }
+        }
+        pp = &P.parts[(size_t)t * kMaxPieces];
 #pragma unroll
         for (int q = 0; q < kResolveChunk; ++q) {
-            mm[q] = L.mm[q];
-            gg[q] = L.gg[q];
-            zz[q] = L.zz[q];
+            const bool in = q < np;
+            mm[q] = in ? pp[q].m : -INFINITY;
+            gg[q] = in ? pp[q].g : 0x7fffffff;
+            zz[q] = in ? pp[q].z : 0.0;
         }
-        // ---- merge the row's pieces
-        const bool greedy = !(T > 0.0f);
-        // 1024 times the pieces' scale log2(e) / T as the rows kernel rounded it
-        // (exact), and 1024 log2(e) / T for the accept ratio: exponentials by the
-        // same table-based exp2 as the draw weights
-        const double cpz = greedy ? 0.0 : kExp2Scale * static_cast<double>(static_cast<float>(kLog2e / static_cast<double>(T)));
-        const double c2 = greedy ? 0.0 : kExp2Scale * (kLog2e / static_cast<double>(T));
-        const int np = min(max(L.np, 1), kMaxPieces);
-        float M = -INFINITY;          // row max, or the argmax value
-        int g = 0x7fffffff;           // argmax
-        double Z = 0.0;
-        if (!greedy) {
-            // the row max first, then the pieces' sums rescaled to it in piece order
+    }
+    // publishes the exponential table (stored to LDS by the caller); the loads
+    // above are complete after it
+    __syncthreads();
+    if (owner) {
+        for (int p0 = 0; p0 < np; p0 += kResolveChunk) {
+            if (p0 > 0) {
 #pragma unroll
-            for (int q = 0; q < kResolveChunk; ++q)
-                if (q < np) M = fmaxf(M, mm[q]);
-            for (int q = kResolveChunk; q < np; ++q) M = fmaxf(M, pp[q].m);
-            if (M > -INFINITY) {
-#pragma unroll
-                for (int q = 0; q < kResolveChunk; ++q)
-                    if (q < np && mm[q] > -INFINITY)
-                        Z += zz[q] * exp2_tab((static_cast<double>(mm[q]) - static_cast<double>(M)) * cpz, tab);
-                for (int q = kResolveChunk; q < np; ++q) {
-                    const float mq = pp[q].m;
-                    if (mq > -INFINITY)
-                        Z += pp[q].z * exp2_tab((static_cast<double>(mq) - static_cast<double>(M)) * cpz, tab);
+                for (int q = 0; q < kResolveChunk; ++q) {
+                    const bool in = p0 + q < np;
+                    mm[q] = in ? pp[p0 + q].m : -INFINITY;
+                    gg[q] = in ? pp[p0 + q].g : 0x7fffffff;
+                    zz[q] = in ? pp[p0 + q].z : 0.0;
                 }
             }
-        } else {
+            if (!greedy) {
+                // the pieces' sums rescaled to the row max, in piece order
+                float Mc = M;
 #pragma unroll
-            for (int q = 0; q < kResolveChunk; ++q)
-                if (q < np) argmax_merge(M, g, mm[q], gg[q]);
-            for (int q = kResolveChunk; q < np; ++q) argmax_merge(M, g, pp[q].m, pp[q].g);
+                for (int q = 0; q < kResolveChunk; ++q) Mc = fmaxf(Mc, mm[q]);
+                if (Mc > M && M > -INFINITY)
+                    Z *= exp2_tab((static_cast<double>(M) - static_cast<double>(Mc)) * cpz, tab);
+                M = Mc;
+#pragma unroll
+                for (int q = 0; q < kResolveChunk; ++q)
+                    if (mm[q] > -INFINITY)
+                        Z += zz[q] * exp2_tab((static_cast<double>(mm[q]) - static_cast<double>(M)) * cpz, tab);
+            } else {
+#pragma unroll
+                for (int q = 0; q < kResolveChunk; ++q) argmax_merge(M, g, mm[q], gg[q]);
+            }
         }
-        // ---- accept test (page section 5.2: q floored at 1e-10, strict
-        // comparison); p(x) by the draw weights' own expression
+        // accept test (page section 5.2: q floored at 1e-10, strict comparison);
+        // p(x) by the draw weights' own expression
         uint32_t bad = 0u;
-        bool rej = false;
-        double r = 0.0;
-        if (draft) {
+        if (tid < gb) {
             bool acc;
-            if (xid < 0 || xid >= V) bad |= kErrDraftId;
+            if (xid < 0 || xid >= P.vocab) bad |= kErrDraftId;
             if (greedy) {
                 acc = (xid == g);
             } else {
@@ -1677,166 +1745,121 @@ __device__ WaveTask resolve_wave(const Params& P, int b, bool writer, const doub
             }
             rej = !acc;
         }
-        if (owner && !greedy && !(Z > 0.0 && Z < INFINITY && fabsf(M) < INFINITY)) bad |= kErrNonFinite;
-        badq |= wave_or(bad);
-        if (writer && owner) {
-            if (P.diag_m) P.diag_m[t0 + i] = M;
-            if (P.diag_z) P.diag_z[t0 + i] = greedy ? 0.0 : Z;
-            if (draft && P.diag_r) P.diag_r[o0 + i] = greedy ? __uint_as_float(0x7fc00000u) : static_cast<float>(r);
-        }
-        // the first rejected draft, and the draw row's statistics once it lies in
-        // this chunk (every lane finds the same)
-        const unsigned long long rm = __ballot(draft && rej);
-        const bool found_before = found;
-        if (!found && rm != 0ull) {
-            k = base + __ffsll(static_cast<long long>(rm)) - 1;
-            found = true;
-        }
-        const bool last_chunk = base + 64 > gb;
-        if ((found || last_chunk) && k >= base && k < base + 64) {
-            Mk = rdlane(M, k - base);
-            Zk = rdlane(Z, k - base);
-            gk = rdlane(g, k - base);
-        }
-        // ---- outputs of this chunk's columns (the drafts of the rows the lanes
-        // hold) while k is not yet behind us; the drawn token's slot is the
-        // select's (another workgroup of this launch).  A violation found in a
-        // later chunk overwrites them (same wave, program order).
-        if (writer && !found_before) {
-            const int col = base + lane;
-            if (col <= G) {
-                const bool k_here = found || last_chunk;      // else k lies in a later chunk
-                int tok = xid;
-                if (k_here) tok = col < k ? xid : ((col == k && greedy) ? gk : -1);
-                if (!(k_here && col == k && !greedy)) P.out_tokens[(size_t)b * (G + 1) + col] = tok;
-            }
-            if (found && !last_chunk)
-                for (int c2c = base + 64 + lane; c2c <= G; c2c += 64) P.out_tokens[(size_t)b * (G + 1) + c2c] = -1;
-        }
+        if (!greedy && !(Z > 0.0 && Z < INFINITY && fabsf(M) < INFINITY)) bad |= kErrNonFinite;
+        rs.rm[tid] = M;
+        rs.rz[tid] = Z;
+        rs.rej[tid] = rej ? 1 : 0;
+        rs.bad[tid] = bad;
     }
+    __syncthreads();
+    // contract violations anywhere in the request (every wave finds the same)
+    uint32_t badq = 0u;
+    for (int j = 0; j <= gb; ++j) badq |= rs.bad[j];
     if (badq != 0u) {
         if (writer) {
             write_violation(P, b);
-            if (lane == 0) flag_error(P.err, P.err_host, badq);
+            if (tid == 0) flag_error(P.err, P.err_host, badq);
         }
         return tk;
     }
+    // k = the first rejected draft (every wave finds the same)
+    const int lane = tid & 63;
+    int k = gb;
+    for (int base = 0; base < gb; base += 64) {
+        const unsigned long long m = __ballot(base + lane < gb && rs.rej[base + lane] != 0);
+        if (m != 0ull) {
+            k = base + __ffsll(static_cast<long long>(m)) - 1;
+            break;
+        }
+    }
     if (writer) {
-        if (lane == 0) P.out_num[b] = k;
+        if (owner) {
+            if (P.diag_m) P.diag_m[t0 + tid] = M;
+            if (P.diag_z) P.diag_z[t0 + tid] = greedy ? 0.0 : Z;
+            if (tid < gb && P.diag_r) P.diag_r[o0 + tid] = greedy ? __uint_as_float(0x7fc00000u) : static_cast<float>(r);
+        }
+        if (tid <= G) {
+            int tok = -1;
+            if (tid < k) tok = xid;
+            else if (tid == k && greedy) tok = g;
+            // the drawn token's slot is the select's (another workgroup of this launch)
+            if (!(tid == k && !greedy)) P.out_tokens[(size_t)b * (G + 1) + tid] = tok;
+        }
+        if (tid == 0) P.out_num[b] = k;
         if (P.stats) {
             uint32_t* S = P.stats;
-            if (lane == 0) {
+            if (tid == 0) {
                 count_add(&S[0], 1u);
                 count_add(&S[1], static_cast<uint32_t>(gb));
                 count_add(&S[2], static_cast<uint32_t>(k));
                 if (k == gb) count_add(&S[3], 1u);
                 count_add(&S[4 + k], 1u);
             }
-            for (int j = lane; j < gb; j += 64) {
-                if (j <= k) count_add(&S[5 + G + j], 1u);
-                if (j < k) count_add(&S[5 + 2 * G + j], 1u);
-            }
+            if (tid < gb && tid <= k) count_add(&S[5 + G + tid], 1u);
+            if (tid < k) count_add(&S[5 + 2 * G + tid], 1u);
         }
     }
-    if (!(T > 0.0f)) return tk;
+    if (greedy) return tk;
     tk.kind = k < gb ? kDrawResidual : kDrawBonus;
     tk.row = t0 + k;
     tk.drow = o0 + k;
     tk.pos = k;
     tk.v = k < gb ? v_res : v_bonus;
-    tk.m = Mk;
-    tk.z32 = Zk;
-    tk.T = T;
+    tk.m = rs.rm[k];
+    tk.z32 = rs.rz[k];
     return tk;
 }
 
-// ----------------------------------------------------------------- draw kernel
-// A workgroup's four waves take four consecutive ranges of one request (a
-// quad); the workgroup works through a contiguous run of quads.  One wave
-// resolves the request (once per request) and shares the task through LDS,
-// every wave streams its range into the range's record, and one arrival per
-// quad tells whether the quad completed the request, in which case the
-// workgroup selects its token.  The first barrier publishes the exponential
-// table in LDS.
-static_assert(kExp2TableSize % kThreads == 0, "whole table entries per draw thread");
-constexpr int kTabPerThread = kExp2TableSize / kThreads;
+// kLoop: waves may hold more than two blocks (taken two at a time in a loop;
+// such grids hold at most three workgroups per CU, so the register budget is
+// that of three); otherwise the grid gives every wave at most two blocks
+// (checked by the host).  The rows kernel only streamed: every workgroup first
+// resolves its request.
+template <typename E, bool kLoop>
+__global__ __launch_bounds__(kThreads, kLoop ? 3 : 4) void draw_kernel(Params P) {
+    __shared__ DrawShared sh;
+    __shared__ ResolveShared rsh;
 
-template <typename E>
-__global__ __launch_bounds__(kThreads, 3) void draw_kernel(Params P) {
-    __shared__ double tab[kExp2TableSize];
-    __shared__ SelShared ss;
-    __shared__ int last_flag;
-    __shared__ WaveTask task_sh;
     const int tid = threadIdx.x;
-    const int wv = tid >> 6;
-    {
-        double tv[kTabPerThread];
+    const int C = P.draw_wgs;
+    // a grid that is resident in one round is dispatched piece-index-major, so
+    // that the workgroups holding the most blocks (low c) start first and the
+    // lightest last (a CU serves its older workgroups first); a larger grid is
+    // request-major, so that early requests finish while later ones wait for slots
+    const int b = P.draw_cmajor ? static_cast<int>(blockIdx.x % P.batch) : static_cast<int>(blockIdx.x / C);
+    const int c = P.draw_cmajor ? static_cast<int>(blockIdx.x / P.batch) : static_cast<int>(blockIdx.x - b * C);
+    const int NB = P.nblocks;
+
+    // the task (or the request's inputs), the temperature and the exponential
+    // table in one round of loads
+    double tv[kTabPerThread];
 #pragma unroll
-        for (int j = 0; j < kTabPerThread; ++j) tv[j] = kExp2Table[tid + j * kThreads];
+    for (int j = 0; j < kTabPerThread; ++j) tv[j] = kExp2Table[tid + j * kThreads];
+    const float T = P.temperature[b];
 #pragma unroll
-        for (int j = 0; j < kTabPerThread; ++j) tab[tid + j * kThreads] = tv[j];
-    }
-    __syncthreads();
-    const int V = P.vocab;
-    const int NR = P.nranges;
-    const int QR = (NR + kWaves - 1) / kWaves;            // quads per request
-    const long Q = (long)P.batch * QR;
-    const long q0 = (long)blockIdx.x * Q / gridDim.x, q1 = (long)(blockIdx.x + 1) * Q / gridDim.x;
-    int cur = -1;
-    WaveTask tk;
-    tk.kind = kDrawNone;
+    for (int j = 0; j < kTabPerThread; ++j) sh.tab[tid + j * kThreads] = tv[j];
+    const DrawTask tk = resolve_request<E>(P, b, c == 0, T, rsh, sh.tab);
+    if (tk.kind == kDrawNone) return;
+    const bool residual = (tk.kind == kDrawResidual);
+    if (tk.row < 0 || tk.row >= P.total_draft + P.batch || tk.pos < 0 || tk.pos > P.gamma ||
+        (residual && (tk.drow < 0 || tk.drow >= P.total_draft)))
+        return;                                    // only reachable with inconsistent offsets
     DrawRow<E> d;
-    double apos = 0.0, aneg = 0.0;
-    for (long q = q0; q < q1; ++q) {
-        const int b = static_cast<int>(q / QR);
-        const int qr = static_cast<int>(q - (long)b * QR);
-        const int j = qr * kWaves + wv;                   // this wave's range (none when j >= NR)
-        if (b != cur) {
-            // one wave of the workgroup resolves the request (a different wave in
-            // neighbouring workgroups, so that the resolves of the workgroups on a
-            // CU fall on different SIMDs) and shares the task through LDS; the
-            // wave of the request's first quad writes its outputs
-            cur = b;
-            if (wv == static_cast<int>(blockIdx.x % kWaves)) {
-                const WaveTask t = resolve_wave<E>(P, b, qr == 0, tab);
-                if ((tid & 63) == 0) task_sh = t;
-            }
-            __syncthreads();
-            tk = task_sh;
-            if (tk.kind != kDrawNone) {
-                const bool residual = (tk.kind == kDrawResidual);
-                if (tk.row < 0 || tk.row >= P.total_draft + P.batch || tk.pos < 0 || tk.pos > P.gamma ||
-                    (residual && (tk.drow < 0 || tk.drow >= P.total_draft))) {
-                    tk.kind = kDrawNone;               // only reachable with inconsistent offsets
-                } else {
-                    init_draw_row<E>(d, P, tk.kind, tk.row, tk.drow, tk.pos, tk.v, tk.m, tk.z32, tk.T);
-                    const double invZ32 = 1.0 / d.z32;
-                    apos = invZ32 * (1.0 - kSignMargin);
-                    aneg = invZ32 * (1.0 + kSignMargin);
-                }
-            }
-        }
-        if (tk.kind == kDrawNone) continue;               // the same for every wave of the workgroup
-        RangeRec* recs = P.recs + (size_t)b * kMaxRanges;
-        if (j < NR) {
-            const int x0 = range_start(j, NR, V), x1 = range_start(j + 1, NR, V);
-            if (d.kind == kDrawResidual && !d.qlist)
-                range_finish<E, true>(d, x0, range_sums<E, true>(d, x0, x1, apos, aneg, tab), tab, &recs[j]);
-            else
-                range_finish<E, false>(d, x0, range_sums<E, false>(d, x0, x1, apos, aneg, tab), tab, &recs[j]);
-        }
-        wait_stores();                 // every wave's record stores complete before the arrival
+    init_draw_row<E>(d, P, tk.kind, tk.row, tk.drow, tk.pos, tk.v, tk.m, tk.z32, T);
+    __syncthreads();
+    BlockRec* recs = P.recs + (size_t)b * NB;
+    draw_blocks<E, !kLoop>(d, P.vocab, recs, c * kWaves + (tid >> 6), C * kWaves, NB, sh.tab);
+    wait_stores();                 // every wave's record stores complete before the arrival
+    __syncthreads();
+    if (C > 1) {                   // (a request's only workgroup selects without arriving)
+        if (tid == 0) sh.flag = (arrive(&P.draw_cnt[b]) == static_cast<uint32_t>(C - 1));
         __syncthreads();
-        if (tid == 0) {
-            const uint32_t n = static_cast<uint32_t>(min(kWaves, NR - qr * kWaves));
-            last_flag = (arrive_n(&P.draw_cnt[b], n) + n == static_cast<uint32_t>(NR));
-        }
-        __syncthreads();
-        if (!last_flag) continue;
+        if (!sh.flag) return;
         if (tid == 0) reset_counter(&P.draw_cnt[b]);
-        const int y = select_wg<E>(d, V, NR, recs, tab, P.err, P.err_host, ss);
-        if (tid == 0) P.out_tokens[(size_t)b * (P.gamma + 1) + tk.pos] = y;
-        __syncthreads();               // ss and last_flag are reused by the next quad
+    }
+    const int y = draw_select_wg<E>(d, P.vocab, NB, recs, sh.tab, P.err, P.err_host, sh.sel);
+    if (tid == 0) {
+        P.out_tokens[(size_t)b * (P.gamma + 1) + tk.pos] = y;
     }
 }
 
