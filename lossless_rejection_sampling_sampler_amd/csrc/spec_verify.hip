@@ -58,23 +58,34 @@ int flat_workgroups(long nv, long vpr, int resident) {
 // Rows kernel then draw kernel on `stream`.  ev, when given, holds four events
 // that the dispatches themselves stamp: rows start / end, draw start / end (the
 // kernels' own execution, without the gap between dispatches).
+// The draw kernel's variant: kLoop (waves take pairs of blocks in a loop),
+// kSplit (one workgroup per block, its waves on the block's sub-blocks), or
+// neither (at most two blocks per wave).
+template <typename E, bool kLoop, bool kSplit>
+void launch_draw(dim3 g2, dim3 blk, const sv::Params& P, hipStream_t stream, const hipEvent_t* ev) {
+    if (ev) hipExtLaunchKernelGGL((sv::draw_kernel<E, kLoop, kSplit>), g2, blk, 0, stream, ev[2], ev[3], 0, P);
+    else hipLaunchKernelGGL((sv::draw_kernel<E, kLoop, kSplit>), g2, blk, 0, stream, P);
+}
+
+// Rows kernel then draw kernel on `stream`.  ev, when given, holds four events
+// that the dispatches themselves stamp: rows start / end, draw start / end (the
+// kernels' own execution, without the gap between dispatches).  draw: 0 pairs
+// of blocks at most per wave, 1 pairs in a loop, 2 split blocks.
 template <typename E>
-int launch_rows_draw(bool aligned, bool loop, long grid1, long grid2, const sv::Params& P, hipStream_t stream,
+int launch_rows_draw(bool aligned, int draw, long grid1, long grid2, const sv::Params& P, hipStream_t stream,
                      const hipEvent_t* ev) {
     const dim3 g1((unsigned)grid1), g2((unsigned)grid2), blk(sv::kThreads);
     if (!ev) {
         if (aligned) hipLaunchKernelGGL(sv::rows_flat_kernel<E>, g1, blk, 0, stream, P);
         else hipLaunchKernelGGL(sv::rows_split_kernel<E>, g1, blk, 0, stream, P);
-        if (loop) hipLaunchKernelGGL((sv::draw_kernel<E, true>), g2, blk, 0, stream, P);
-        else hipLaunchKernelGGL((sv::draw_kernel<E, false>), g2, blk, 0, stream, P);
-        return SV_OK;
-    }
-    if (aligned)
+    } else if (aligned) {
         hipExtLaunchKernelGGL(sv::rows_flat_kernel<E>, g1, blk, 0, stream, ev[0], ev[1], 0, P);
-    else
+    } else {
         hipExtLaunchKernelGGL(sv::rows_split_kernel<E>, g1, blk, 0, stream, ev[0], ev[1], 0, P);
-    if (loop) hipExtLaunchKernelGGL((sv::draw_kernel<E, true>), g2, blk, 0, stream, ev[2], ev[3], 0, P);
-    else hipExtLaunchKernelGGL((sv::draw_kernel<E, false>), g2, blk, 0, stream, ev[2], ev[3], 0, P);
+    }
+    if (draw == 1) launch_draw<E, true, false>(g2, blk, P, stream, ev);
+    else if (draw == 2) launch_draw<E, false, true>(g2, blk, P, stream, ev);
+    else launch_draw<E, false, false>(g2, blk, P, stream, ev);
     return SV_OK;
 }
 
@@ -165,7 +176,12 @@ int enqueue(const Geometry& geo, int resident_flat, int cus, int resident_draw, 
     const int c_max = std::max(1, (geo.nblocks + sv::kWaves - 1) / sv::kWaves);
     const int c_fit = kDrawPerCU * cus / a->batch;
     const bool draw_loop = c_fit < c_min && qmode != sv::kQDense;
-    const int C = draw_loop ? std::max(1, c_fit) : std::max(c_min, std::min(c_max, c_fit));
+    // a call whose blocks all fit one resident round as separate workgroups
+    // (small batches and vocabularies: latency-bound) gives every block its own
+    // workgroup, the block's four sub-blocks to its four waves
+    const bool split = (long)a->batch * geo.nblocks <= (long)resident_draw;
+    const int C = split ? geo.nblocks
+                        : (draw_loop ? std::max(1, c_fit) : std::max(c_min, std::min(c_max, c_fit)));
     P.draw_wgs = C;
     P.parts = sc.parts;
     P.rows = sc.rows;
@@ -189,8 +205,8 @@ int enqueue(const Geometry& geo, int resident_flat, int cus, int resident_draw, 
     P.rows_grid = static_cast<int>(grid1);
     P.draw_cmajor = grid2 <= resident_draw ? 1 : 0;
     const int st = (dtype == SV_BF16)
-                       ? launch_rows_draw<sv::BF16>(aligned, draw_loop, grid1, grid2, P, stream, ev)
-                       : launch_rows_draw<sv::F32>(aligned, draw_loop, grid1, grid2, P, stream, ev);
+                       ? launch_rows_draw<sv::BF16>(aligned, split ? 2 : (draw_loop ? 1 : 0), grid1, grid2, P, stream, ev)
+                       : launch_rows_draw<sv::F32>(aligned, split ? 2 : (draw_loop ? 1 : 0), grid1, grid2, P, stream, ev);
     if (st != SV_OK) return st;
     *schedule = aligned ? SV_SCHEDULE_FLAT : SV_SCHEDULE_SPLIT;
     return SV_OK;

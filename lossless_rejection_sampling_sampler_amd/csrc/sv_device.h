@@ -1256,6 +1256,59 @@ __device__ __forceinline__ void draw_blocks_kind(const DrawRow<E>& d, int V, Blo
     }
 }
 
+// Split blocks: the four waves' sums of one block, met in LDS.
+struct SplitShared {
+    double se[kWaves], ea[kWaves], qa[kWaves];
+    uint32_t mm[kWaves][64];     // every lane's marginal bits
+};
+
+// Split blocks (a call small enough for one workgroup per block in one
+// resident round): wave u streams sub-block u of block j (element-wise where
+// the row's alignment or end requires it), the four waves' sums meet in LDS and
+// wave 0 stores the block's record; a wave then holds 512 tokens, not a whole
+// block.  Uniform call.
+template <typename E, bool kResidual>
+__device__ __forceinline__ void draw_block_split_kind(const DrawRow<E>& d, int V, BlockRec* recs, int j,
+                                                      const double* tab, SplitShared& ss) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const double invZ32 = 1.0 / d.z32;
+    const double apos = invZ32 * (1.0 - kSignMargin), aneg = invZ32 * (1.0 + kSignMargin);
+    const long xb = (long)j * kBlockElems;
+    RawSub<E> r;
+    issue_sub_any<E>(d, sub_first(xb, wv), V, kResidual, r);
+    float l[kSubTokens], q[kSubTokens];
+    decode_sub<E>(r, kResidual, l, q);
+    BlockSums b;
+    accumulate_sub<E, kResidual>(d, l, q, wv, apos, aneg, tab, b);
+    const double se = wave_sum(b.se);
+    const double ea = kResidual ? wave_sum(b.ea) : 0.0;
+    const double qa = kResidual ? wave_sum(b.qa) : 0.0;
+    if (lane == 0) {
+        ss.se[wv] = se;
+        ss.ea[wv] = ea;
+        ss.qa[wv] = qa;
+    }
+    ss.mm[wv][lane] = b.mmask;
+    __syncthreads();
+    if (wv == 0) {
+        // the block's totals on lane 0 (sub-block order), every lane's bits of
+        // all four sub-blocks: store_record's wave sums then give the totals
+        BlockSums t;
+        t.se = lane == 0 ? ((ss.se[0] + ss.se[1]) + ss.se[2]) + ss.se[3] : 0.0;
+        t.ea = lane == 0 ? ((ss.ea[0] + ss.ea[1]) + ss.ea[2]) + ss.ea[3] : 0.0;
+        t.qa = lane == 0 ? ((ss.qa[0] + ss.qa[1]) + ss.qa[2]) + ss.qa[3] : 0.0;
+        t.mmask = ss.mm[0][lane] | ss.mm[1][lane] | ss.mm[2][lane] | ss.mm[3][lane];
+        store_record<E, kResidual>(d, xb, t, tab, &recs[j]);
+    }
+}
+
+template <typename E>
+__device__ __forceinline__ void draw_block_split(const DrawRow<E>& d, int V, BlockRec* recs, int j, const double* tab,
+                                                 SplitShared& ss) {
+    if (d.kind == kDrawResidual && !d.qlist) draw_block_split_kind<E, true>(d, V, recs, j, tab, ss);
+    else draw_block_split_kind<E, false>(d, V, recs, j, tab, ss);
+}
+
 template <typename E, bool kUpTo2 = false>
 __device__ __forceinline__ void draw_blocks(const DrawRow<E>& d, int V, BlockRec* recs, int jfirst, int jstride, int jend,
                             const double* tab) {
@@ -1583,6 +1636,7 @@ constexpr int kTabPerThread = kExp2TableSize / kThreads;
 struct DrawShared {
     double tab[kExp2TableSize];
     SelShared sel;
+    SplitShared split;
     int flag;
 };
 
@@ -1815,7 +1869,7 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
 // that of three); otherwise the grid gives every wave at most two blocks
 // (checked by the host).  The rows kernel only streamed: every workgroup first
 // resolves its request.
-template <typename E, bool kLoop>
+template <typename E, bool kLoop, bool kSplit = false>
 __global__ __launch_bounds__(kThreads, kLoop ? 3 : 4) void draw_kernel(Params P) {
     __shared__ DrawShared sh;
     __shared__ ResolveShared rsh;
@@ -1848,7 +1902,8 @@ __global__ __launch_bounds__(kThreads, kLoop ? 3 : 4) void draw_kernel(Params P)
     init_draw_row<E>(d, P, tk.kind, tk.row, tk.drow, tk.pos, tk.v, tk.m, tk.z32, T);
     __syncthreads();
     BlockRec* recs = P.recs + (size_t)b * NB;
-    draw_blocks<E, !kLoop>(d, P.vocab, recs, c * kWaves + (tid >> 6), C * kWaves, NB, sh.tab);
+    if constexpr (kSplit) draw_block_split<E>(d, P.vocab, recs, c, sh.tab, sh.split);
+    else draw_blocks<E, !kLoop>(d, P.vocab, recs, c * kWaves + (tid >> 6), C * kWaves, NB, sh.tab);
     wait_stores();                 // every wave's record stores complete before the arrival
     __syncthreads();
     if (C > 1) {                   // (a request's only workgroup selects without arriving)
