@@ -21,7 +21,8 @@ namespace {
 constexpr int kRowVecsPerThread = 8;    // target 16-byte vectors per thread per row split
 constexpr int kProfileRing = 2048;      // calls between forced event folds
 constexpr int kDrawBlocksPerWave = 2;   // draw kernel: blocks per wave in straight-line code
-constexpr int kDrawPerCU = 3;           // draw kernel: workgroups per CU aimed at
+constexpr int kDrawPerCU = 4;           // draw kernel (at most two blocks per wave): workgroups per CU aimed at
+constexpr int kDrawLoopPerCU = 3;       // draw kernel taking pairs of blocks in a loop: what it holds per CU
 
 struct Geometry {
     int splits;          // split rows kernel: workgroups per row
@@ -161,9 +162,9 @@ int enqueue(const Geometry& geo, int resident_flat, int cus, int resident_draw, 
     P.vocab = a->vocab;
     P.splits = geo.splits;
     P.nblocks = geo.nblocks;
-    // draw workgroups per request: three per CU over the call (one resident
-    // round) where that keeps between one and kDrawBlocksPerWave blocks per
-    // wave (an even count per CU balances the fp64 work across the SIMDs).  A
+    // draw workgroups per request: four per CU over the call (one resident
+    // round; measured 23.1 against 23.8 us for three on B = 64, V = 151936)
+    // where that keeps between one and kDrawBlocksPerWave blocks per wave.  A
     // call with more draw rows than that round can hold at two blocks per wave
     // (B = 128 or 256 at V = 151936 / 128256) takes a second round of
     // workgroups when its residual blocks stream a dense q row too; with sparse
@@ -176,12 +177,13 @@ int enqueue(const Geometry& geo, int resident_flat, int cus, int resident_draw, 
     const int c_max = std::max(1, (geo.nblocks + sv::kWaves - 1) / sv::kWaves);
     const int c_fit = kDrawPerCU * cus / a->batch;
     const bool draw_loop = c_fit < c_min && qmode != sv::kQDense;
+    const int c_fit_loop = kDrawLoopPerCU * cus / a->batch;
     // a call whose blocks all fit one resident round as separate workgroups
     // (small batches and vocabularies: latency-bound) gives every block its own
     // workgroup, the block's four sub-blocks to its four waves
     const bool split = (long)a->batch * geo.nblocks <= (long)resident_draw;
     const int C = split ? geo.nblocks
-                        : (draw_loop ? std::max(1, c_fit) : std::max(c_min, std::min(c_max, c_fit)));
+                        : (draw_loop ? std::max(1, c_fit_loop) : std::max(c_min, std::min(c_max, c_fit)));
     P.draw_wgs = C;
     P.parts = sc.parts;
     P.rows = sc.rows;
