@@ -639,9 +639,24 @@ struct DraftTok {
 // lookup, and the drafted token's logit and q are read once the stream has been
 // taken in, both so that their round trips overlap other work.  No arrival is
 // counted: the launch boundary orders these stores before the next kernel.
+// Issue priority of a streaming wave: 3 over its workgroup's first quarter of
+// vectors down to 0 over the last.  A CU otherwise issues for its oldest waves
+// first, so its workgroups would finish in dispatch order and the last one
+// would stream alone with a third of the loads in flight; with the priority
+// falling as a wave advances, the waves that are behind are served first and
+// the workgroups of a CU end together.
+__device__ __forceinline__ void set_stream_priority(int level) {
+    if (level >= 3) __builtin_amdgcn_s_setprio(3);
+    else if (level == 2) __builtin_amdgcn_s_setprio(2);
+    else if (level == 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+}
+
+// done0 / total: vectors of the workgroup's range before this piece / in the
+// whole range (total 0: the piece is the range).
 template <typename E>
 __device__ __forceinline__ void row_piece_publish(const Params& P, int t, long v0, long v1, int piece, int npieces,
-                                                 RowShared& sh, DraftTok& dt) {
+                                                 RowShared& sh, DraftTok& dt, long done0 = 0, long total = 0) {
     const int tid = threadIdx.x;
     const int V = P.vocab;
 
@@ -672,6 +687,13 @@ __device__ __forceinline__ void row_piece_publish(const Params& P, int t, long v
     int xd = -1;
     if (tid == 0 && !greedy && i < gb && piece == 0) xd = P.ids[rm.d0 + i];
 
+    // the batches at which the range's second, third and last quarters start
+    const long range = total > 0 ? total : v1 - v0;
+    constexpr int kBatchVecs = kRowUnroll * kThreads;
+    const int q1 = static_cast<int>((range / 4 - done0) / kBatchVecs);
+    const int q2 = static_cast<int>((range / 2 - done0) / kBatchVecs);
+    const int q3 = static_cast<int>((3 * range / 4 - done0) / kBatchVecs);
+
     float mloc;          // piece max (sampled) / argmax value (greedy)
     int gloc = -1;       // argmax (greedy)
     double zloc = 0.0;   // piece sum (sampled)
@@ -687,6 +709,7 @@ __device__ __forceinline__ void row_piece_publish(const Params& P, int t, long v
         int j = 0;
         // (batches j and j + 1 come before the last batch here, so they are full)
         for (; j + 2 < nb; j += 2) {
+            set_stream_priority(3 - static_cast<int>(j >= q1) - static_cast<int>(j >= q2) - static_cast<int>(j >= q3));
             load_batch<E>(Bf, vp, first + (long)(j + 1) * kRowUnroll * kThreads, n - (j + 1) * kRowUnroll);
             take_batch<E, true>(A, kRowUnroll, c, mt, kref, st);
             load_batch<E>(A, vp, first + (long)(j + 2) * kRowUnroll * kThreads, n - (j + 2) * kRowUnroll);
@@ -699,6 +722,7 @@ __device__ __forceinline__ void row_piece_publish(const Params& P, int t, long v
         } else if (j < nb) {
             take_batch<E>(A, n - j * kRowUnroll, c, mt, kref, st);
         }
+        __builtin_amdgcn_s_setprio(0);
         dt.x = -1;
         if (tid == 0 && xd >= 0 && xd < V) {
             dt.x = xd;
@@ -746,6 +770,7 @@ __device__ __forceinline__ void row_piece_publish(const Params& P, int t, long v
         const int nb = (n + kRowUnroll - 1) / kRowUnroll;
         int j = 0;
         for (; j + 2 < nb; j += 2) {
+            set_stream_priority(3 - static_cast<int>(j >= q1) - static_cast<int>(j >= q2) - static_cast<int>(j >= q3));
             load_batch<E>(Bf, vp, first + (long)(j + 1) * kRowUnroll * kThreads, n - (j + 1) * kRowUnroll);
             argmax_batch<E>(A, j * kRowUnroll, n, first, head, bv, bi);
             load_batch<E>(A, vp, first + (long)(j + 2) * kRowUnroll * kThreads, n - (j + 2) * kRowUnroll);
@@ -758,6 +783,7 @@ __device__ __forceinline__ void row_piece_publish(const Params& P, int t, long v
         } else if (j < nb) {
             argmax_batch<E>(A, j * kRowUnroll, n, first, head, bv, bi);
         }
+        __builtin_amdgcn_s_setprio(0);
         if (piece == 0 && tid < head) argmax_merge(bv, bi, E::load1(row, tid), tid);
         if (piece == npieces - 1 && tid >= 64 && tid - 64 < tail) {
             const int x = head + static_cast<int>(nvec * E::kPerVec) + (tid - 64);
@@ -830,7 +856,7 @@ __global__ __launch_bounds__(kThreads) void rows_flat_kernel(Params P) {
         const long s1 = e < re ? e : re;
         const int wf = range_owner(rs, NV, G), wl = range_owner(re - 1, NV, G);
         DraftTok dt;
-        row_piece_publish<E>(P, static_cast<int>(r), s0 - rs, s1 - rs, w - wf, wl - wf + 1, sh, dt);
+        row_piece_publish<E>(P, static_cast<int>(r), s0 - rs, s1 - rs, w - wf, wl - wf + 1, sh, dt, s0 - a, e - a);
         __syncthreads();
         s0 = s1;
     }
@@ -1125,24 +1151,6 @@ __device__ __forceinline__ int sub_first32(int xb, int u) {
     return xb + u * kSubElems + (threadIdx.x & 63) * kSubTokens;
 }
 
-// Sums of one block of a whole-vector row whose loads are in r; once a
-// sub-block's tokens are summed, its registers are refilled with that sub-block
-// of block xn (kRefill), so the wave keeps about a block's loads in flight.
-// No calls: a call would leave the compiler unable to wait for one refill
-// while the later ones stay in flight.
-template <typename E, bool kResidual, bool kRefill>
-__device__ __forceinline__ BlockSums block_stream(const DrawRow<E>& d, RawBlock<E>& r, int xb, int xn, int V,
-                                                  double apos, double aneg, const double* tab) {
-    BlockSums b;
-#pragma unroll
-    for (int u = 0; u < kSubBlocks; ++u) {
-        accumulate_raw<E, kResidual>(d, r.s[u], u, apos, aneg, tab, b);
-        if (kRefill) issue_sub_full<E, kResidual>(d, sub_first32(xn, u), r.s[u]);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    return b;
-}
-
 // Wave totals of one streamed block, stored to its record; a block with inline
 // marginal tokens is remembered (at most two per stream; further ones are left
 // for the select to re-evaluate from their tokens) and captured after the
@@ -1183,27 +1191,48 @@ __device__ __forceinline__ void stream_finish(const BlockSums& b, int j, BlockRe
     }
 }
 
-// Blocks jfirst and, if n == 2, jfirst + jstride of a whole-vector row, all of
-// their loads issued before the first is summed.  Straight-line code: with a
-// loop around it the compiler's allocation spills.
+// Blocks j and, if kN == 2, j2 of a whole-vector row, streamed as one sequence
+// of sub-blocks (block j's four, then j2's) with kStreamDepth sub-blocks' loads
+// in flight: a sub-block's registers are refilled with the one kStreamDepth
+// further on as soon as its tokens are summed.  A wave thus asks for a few KB at
+// a time, and the loads of all the waves meet the memory system interleaved: a
+// wave that starts late is not queued behind whole blocks of earlier waves, and
+// the tokens arrive spread over the stream instead of in per-wave bursts.
+// Straight-line code (a loop around it spills; a call would leave the compiler
+// unable to wait for one refill while the later ones stay in flight).
+constexpr int kStreamDepth = 2;
+template <typename E, bool kResidual, int kN>
+__device__ __forceinline__ void stream_subs(const DrawRow<E>& d, BlockRec* recs, int j, int j2, double apos,
+                                            double aneg, const double* tab, StreamCaps& c) {
+    constexpr int K = kSubBlocks * kN;
+    RawSub<E> slot[kStreamDepth];
+#pragma unroll
+    for (int k = 0; k < kStreamDepth && k < K; ++k)
+        issue_sub_full<E, kResidual>(d, sub_first32((k < kSubBlocks ? j : j2) * kBlockElems, k % kSubBlocks), slot[k]);
+    BlockSums b;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        accumulate_raw<E, kResidual>(d, slot[k % kStreamDepth], k % kSubBlocks, apos, aneg, tab, b);
+        if (k + kStreamDepth < K) {
+            const int kn = k + kStreamDepth;
+            issue_sub_full<E, kResidual>(d, sub_first32((kn < kSubBlocks ? j : j2) * kBlockElems, kn % kSubBlocks),
+                                         slot[k % kStreamDepth]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (k % kSubBlocks == kSubBlocks - 1) {
+            stream_finish<kResidual>(b, k < kSubBlocks ? j : j2, recs, c);
+            b = BlockSums();
+        }
+    }
+}
+
+// Blocks j and, if n == 2, j + jstride of a whole-vector row.
 template <typename E, bool kResidual>
 __device__ __forceinline__ void draw_blocks_upto2(const DrawRow<E>& d, int V, BlockRec* recs, int j, int jstride,
                                                   int n, double apos, double aneg, const double* tab,
                                                   StreamCaps& c) {
-    RawBlock<E> r;
-#pragma unroll
-    for (int u = 0; u < kSubBlocks; ++u) issue_sub_full<E, kResidual>(d, sub_first32(j * kBlockElems, u), r.s[u]);
-    if (n >= 2) {
-        const int j2 = j + jstride;
-        const BlockSums b1 = block_stream<E, kResidual, true>(d, r, j * kBlockElems, j2 * kBlockElems, V, apos, aneg,
-                                                             tab);
-        stream_finish<kResidual>(b1, j, recs, c);
-        const BlockSums b2 = block_stream<E, kResidual, false>(d, r, j2 * kBlockElems, 0, V, apos, aneg, tab);
-        stream_finish<kResidual>(b2, j2, recs, c);
-    } else {
-        const BlockSums b = block_stream<E, kResidual, false>(d, r, j * kBlockElems, 0, V, apos, aneg, tab);
-        stream_finish<kResidual>(b, j, recs, c);
-    }
+    if (n >= 2) stream_subs<E, kResidual, 2>(d, recs, j, j + jstride, apos, aneg, tab, c);
+    else stream_subs<E, kResidual, 1>(d, recs, j, j, apos, aneg, tab, c);
 }
 
 template <typename E, bool kResidual>
@@ -1708,8 +1737,8 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
     // same table-based exp2 as the draw weights
     const double cpz = greedy ? 0.0 : kExp2Scale * static_cast<double>(static_cast<float>(kLog2e / static_cast<double>(T)));
     const double c2 = greedy ? 0.0 : kExp2Scale * (kLog2e / static_cast<double>(T));
-    const float v_res = P.uniforms[(size_t)b * (G + 2) + G];
-    const float v_bonus = P.uniforms[(size_t)b * (G + 2) + G + 1];
+    float v_res = P.uniforms[(size_t)b * (G + 2) + G];
+    float v_bonus = P.uniforms[(size_t)b * (G + 2) + G + 1];
     const bool owner = tid <= gb;
     float M = -INFINITY;          // row max, or the argmax value
     int g = 0x7fffffff;           // argmax
@@ -1755,6 +1784,10 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
     // publishes the exponential table (stored to LDS by the caller); the loads
     // above are complete after it
     __syncthreads();
+    // the draw's uniforms taken into registers here, with the other loads: their
+    // first use comes after the writer's output stores, and a wait there would
+    // wait for those stores too
+    asm volatile("" : "+v"(v_res), "+v"(v_bonus));
     if (owner) {
         for (int p0 = 0; p0 < np; p0 += kResolveChunk) {
             if (p0 > 0) {
