@@ -85,7 +85,7 @@ struct RowStat {         // merged statistics of one target row
     float lx;            // logit of the drafted token of this position
     float qx;            // q of the drafted token
     int x;               // drafted token, -1 if invalid / none
-    int pad;
+    int np;              // pieces of the row (stored by its piece 0)
 };
 
 struct DrawTask {        // written by the resolving workgroup, read by the draw kernel
@@ -811,6 +811,7 @@ __device__ __forceinline__ void row_piece_publish(const Params& P, int t, long v
             st_coherent(&rp->x, dt.x);
             st_coherent(&rp->lx, dt.lx);
             st_coherent(&rp->qx, dt.qx);
+            st_coherent(&rp->np, npieces);
         }
     }
 }
@@ -1753,32 +1754,27 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
     int gg[kResolveChunk];
     double zz[kResolveChunk];
     if (owner) {
+        // stored by the rows kernel: the launch boundary orders those stores
+        // before these plain loads.  The row's first kResolveChunk piece slots
+        // are loaded together with its piece count (slots past the count hold
+        // stale values and are masked once it is in), so that no load waits for
+        // another or for the temperature.
         const int t = t0 + tid;
-        if (P.split_pieces > 0) {
-            np = P.split_pieces;
-        } else {
-            const long rsv = (long)t * P.flat_vpr;
-            np = range_owner(rsv + P.flat_vpr - 1, P.flat_nv, P.rows_grid) - range_owner(rsv, P.flat_nv, P.rows_grid) + 1;
-        }
+        const RowStat* rp = &P.rows[t];
+        np = rp->np;
         if (tid < gb) {
             xid = P.ids[o0 + tid];
-            if (!greedy) {
-                // stored by the rows kernel: the launch boundary orders those
-                // stores before these plain loads
-                const RowStat* rp = &P.rows[t];
-                xs = rp->x;
-                lx = rp->lx;
-                qx = rp->qx;
-                u = P.uniforms[(size_t)b * (G + 2) + tid];
-            }
+            xs = rp->x;
+            lx = rp->lx;
+            qx = rp->qx;
+            u = P.uniforms[(size_t)b * (G + 2) + tid];
         }
         pp = &P.parts[(size_t)t * kMaxPieces];
 #pragma unroll
         for (int q = 0; q < kResolveChunk; ++q) {
-            const bool in = q < np;
-            mm[q] = in ? pp[q].m : -INFINITY;
-            gg[q] = in ? pp[q].g : 0x7fffffff;
-            zz[q] = in ? pp[q].z : 0.0;
+            mm[q] = pp[q].m;
+            gg[q] = pp[q].g;
+            zz[q] = pp[q].z;
         }
     }
     // publishes the exponential table (stored to LDS by the caller); the loads
@@ -1789,6 +1785,15 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
     // wait for those stores too
     asm volatile("" : "+v"(v_res), "+v"(v_bonus));
     if (owner) {
+        np = min(max(np, 0), kMaxPieces);
+#pragma unroll
+        for (int q = 0; q < kResolveChunk; ++q) {
+            if (q >= np) {
+                mm[q] = -INFINITY;
+                gg[q] = 0x7fffffff;
+                zz[q] = 0.0;
+            }
+        }
         for (int p0 = 0; p0 < np; p0 += kResolveChunk) {
             if (p0 > 0) {
 #pragma unroll
@@ -1807,10 +1812,14 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
                 if (Mc > M && M > -INFINITY)
                     Z *= exp2_tab((static_cast<double>(M) - static_cast<double>(Mc)) * cpz, tab);
                 M = Mc;
+                // every slot's factor first (one round of table reads); an empty
+                // slot (max -inf, sum 0) adds 0, its factor being 0
+                double f[kResolveChunk];
 #pragma unroll
                 for (int q = 0; q < kResolveChunk; ++q)
-                    if (mm[q] > -INFINITY)
-                        Z += zz[q] * exp2_tab((static_cast<double>(mm[q]) - static_cast<double>(M)) * cpz, tab);
+                    f[q] = exp2_tab((static_cast<double>(mm[q]) - static_cast<double>(M)) * cpz, tab);
+#pragma unroll
+                for (int q = 0; q < kResolveChunk; ++q) Z += zz[q] * f[q];
             } else {
 #pragma unroll
                 for (int q = 0; q < kResolveChunk; ++q) argmax_merge(M, g, mm[q], gg[q]);
@@ -1839,10 +1848,14 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
         rs.bad[tid] = bad;
     }
     __syncthreads();
-    // contract violations anywhere in the request (every wave finds the same)
-    uint32_t badq = 0u;
-    for (int j = 0; j <= gb; ++j) badq |= rs.bad[j];
-    if (badq != 0u) {
+    // contract violations anywhere in the request (every wave finds the same):
+    // a lane per row, then the bits themselves only when there are any
+    const int lane = tid & 63;
+    uint32_t badl = 0u;
+    for (int j = lane; j <= gb; j += 64) badl |= rs.bad[j];
+    if (__ballot(badl != 0u) != 0ull) {
+        uint32_t badq = 0u;
+        for (int j = 0; j <= gb; ++j) badq |= rs.bad[j];
         if (writer) {
             write_violation(P, b);
             if (tid == 0) flag_error(P.err, P.err_host, badq);
@@ -1850,7 +1863,6 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
         return tk;
     }
     // k = the first rejected draft (every wave finds the same)
-    const int lane = tid & 63;
     int k = gb;
     for (int base = 0; base < gb; base += 64) {
         const unsigned long long m = __ballot(base + lane < gb && rs.rej[base + lane] != 0);
