@@ -194,17 +194,22 @@ int enqueue(const Geometry& geo, int resident_flat, int cus, int resident_draw, 
 
     const long rows = (long)a->total_draft + a->batch;
     // rows start on 16-byte boundaries: stream the flattened rows in equal ranges
-    const bool aligned = (reinterpret_cast<uintptr_t>(a->target_logits) % 16 == 0) &&
-                         (((long)a->vocab * (long)esize) % 16 == 0);
     P.flat_vpr = (long)a->vocab * (long)esize / 16;
     P.flat_nv = rows * P.flat_vpr;
+    // (the flat kernel's range arithmetic needs flat_nv * grid below 2^52: far
+    // beyond any call that fits in device memory, but checked)
+    const bool aligned = (reinterpret_cast<uintptr_t>(a->target_logits) % 16 == 0) &&
+                         (((long)a->vocab * (long)esize) % 16 == 0) &&
+                         static_cast<double>(P.flat_nv) * resident_flat < 4.5e15;
     // rows are streamed without any hand-off between workgroups (flattened
     // ranges for 16-byte aligned rows, per-row splits otherwise) and every
     // request is resolved by its draw workgroups
-    P.split_pieces = aligned ? 0 : P.splits;
     const long grid1 = aligned ? flat_workgroups(P.flat_nv, P.flat_vpr, resident_flat) : rows * P.splits;
     const long grid2 = (long)a->batch * C;
     P.rows_grid = static_cast<int>(grid1);
+    P.flat_inv_nv = 1.0 / static_cast<double>(P.flat_nv);
+    P.flat_inv_vpr = 1.0 / static_cast<double>(P.flat_vpr);
+    P.flat_inv_grid = 1.0 / static_cast<double>(grid1);
     P.draw_cmajor = grid2 <= resident_draw ? 1 : 0;
     const int st = (dtype == SV_BF16)
                        ? launch_rows_draw<sv::BF16>(aligned, split ? 2 : (draw_loop ? 1 : 0), grid1, grid2, P, stream, ev)

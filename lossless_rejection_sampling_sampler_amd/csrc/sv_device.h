@@ -134,8 +134,8 @@ struct Params {
     long flat_vpr;       // flat rows kernel: vectors per row
     int draw_wgs;        // draw kernel: workgroups per request
     int draw_cmajor;     // draw kernel: workgroup w serves request w % batch (else w / draw_wgs)
-    int rows_grid;       // flat rows kernel: its grid (the piece geometry the draw kernel's resolve reads)
-    int split_pieces;    // split rows kernel: pieces per row (0: the flat geometry)
+    int rows_grid;       // flat rows kernel: its grid
+    double flat_inv_nv, flat_inv_vpr, flat_inv_grid;   // 1 / flat_nv, 1 / flat_vpr, 1 / rows_grid
     int nblocks;         // draw blocks per row
     // scratch
     Piece* parts;        // [rows][kMaxPieces]
@@ -830,14 +830,27 @@ __global__ __launch_bounds__(kThreads) void rows_split_kernel(Params P) {
     if (head > V) head = V;
     const long nvec = (V - head) / E::kPerVec;
     DraftTok dt;
-    // pieces only: the draw kernel merges and resolves (P.split_pieces = S)
+    // pieces only: the draw kernel merges and resolves
     row_piece_publish<E>(P, t, (long)s * nvec / S, (long)(s + 1) * nvec / S, s, S, sh, dt);
+}
+
+// floor(x / d) for 0 <= x < 2^52 and d >= 1, given inv = 1 / d rounded to
+// double.  The rounded product x * inv is within a few units in its last place
+// of x / d, so its truncation is the quotient or one off it, and one step each
+// way on the remainder makes it exact (the device has no integer divider; its
+// software 64-bit division is a long dependent chain).
+__device__ __forceinline__ long div_exact(long x, long d, double inv) {
+    long q = static_cast<long>(static_cast<double>(x) * inv);
+    const long r = x - q * d;
+    q += (r >= d) ? 1 : 0;
+    q -= (r < 0) ? 1 : 0;
+    return q;
 }
 
 // Workgroup owning vector v when nv vectors are cut into g equal ranges
 // [floor(w nv / g), floor((w+1) nv / g)).
-__device__ __forceinline__ int range_owner(long v, long nv, int g) {
-    return static_cast<int>(((v + 1) * (long)g - 1) / nv);
+__device__ __forceinline__ int range_owner(long v, long nv, int g, double inv_nv) {
+    return static_cast<int>(div_exact((v + 1) * (long)g - 1, nv, inv_nv));
 }
 
 // Rows streamed only: every piece of this workgroup's range is stored
@@ -848,14 +861,14 @@ template <typename E>
 __global__ __launch_bounds__(kThreads) void rows_flat_kernel(Params P) {
     __shared__ RowShared sh;
     const int w = blockIdx.x;
-    const int G = gridDim.x;
+    const int G = P.rows_grid;
     const long VPR = P.flat_vpr, NV = P.flat_nv;
-    const long a = (long)w * NV / G, e = (long)(w + 1) * NV / G;
-    long r = a / VPR;
+    const long a = div_exact((long)w * NV, G, P.flat_inv_grid), e = div_exact((long)(w + 1) * NV, G, P.flat_inv_grid);
+    long r = div_exact(a, VPR, P.flat_inv_vpr);
     for (long s0 = a; s0 < e; ++r) {
         const long rs = r * VPR, re = rs + VPR;
         const long s1 = e < re ? e : re;
-        const int wf = range_owner(rs, NV, G), wl = range_owner(re - 1, NV, G);
+        const int wf = range_owner(rs, NV, G, P.flat_inv_nv), wl = range_owner(re - 1, NV, G, P.flat_inv_nv);
         DraftTok dt;
         row_piece_publish<E>(P, static_cast<int>(r), s0 - rs, s1 - rs, w - wf, wl - wf + 1, sh, dt, s0 - a, e - a);
         __syncthreads();
