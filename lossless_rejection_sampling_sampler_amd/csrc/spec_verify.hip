@@ -207,6 +207,12 @@ int enqueue(const Geometry& geo, int resident_flat, int cus, int resident_draw, 
     const long grid1 = aligned ? flat_workgroups(P.flat_nv, P.flat_vpr, resident_flat) : rows * P.splits;
     const long grid2 = (long)a->batch * C;
     P.rows_grid = static_cast<int>(grid1);
+    if (aligned) {
+        const long lmin = P.flat_nv / grid1;       // shortest range
+        P.max_pieces = static_cast<int>(std::min<long>(sv::kMaxPieces, (P.flat_vpr + lmin - 1) / lmin + 1));
+    } else {
+        P.max_pieces = P.splits;
+    }
     P.flat_inv_nv = 1.0 / static_cast<double>(P.flat_nv);
     P.flat_inv_vpr = 1.0 / static_cast<double>(P.flat_vpr);
     P.flat_inv_grid = 1.0 / static_cast<double>(grid1);

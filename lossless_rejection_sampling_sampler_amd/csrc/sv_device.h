@@ -135,6 +135,7 @@ struct Params {
     int draw_wgs;        // draw kernel: workgroups per request
     int draw_cmajor;     // draw kernel: workgroup w serves request w % batch (else w / draw_wgs)
     int rows_grid;       // flat rows kernel: its grid
+    int max_pieces;      // most pieces any row is cut into (either rows kernel)
     double flat_inv_nv, flat_inv_vpr, flat_inv_grid;   // 1 / flat_nv, 1 / flat_vpr, 1 / rows_grid
     int nblocks;         // draw blocks per row
     // scratch
@@ -1763,9 +1764,12 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
     int xs = -1, np = 0;
     float lx = 0.0f, qx = 0.0f, u = 0.0f;
     const Piece* pp = nullptr;
-    float mm[kResolveChunk];
-    int gg[kResolveChunk];
-    double zz[kResolveChunk];
+    float mm[kResolveChunk], mm2[kResolveChunk];
+    int gg[kResolveChunk], gg2[kResolveChunk];
+    double zz[kResolveChunk], zz2[kResolveChunk];
+    // rows of more than kResolveChunk pieces: the second round of slots is
+    // loaded with the first (the geometry's bound, not the row's count, decides)
+    const bool two = P.max_pieces > kResolveChunk;
     if (owner) {
         // stored by the rows kernel: the launch boundary orders those stores
         // before these plain loads.  The row's first kResolveChunk piece slots
@@ -1789,6 +1793,14 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
             gg[q] = pp[q].g;
             zz[q] = pp[q].z;
         }
+        if (two) {
+#pragma unroll
+            for (int q = 0; q < kResolveChunk; ++q) {
+                mm2[q] = pp[kResolveChunk + q].m;
+                gg2[q] = pp[kResolveChunk + q].g;
+                zz2[q] = pp[kResolveChunk + q].z;
+            }
+        }
     }
     // publishes the exponential table (stored to LDS by the caller); the loads
     // above are complete after it
@@ -1808,7 +1820,15 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
             }
         }
         for (int p0 = 0; p0 < np; p0 += kResolveChunk) {
-            if (p0 > 0) {
+            if (p0 == kResolveChunk && two) {
+#pragma unroll
+                for (int q = 0; q < kResolveChunk; ++q) {
+                    const bool in = p0 + q < np;
+                    mm[q] = in ? mm2[q] : -INFINITY;
+                    gg[q] = in ? gg2[q] : 0x7fffffff;
+                    zz[q] = in ? zz2[q] : 0.0;
+                }
+            } else if (p0 > 0) {
 #pragma unroll
                 for (int q = 0; q < kResolveChunk; ++q) {
                     const bool in = p0 + q < np;
