@@ -1615,6 +1615,7 @@ static_assert(kSubBlocks == kWaves, "one sub-block per wave");
 struct SelShared {
     double tot[kWaves];
     int yc[kWaves], yl[kWaves];
+    double zs[kWaves];       // (single-block draws) wave sums of e
 };
 
 template <typename E>
@@ -1645,6 +1646,81 @@ __device__ __forceinline__ int draw_select_wg(const DrawRow<E>& d, int V, int NB
 #pragma unroll
     for (int u = 1; u < kWaves; ++u) { yc = min(yc, ss.yc[u]); yl = max(yl, ss.yl[u]); }
     return select_token(yc, yl, V, sb.jsel);
+}
+
+// The whole draw of a row that is a single block (V <= 2048), by the request's
+// only workgroup: wave u loads sub-block u once and keeps it; Z64 (every
+// token's e, wave sums met in LDS in wave order), the token weights with the
+// exact normaliser, their sum S and the token holding v * S all come from
+// those registers.  No block record, no marginal tokens, no second read.
+// Every thread returns the token.  Uniform call.
+template <typename E>
+__device__ __forceinline__ int draw_single_block(const DrawRow<E>& d, int V, const double* tab, uint32_t* err,
+                                                 uint32_t* err_host, SelShared& ss) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const bool residual = (d.kind == kDrawResidual);
+    SelBlock sb;
+    sb.jsel = 0;
+    sb.base = 0.0;
+    sb.fallback = false;
+    sb.qid = -1;
+    sb.qq = 0.0f;
+    if (residual && d.qlist && lane < d.nq) {
+        sb.qid = d.sid[lane];
+        sb.qq = d.sq ? d.sq[lane] : 1.0f;
+    }
+    const long x0 = sub_first(0, wv);
+    RawSub<E> raw;
+    issue_sub_any<E>(d, x0, V, residual && !d.qlist, raw);
+    const bool qvalid = sb.qid >= 0 && sb.qid < V;
+    if (wv == 0 && lane < d.nq && !qvalid && sb.qid != -1) flag_error(err, err_host, kErrTopk);
+    double se = 0.0;
+#pragma unroll
+    for (int k = 0; k < kSubTokens; ++k) {
+        if (x0 + k < V) se += draw_e<E>(d, sub_logit<E>(raw, k), tab);
+        if (k & 1) __builtin_amdgcn_sched_barrier(0);
+    }
+    const double zw = wave_sum(se);
+    if (lane == 0) ss.zs[wv] = zw;
+    __syncthreads();
+    sb.invZ64 = 1.0 / (((ss.zs[0] + ss.zs[1]) + ss.zs[2]) + ss.zs[3]);
+    sb.res_w = residual;
+    sb.with_q = residual && !d.qlist;
+    // every listed token lies in the one block
+    sb.qmask = residual ? __ballot(qvalid) : 0ull;
+    double w[kSubTokens];
+    double tsum = sub_weights<E>(d, raw, x0, V, sb, tab, w);
+    double ti = wave_inclusive_scan(tsum);
+    if (lane == 63) ss.tot[wv] = ti;
+    __syncthreads();
+    double Stot = ((ss.tot[0] + ss.tot[1]) + ss.tot[2]) + ss.tot[3];
+    if (residual && !(Stot > 0.0)) {
+        // residual lost to rounding: draw from p itself
+        sb.res_w = false;
+        sb.with_q = false;
+        sb.qmask = 0ull;
+        __syncthreads();                 // every thread has read the first sums
+        tsum = sub_weights<E>(d, raw, x0, V, sb, tab, w);
+        ti = wave_inclusive_scan(tsum);
+        if (lane == 63) ss.tot[wv] = ti;
+        __syncthreads();
+        Stot = ((ss.tot[0] + ss.tot[1]) + ss.tot[2]) + ss.tot[3];
+    }
+    if (!(Stot > 0.0) && tid == 0) flag_error(err, err_host, kErrNonFinite);
+    sb.tsel = static_cast<double>(d.v) * Stot;
+    double run_base = 0.0;
+#pragma unroll
+    for (int u = 0; u < kWaves; ++u) run_base += (u < wv) ? ss.tot[u] : 0.0;
+    int ycand = 0x7fffffff, ylast = -1;
+    sub_find(w, x0, run_base + (ti - tsum), sb, ycand, ylast);
+    ycand = wave_min_int(ycand);
+    ylast = wave_max_int(ylast);
+    if (lane == 0) { ss.yc[wv] = ycand; ss.yl[wv] = ylast; }
+    __syncthreads();
+    int yc = ss.yc[0], yl = ss.yl[0];
+#pragma unroll
+    for (int u = 1; u < kWaves; ++u) { yc = min(yc, ss.yc[u]); yl = max(yl, ss.yl[u]); }
+    return select_token(yc, yl, V, 0);
 }
 
 template <typename E>
@@ -1979,6 +2055,13 @@ __global__ __launch_bounds__(kThreads, kLoop ? 3 : 4) void draw_kernel(Params P)
     DrawRow<E> d;
     init_draw_row<E>(d, P, tk.kind, tk.row, tk.drow, tk.pos, tk.v, tk.m, tk.z32, T);
     __syncthreads();
+    if constexpr (kSplit) {
+        if (NB == 1) {             // (then this is the request's only workgroup)
+            const int y = draw_single_block<E>(d, P.vocab, sh.tab, P.err, P.err_host, sh.sel);
+            if (tid == 0) P.out_tokens[(size_t)b * (P.gamma + 1) + tk.pos] = y;
+            return;
+        }
+    }
     BlockRec* recs = P.recs + (size_t)b * NB;
     if constexpr (kSplit) draw_block_split<E>(d, P.vocab, recs, c, sh.tab, sh.split);
     else draw_blocks<E, !kLoop>(d, P.vocab, recs, c * kWaves + (tid >> 6), C * kWaves, NB, sh.tab);
