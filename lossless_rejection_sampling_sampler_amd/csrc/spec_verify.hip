@@ -166,17 +166,17 @@ int enqueue(const Geometry& geo, int resident_flat, int cus, int resident_draw, 
     // round; measured 23.1 against 23.8 us for three on B = 64, V = 151936)
     // where that keeps between one and kDrawBlocksPerWave blocks per wave.  A
     // call with more draw rows than that round can hold at two blocks per wave
-    // (B = 128 or 256 at V = 151936 / 128256) takes a second round of
-    // workgroups when its residual blocks stream a dense q row too; with sparse
-    // or point-mass q (every block streams logits only, so a workgroup's
-    // fixed latency outweighs its bytes) its waves take pairs of blocks in a
-    // loop instead (measured: 100 against 110 us at B = 256 with top-50 lists,
-    // 114 against 109 us with dense q)
+    // (B = 128 or 256 at V = 151936 / 128256) has its waves take pairs of
+    // blocks in a loop, in one resident round at three workgroups per CU
+    // (draw kernel, against a second round of workgroups: B = 128 T mix 32.1
+    // against 34.5 us, B = 256 ragged 44.0 against 45.2, B = 256 top-50 q in
+    // dense rows 47.0 against 52.1; four per CU was faster on some of these and
+    // slower on others)
     const int c_min = std::max(1, (geo.nblocks + sv::kWaves * kDrawBlocksPerWave - 1) /
                                       (sv::kWaves * kDrawBlocksPerWave));
     const int c_max = std::max(1, (geo.nblocks + sv::kWaves - 1) / sv::kWaves);
     const int c_fit = kDrawPerCU * cus / a->batch;
-    const bool draw_loop = c_fit < c_min && qmode != sv::kQDense;
+    const bool draw_loop = c_fit < c_min;
     const int c_fit_loop = kDrawLoopPerCU * cus / a->batch;
     // a call whose blocks all fit one resident round as separate workgroups
     // (small batches and vocabularies: latency-bound) gives every block its own

@@ -681,7 +681,7 @@ __device__ __forceinline__ void row_piece_publish(const Params& P, int t, long v
         if (tid == 0 && piece == 0) flag_error(P.err, P.err_host, kErrOffsets);
         return;
     }
-    const int b = rm.b, i = rm.i, gb = rm.gb;
+    const int i = rm.i, gb = rm.gb;
     const float T = rm.T;
     const bool greedy = !(T > 0.0f);
     const float c = greedy ? 0.0f : static_cast<float>(kLog2e / static_cast<double>(T));
