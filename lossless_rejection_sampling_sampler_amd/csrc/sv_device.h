@@ -1147,16 +1147,20 @@ __device__ __forceinline__ void block_record(const DrawRow<E>& d, const RawBlock
 }
 
 // Loads of this lane's tokens [x0, x0 + 8) of a block lying wholly inside a
-// 16-byte aligned row (and q row): plain vector loads.
+// 16-byte aligned row (and q row): plain vector loads with the default cache
+// policy (measured against non-temporal loads, with the inputs rotating over
+// more than the Infinity Cache holds: draw kernel -0.5 us and rows kernel
+// +0.5 us on B = 64, V = 151936; the step -1.1 us on B = 256 ragged and
+// -0.35 us with point-mass q).
 template <typename E, bool kWithQ>
 __device__ __forceinline__ void issue_sub_full(const DrawRow<E>& d, int x0, RawSub<E>& r) {
     const v4u* lp = reinterpret_cast<const v4u*>(d.lrow + x0);
 #pragma unroll
-    for (int h = 0; h < kSubTokens / E::kPerVec; ++h) r.l[h] = __builtin_nontemporal_load(lp + h);
+    for (int h = 0; h < kSubTokens / E::kPerVec; ++h) r.l[h] = lp[h];
     if (kWithQ) {
         const v4u* qp = reinterpret_cast<const v4u*>(d.qrow + x0);
 #pragma unroll
-        for (int h = 0; h < kSubTokens / 4; ++h) r.q[h] = __builtin_nontemporal_load(qp + h);
+        for (int h = 0; h < kSubTokens / 4; ++h) r.q[h] = qp[h];
     }
 }
 
