@@ -1147,16 +1147,18 @@ __device__ __forceinline__ void block_record(const DrawRow<E>& d, const RawBlock
 }
 
 // Loads of this lane's tokens [x0, x0 + 8) of a block lying wholly inside a
-// 16-byte aligned row (and q row): plain vector loads with the default cache
-// policy (measured against non-temporal loads, with the inputs rotating over
-// more than the Infinity Cache holds: draw kernel -0.5 us and rows kernel
-// +0.5 us on B = 64, V = 151936; the step -1.1 us on B = 256 ragged and
-// -0.35 us with point-mass q).
+// 16-byte aligned row (and q row).  Cache policy, as measured with the inputs
+// rotating over more than the Infinity Cache holds: q rows with the default
+// policy, logits non-temporal beside a q row and default-policy without one
+// (B = 64, V = 151936: 44.2-44.4 us per step against 44.7-45.1 with every
+// load default-policy and 44.9 with every load non-temporal; B = 256 ragged
+// 98.4 against 99.4 and 100.3; point-mass q, logits only, 37.8 default-policy
+// against 38.3 non-temporal).
 template <typename E, bool kWithQ>
 __device__ __forceinline__ void issue_sub_full(const DrawRow<E>& d, int x0, RawSub<E>& r) {
     const v4u* lp = reinterpret_cast<const v4u*>(d.lrow + x0);
 #pragma unroll
-    for (int h = 0; h < kSubTokens / E::kPerVec; ++h) r.l[h] = lp[h];
+    for (int h = 0; h < kSubTokens / E::kPerVec; ++h) r.l[h] = kWithQ ? __builtin_nontemporal_load(lp + h) : lp[h];
     if (kWithQ) {
         const v4u* qp = reinterpret_cast<const v4u*>(d.qrow + x0);
 #pragma unroll
