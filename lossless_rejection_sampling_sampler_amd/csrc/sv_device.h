@@ -1267,7 +1267,7 @@ __device__ __forceinline__ void capture_marginals(const DrawRow<E>& d, BlockRec*
 
 // Per-block sums of draw blocks jfirst, jfirst + jstride, ... < jend, written to
 // recs.  In 16-byte aligned rows, blocks lying wholly inside the row are taken
-// two at a time with all of their loads in flight together (kUpTo2: the caller
+// two at a time as one stream of sub-blocks (stream_subs; kUpTo2: the caller
 // guarantees at most two blocks, and no loop is generated around them); the
 // row's ragged last block, and every block of other rows, is taken on its own.
 template <typename E, bool kResidual, bool kUpTo2>
