@@ -114,6 +114,21 @@ def test_full_workload_parity(n, nsets):
     _assert_ok(rep, errs, min_requests=20000)
 
 
+# distinct logits and q draws at full size (row statistics at V = 151936 over
+# 8 x 384 rows of the headline shapes, not one draw under many uniform sets)
+DISTINCT = [(3, 8, 8), (4, 2, 4)]
+
+
+@pytest.mark.parametrize("n,ndraws,nsets", DISTINCT, ids=[f"config{n}" for n, _, _ in DISTINCT])
+def test_full_workload_distinct_draws(n, ndraws, nsets):
+    for r in range(1, ndraws + 1):
+        log(f"[distinct] config {n} seed={1000 * n + r} sets={nsets}")
+        inp = make_config(n, replicate=r)
+        sets = [inp.uniforms] + [uniforms_from_seed(inp.uniforms.shape, 700 + 10 * r + s) for s in range(nsets - 1)]
+        rep, errs, _ = parity_check(inp, sets, label=f"config{n}-draw{r}")
+        _assert_ok(rep, errs)
+
+
 @pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("n", [3, 5], ids=["config3", "config5"])
 def test_full_workload_each_schedule(n, schedule):
