@@ -1,11 +1,13 @@
-"""The library's largest shapes through the HIP path, element by element against
-the CPU oracle (runs on an MI355X).
+"""The library's largest and smallest shapes through the HIP path, element by
+element against the CPU oracle (runs on an MI355X).
 
 The boundary takes vocabularies up to 524,288 (256 draw blocks of 2048 tokens
 per row: every slot of the select's block scan) and drafts up to 128 tokens
 per request (129 target rows: one more than the resolve's threads of a wave,
-so its row owners span three waves).  Each case prints its name and shape
-before touching the GPU.
+so its row owners span three waves).  At the other end, a vocabulary of one
+token (every draw is token 0 and every draft is accepted) or two, and the
+vocabularies around one draw block.  Each case prints its name and shape before
+touching the GPU.
 """
 
 import numpy as np
@@ -40,6 +42,30 @@ def test_largest_shapes(name, n, kw, depth):
         # the case reaches the depth it is meant to exercise
         assert int(oracle.verify(inp).num_accepted.max()) >= depth
     sets = [inp.uniforms] + [uniforms_from_seed(inp.uniforms.shape, 300 + s) for s in range(11)]
+    rep, errs, _ = parity_check(inp, sets, label=name)
+    assert not rep.unexcused, "\n".join(rep.unexcused[:10])
+    assert not errs, errs
+    assert rep.excused <= 1e-4 * rep.requests + 1e-9 or rep.excused == 0
+
+
+SMALLEST = [
+    ("V1_f32", 1, dict(vocab=1, batch=5)),                                    # 4-byte rows: unaligned path
+    ("V2_f32", 1, dict(vocab=2, batch=7)),
+    ("V1_bf16", 3, dict(vocab=1, batch=4, n_peaks=0)),
+    ("V1_bf16_tmix", 4, dict(vocab=1, batch=9, n_peaks=0)),                  # greedy rows of one token
+    ("V2_bf16_tmix", 4, dict(vocab=2, batch=9, n_peaks=0)),
+    ("V2_bf16_ragged", 5, dict(vocab=2, batch=9, n_peaks=0, top_k=2)),
+    ("V8_bf16", 3, dict(vocab=8, batch=4)),                                   # one 16-byte vector per row
+    ("V2049_f32", 2, dict(vocab=2049, batch=6)),                              # a second block of one token
+    ("V2047_bf16", 3, dict(vocab=2047, batch=6)),                             # one block, unaligned rows
+]
+
+
+@pytest.mark.parametrize("name,n,kw", SMALLEST, ids=[c[0] for c in SMALLEST])
+def test_smallest_shapes(name, n, kw):
+    inp = make_config(n, replicate=5, **kw)
+    log(f"[limits] {name} B={inp.batch} gamma={inp.gamma} V={inp.vocab} {inp.dtype} rows={inp.total_rows}")
+    sets = [inp.uniforms] + [uniforms_from_seed(inp.uniforms.shape, 400 + s) for s in range(15)]
     rep, errs, _ = parity_check(inp, sets, label=name)
     assert not rep.unexcused, "\n".join(rep.unexcused[:10])
     assert not errs, errs
