@@ -1803,7 +1803,7 @@ __device__ __forceinline__ void write_violation(const Params& P, int b) {
 // outputs are then all -1, the bits are flagged, and it is not counted.
 template <typename E>
 __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool writer, float T, ResolveShared& rs,
-                                                   const double* tab) {
+                                                   double* tab, const double* tv) {
     const int tid = threadIdx.x;
     const int G = P.gamma;
     DrawTask tk;
@@ -1858,16 +1858,16 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
         // are loaded together with its piece count (slots past the count hold
         // stale values and are masked once it is in), so that no load waits for
         // another or for the temperature.
+        // (the bonus row's drafted-token fields and uniform slot are loaded too
+        // and left unused: no branch, so no copy that waits for them)
         const int t = t0 + tid;
         const RowStat* rp = &P.rows[t];
         np = rp->np;
-        if (tid < gb) {
-            xid = P.ids[o0 + tid];
-            xs = rp->x;
-            lx = rp->lx;
-            qx = rp->qx;
-            u = P.uniforms[(size_t)b * (G + 2) + tid];
-        }
+        xs = rp->x;
+        lx = rp->lx;
+        qx = rp->qx;
+        u = P.uniforms[(size_t)b * (G + 2) + tid];
+        if (tid < gb) xid = P.ids[o0 + tid];
         pp = &P.parts[(size_t)t * kMaxPieces];
 #pragma unroll
         for (int q = 0; q < kResolveChunk; ++q) {
@@ -1884,13 +1884,19 @@ __device__ __forceinline__ DrawTask resolve_request(const Params& P, int b, bool
             }
         }
     }
-    // publishes the exponential table (stored to LDS by the caller); the loads
-    // above are complete after it
+    // the exponential table (tv: this thread's entries, loaded by the caller
+    // before everything above) into LDS only now, so that its wait does not
+    // hold back the loads above; the barrier publishes it, and the loads are
+    // complete after it
+#pragma unroll
+    for (int j = 0; j < kTabPerThread; ++j) tab[tid + j * kThreads] = tv[j];
     __syncthreads();
     // the draw's uniforms taken into registers here, with the other loads: their
     // first use comes after the writer's output stores, and a wait there would
-    // wait for those stores too
-    asm volatile("" : "+v"(v_res), "+v"(v_bonus));
+    // wait for those stores too; the drafted token's logit, q and uniform too,
+    // so that their conversions are not hoisted above the piece loads (which
+    // would then wait for them)
+    asm volatile("" : "+v"(v_res), "+v"(v_bonus), "+v"(lx), "+v"(qx), "+v"(u));
     if (owner) {
         np = min(max(np, 0), kMaxPieces);
 #pragma unroll
@@ -2044,15 +2050,13 @@ __global__ __launch_bounds__(kThreads, kLoop ? 3 : 4) void draw_kernel(Params P)
     const int c = P.draw_cmajor ? static_cast<int>(blockIdx.x / P.batch) : static_cast<int>(blockIdx.x - b * C);
     const int NB = P.nblocks;
 
-    // the task (or the request's inputs), the temperature and the exponential
-    // table in one round of loads
+    // the request's inputs, the temperature and the exponential table in one
+    // round of loads (the resolve stores the table to LDS)
     double tv[kTabPerThread];
 #pragma unroll
     for (int j = 0; j < kTabPerThread; ++j) tv[j] = kExp2Table[tid + j * kThreads];
     const float T = P.temperature[b];
-#pragma unroll
-    for (int j = 0; j < kTabPerThread; ++j) sh.tab[tid + j * kThreads] = tv[j];
-    const DrawTask tk = resolve_request<E>(P, b, c == 0, T, rsh, sh.tab);
+    const DrawTask tk = resolve_request<E>(P, b, c == 0, T, rsh, sh.tab, tv);
     if (tk.kind == kDrawNone) return;
     const bool residual = (tk.kind == kDrawResidual);
     if (tk.row < 0 || tk.row >= P.total_draft + P.batch || tk.pos < 0 || tk.pos > P.gamma ||
