@@ -964,10 +964,21 @@ __device__ __forceinline__ long sub_first(long xb, int u) {
     return xb + u * kSubElems + (threadIdx.x & 63) * kSubTokens;
 }
 
+// (a sub-block wholly past the row's end, in its ragged last block, is set to
+// -inf logits and zero q without any load)
 template <typename E>
 __device__ __forceinline__ void issue_block_any(const DrawRow<E>& d, long xb, int V, bool with_q, RawBlock<E>& r) {
 #pragma unroll
-    for (int u = 0; u < kSubBlocks; ++u) issue_sub_any<E>(d, sub_first(xb, u), V, with_q, r.s[u]);
+    for (int u = 0; u < kSubBlocks; ++u) {
+        if (xb + u * kSubElems >= V) {
+#pragma unroll
+            for (int h = 0; h < kSubTokens / E::kPerVec; ++h) r.s[u].l[h] = v4u(E::kNegInfWord);
+#pragma unroll
+            for (int h = 0; h < kSubTokens / 4; ++h) r.s[u].q[h] = v4u(0u);
+        } else {
+            issue_sub_any<E>(d, sub_first(xb, u), V, with_q, r.s[u]);
+        }
+    }
 }
 
 template <typename E>
@@ -1134,11 +1145,13 @@ __device__ __forceinline__ void store_record(const DrawRow<E>& d, long xb, Block
 
 // Sums of one loaded block (any row layout).
 template <typename E, bool kResidual>
-__device__ __forceinline__ void block_record(const DrawRow<E>& d, const RawBlock<E>& r, long xb, double apos,
+__device__ __forceinline__ void block_record(const DrawRow<E>& d, const RawBlock<E>& r, long xb, int V, double apos,
                                              double aneg, const double* tab, BlockRec* rec) {
     BlockSums b;
 #pragma unroll
     for (int u = 0; u < kSubBlocks; ++u) {
+        // (a sub-block wholly past the row's end weighs nothing)
+        if (xb + u * kSubElems >= V) continue;
         float l[kSubTokens], q[kSubTokens];
         decode_sub<E>(r.s[u], kResidual, l, q);
         accumulate_sub<E, kResidual>(d, l, q, u, apos, aneg, tab, b);
@@ -1276,19 +1289,50 @@ __device__ __forceinline__ void draw_blocks_kind(const DrawRow<E>& d, int V, Blo
     const double invZ32 = 1.0 / d.z32;
     const double apos = invZ32 * (1.0 - kSignMargin), aneg = invZ32 * (1.0 + kSignMargin);
     const bool fastrow = d.lalign && (!kResidual || d.qalign);
+    const int jfull = V / kBlockElems;             // blocks wholly inside the row
+    if constexpr (kUpTo2) {
+        // this wave's blocks j1 = jfirst and j2 = jfirst + jstride (those below
+        // jend).  The row's ragged last block jr = jfull, read in a round trip of
+        // its own after the wave's stream, would otherwise end a wave that also
+        // streams a full block: it trades places with the last block of the last
+        // wave, which holds the fewest blocks
+        int j1 = jfirst, j2 = jfirst + jstride;
+        const int nb = (j1 < jend ? 1 : 0) + (j2 < jend ? 1 : 0);
+        if (fastrow && jfull < jend && jfull >= jstride) {
+            const int jr = jfull, wr = jr - jstride, xw = jstride - 1;
+            const int X = xw + jstride < jend ? xw + jstride : xw;
+            if (wr != xw && X != jr) {
+                if (jfirst == wr) j2 = X;
+                else if (jfirst == xw) {
+                    if (X == xw) j1 = jr;
+                    else j2 = jr;
+                }
+            }
+        }
+        const bool f1 = fastrow && nb >= 1 && j1 < jfull, f2 = fastrow && nb >= 2 && j2 < jfull;
+        if (f1) {
+            StreamCaps c;
+            if (f2) stream_subs<E, kResidual, 2>(d, recs, j1, j2, apos, aneg, tab, c);
+            else stream_subs<E, kResidual, 1>(d, recs, j1, j1, apos, aneg, tab, c);
+            capture_marginals<E, kResidual>(d, recs, c, tab);
+        }
+        // the rest on their own (a ragged block, or a row that is not aligned)
+        for (int t = 0; t < nb; ++t) {
+            if (t == 0 ? f1 : f2) continue;
+            const int j = t == 0 ? j1 : j2;
+            RawBlock<E> r;
+            const long xb = (long)j * kBlockElems;
+            issue_block_any<E>(d, xb, V, kResidual, r);
+            block_record<E, kResidual>(d, r, xb, V, apos, aneg, tab, &recs[j]);
+        }
+        return;
+    }
     int jany = jfirst;                             // first block taken on its own
     if (fastrow) {
-        const int jfull = V / kBlockElems;         // blocks wholly inside the row
         const int jend_full = jend < jfull ? jend : jfull;
         StreamCaps c;
         int j = jfirst;
-        if (kUpTo2) {
-            if (j < jend_full) {
-                const int n = j + jstride < jend_full ? 2 : 1;
-                draw_blocks_upto2<E, kResidual>(d, V, recs, j, jstride, n, apos, aneg, tab, c);
-                j += n * jstride;
-            }
-        } else {
+        {
             while (j < jend_full) {
                 const int n = j + jstride < jend_full ? 2 : 1;
                 draw_blocks_upto2<E, kResidual>(d, V, recs, j, jstride, n, apos, aneg, tab, c);
@@ -1302,7 +1346,7 @@ __device__ __forceinline__ void draw_blocks_kind(const DrawRow<E>& d, int V, Blo
         RawBlock<E> r;
         const long xb = (long)j * kBlockElems;
         issue_block_any<E>(d, xb, V, kResidual, r);
-        block_record<E, kResidual>(d, r, xb, apos, aneg, tab, &recs[j]);
+        block_record<E, kResidual>(d, r, xb, V, apos, aneg, tab, &recs[j]);
     }
 }
 
