@@ -1510,30 +1510,44 @@ __device__ __forceinline__ SelBlock select_block(const DrawRow<E>& d, int V, int
                 }
             }
         }
-        // rare: blocks re-evaluated from their tokens, one at a time by the wave
+        // rare: blocks re-evaluated from their tokens, one at a time by the wave,
+        // a sub-block per round trip.  One copy of the body, not unrolled: the
+        // select runs once per request, on code the stream has usually pushed
+        // out of the instruction cache, and every line of code it passes costs
+        unsigned long long needs[kSelPer];
 #pragma unroll
-        for (int r = 0; r < kSelPer; ++r) {
-            const int j = lane * kSelPer + r;
-            unsigned long long need = __ballot(j < NB && (full || nm_t[r] > kMarginSlots));
-            while (need != 0ull) {
-                const int L = __ffsll(static_cast<long long>(need)) - 1;
-                need &= need - 1ull;
-                const long xb = (long)(L * kSelPer + r) * kBlockElems;
-                RawBlock<E> raw;
-                issue_block_any<E>(d, xb, V, true, raw);
-                double w = 0.0;
+        for (int r = 0; r < kSelPer; ++r)
+            needs[r] = __ballot(lane * kSelPer + r < NB && (full || nm_t[r] > kMarginSlots));
+        unsigned long long anyneed = 0ull;
 #pragma unroll
-                for (int u = 0; u < kSubBlocks; ++u) {
-                    float l[kSubTokens], q[kSubTokens];
-                    decode_sub<E>(raw.s[u], true, l, q);
+        for (int r = 0; r < kSelPer; ++r) anyneed |= needs[r];
+        if (anyneed != 0ull) {
+#pragma unroll 1
+            for (int r = 0; r < kSelPer; ++r) {
+                unsigned long long need = needs[0];
 #pragma unroll
-                    for (int k = 0; k < kSubTokens; ++k) {
-                        w += fmax(draw_e<E>(d, l[k], tab) * invZ64 - static_cast<double>(q[k]), 0.0);
-                        if (k & 1) __builtin_amdgcn_sched_barrier(0);
+                for (int rr = 1; rr < kSelPer; ++rr)
+                    if (rr == r) need = needs[rr];
+                while (need != 0ull) {
+                    const int L = __ffsll(static_cast<long long>(need)) - 1;
+                    need &= need - 1ull;
+                    const long xb = (long)(L * kSelPer + r) * kBlockElems;
+                    double w = 0.0;
+#pragma unroll 1
+                    for (int u = 0; u < kSubBlocks; ++u) {
+                        RawSub<E> raw;
+                        issue_sub_any<E>(d, sub_first(xb, u), V, true, raw);
+                        float l[kSubTokens], q[kSubTokens];
+                        decode_sub<E>(raw, true, l, q);
+#pragma unroll
+                        for (int k = 0; k < kSubTokens; ++k)
+                            w += fmax(draw_e<E>(d, l[k], tab) * invZ64 - static_cast<double>(q[k]), 0.0);
                     }
+                    w = wave_sum(w);
+#pragma unroll
+                    for (int rr = 0; rr < kSelPer; ++rr)
+                        if (rr == r && lane == L) wt[rr] = w;
                 }
-                w = wave_sum(w);
-                if (lane == L) wt[r] = w;
             }
         }
     } else {

@@ -20,7 +20,7 @@ import oracle
 from synth import make_config
 from synth.workloads import f32_to_bf16_bits, uniforms_from_seed
 from tests.gpu_helpers import log, parity_check, run_gpu
-from tests.helpers import U_STEP, explicit_inputs
+from tests.helpers import U_STEP, explicit_inputs, uniform_grid_u
 
 pytestmark = pytest.mark.gpu
 
@@ -230,3 +230,66 @@ def test_full_size_more_logits_replicates(n, rep_id, nsets):
     assert not rep.unexcused, "\n".join(rep.unexcused[:10])
     assert not errs, errs
     assert rep.excused <= 1e-4 * rep.requests + 1e-9 or rep.excused == 0
+
+
+# ---------------------------------------------------------------- marginal tokens
+def _marginal_case(dtype, seed, only):
+    """Residual rows whose blocks hold 0, 1, 2, 3 and 2048 tokens with q within
+    4e-6 of p (the draw's fp32-normaliser sign test cannot place them: they are
+    captured inline, or their block is summed again from its tokens) and a
+    drafted token with a large q, so that position 0 is rejected.  The other
+    tokens have q = p / 2 (the drafted token's q takes the rest of the mass), or,
+    with `only`, q = 1.001 p and the marginal ones q < p, so that every token of
+    positive residual weight is a marginal one (q is then not normalised: the
+    arithmetic is the same)."""
+    rng = np.random.default_rng(seed)
+    B, g, V, blk = 24, 2, 5 * 2048, 2048
+    logits = rng.normal(0.0, 1.5, size=(B, g + 1, V))
+    # a +10 peak in each of the first four blocks: in the marginal picks of blocks
+    # 1-3 (below), so that those blocks hold most of the positive residual weight
+    peaks = np.array([rng.integers(j * blk, (j + 1) * blk) for j in range(4)])
+    logits[:, :, peaks] += 10.0
+    logits = logits.astype(np.float32)
+    if dtype == "bf16":
+        logits = (f32_to_bf16_bits(logits).astype(np.uint32) << 16).view(np.float32)
+    q = np.zeros((B, g, V), dtype=np.float32)
+    ids = np.zeros((B, g), dtype=np.int32)
+    for b in range(B):
+        for i in range(g):
+            p = scipy.special.softmax(logits[b, i].astype(np.float64))
+            qq = (1.001 if only else 0.5) * p
+            for j, count in enumerate([0, 1, 2, 3, blk]):
+                toks = np.arange(j * blk, (j + 1) * blk)
+                pick = toks if count == blk else rng.choice(toks, count, replace=False)
+                if 0 < count < blk and peaks[j] not in pick:
+                    pick[0] = peaks[j]
+                eps = rng.uniform(-4e-6, -1e-6, size=len(pick)) if only else rng.uniform(-4e-6, 4e-6, size=len(pick))
+                qq[pick] = p[pick] * (1.0 + eps)
+            x = int(np.argmin(p[:blk]))              # a drafted token far less likely under p
+            qq[x] = 0.0
+            qq[x] = 0.5 if only else 1.0 - qq.sum()
+            q[b, i] = qq.astype(np.float32)
+            ids[b, i] = x
+    u = uniform_grid_u(rng, (B, g + 2))
+    inp = explicit_inputs(logits, q, ids, np.ones(B, dtype=np.float32), u)
+    if dtype == "bf16":
+        inp = _as(inp, "bf16")
+    return inp
+
+
+@pytest.mark.parametrize("only", [False, True], ids=["mixed", "only_marginal"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_marginal_tokens_in_residual_blocks(dtype, only):
+    inp = _marginal_case(dtype, (77 if dtype == "f32" else 78) + (10 if only else 0), only)
+    log(f"[marginal] B={inp.batch} gamma={inp.gamma} V={inp.vocab} {inp.dtype} only={only}")
+    o = oracle.verify(inp)
+    assert (o.num_accepted == 0).all()                # every request draws from a residual row
+    sets = [inp.uniforms] + [uniforms_from_seed(inp.uniforms.shape, 600 + s) for s in range(15)]
+    if only:
+        # the drawn tokens are marginal ones, in blocks of 1 and 2 inline tokens
+        # and in blocks summed again from their tokens
+        drawn = {int(t) // 2048 for t in o.tokens[:, 0]}
+        assert {1, 2, 3} <= drawn and 0 not in drawn
+    rep, errs, _ = parity_check(inp, sets, label=f"marginal-{dtype}-{'only' if only else 'mixed'}")
+    assert not rep.unexcused, "\n".join(rep.unexcused[:10])
+    assert not errs, errs
